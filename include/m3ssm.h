@@ -1,0 +1,154 @@
+/*
+ * m3ssm.h -- C ABI of libm3ssm: the Mamba-3 SSM layer recurrence on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (per batch b and head h, t = 0..T-1):
+ *
+ *   h_t = alpha_t R_t ( h_{t-1} + (1 - lam_t) dt_t B_{t-1} x_{t-1}^T )
+ *         + lam_t dt_t B_t x_t^T
+ *   y_t = C_t^T h_t
+ *
+ * with alpha_t = exp(dt_t * A) and R_t the block-diagonal rotation whose 2x2
+ * block for rows (2k, 2k+1) is [[cos p, -sin p], [sin p, cos p]], p = dt_t *
+ * theta_t[k].  This is the exponential-trapezoidal rule (Mamba-3 paper
+ * summary, aipaper.cc, "Mathematical formulas", Proposition 1: alpha =
+ * e^{dt A}, beta = (1-lam) dt alpha, gamma = lam dt; Mamba-3 explainer,
+ * yunpan.plus, "first improvement") applied to the complex transition
+ * A + i theta, realised as 2x2 rotations (explainer, "second improvement";
+ * paper summary, Proposition 3: the rotations can be moved onto B and C as a
+ * data-dependent RoPE).  MIMO (paper summary, item 3; explainer, "third
+ * improvement"): x_t is P x R and B_t, C_t are N x R, so B x^T is a rank-R
+ * product and y_t is R x P.  h_{-1} = 0 and B_{-1} x_{-1}^T = 0.
+ *
+ * Layouts (row-major, dense, no strides).  T is the storage type chosen by
+ * m3_dtype (float or bfloat16) for x, B, C and y; everything else is float:
+ *   x, y       [batch, T, H, R, P]   (x_t stored as its transpose, P contiguous)
+ *   B, C       [batch, T, H, R, N]   (N contiguous)
+ *   dt, lam    [batch, T, H]         (dt > 0 already softplus'd; lam in [0,1])
+ *   theta      [batch, T, H, N/2]    (angle rate per rotation pair)
+ *   A          [H]                   (A <= 0, constant in time)
+ *   h_final    [batch, H, N, P]      (state after the last token, float)
+ *
+ * Ownership and threading: every pointer is caller-owned DEVICE memory on the
+ * current HIP device, aligned to its element size and further as each call
+ * states (vector loads).  The library allocates nothing and
+ * keeps no mutable global state; calls enqueue work on `stream` (a
+ * hipStream_t; NULL = the default stream) and return without synchronising.
+ * Calls on different streams that write different buffers may overlap.
+ *
+ * Errors: every argument is validated on the host before anything is
+ * enqueued; an invalid call returns an error code and enqueues nothing.  A
+ * failed kernel launch returns M3_ERR_HIP.  Faults inside kernels surface, as
+ * with any HIP kernel, at the caller's next synchronisation.  Data
+ * preconditions (A <= 0, dt > 0, lam in [0,1], finite inputs) are documented,
+ * not checked.  No C++ exception crosses this interface.
+ */
+#ifndef M3SSM_H_
+#define M3SSM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define M3SSM_VERSION 100 /* 1.0.0 */
+
+typedef enum {
+  M3_SUCCESS = 0,
+  M3_ERR_INVALID_VALUE = 1, /* null pointer, bad size, misalignment, bad chunk */
+  M3_ERR_NOT_SUPPORTED = 2, /* valid but outside the compiled shape set */
+  M3_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  M3_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} m3_status;
+
+typedef enum {
+  M3_F32 = 0, /* x, B, C, y stored as float */
+  M3_BF16 = 1 /* x, B, C, y stored as bfloat16; accumulation stays float */
+} m3_dtype;
+
+typedef struct {
+  int64_t batch;     /* sequences (>= 0) */
+  int64_t seqlen;    /* T, tokens per sequence (>= 0; ignored by decode) */
+  int64_t nheads;    /* H (>= 1) */
+  int64_t headdim_p; /* P: 16, 32, 64 or 128 */
+  int64_t dstate_n;  /* N: even; 16..256 and a multiple of 16 (bf16 prefill: of 32) */
+  int64_t rank_r;    /* R: 1, 2 or 4 (MIMO rank) */
+} m3_dims;
+
+/* Library version (M3SSM_VERSION of the build). */
+int m3_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* m3_status_string(m3_status status);
+
+/*
+ * Bytes of device workspace m3_prefill needs for these dims, chunk and dtype;
+ * 0 if the combination is invalid or unsupported (m3_prefill then says why).
+ * Host only; enqueues nothing.
+ */
+size_t m3_prefill_workspace_size(const m3_dims* dims, int chunk, m3_dtype dtype);
+
+/*
+ * Chunked prefill of the whole sequence: writes y for every token and, if
+ * h_final is not NULL, the state after the last token.
+ *
+ * chunk: tokens per chunk, a multiple of 16 with 16 <= chunk <= 128 and
+ * chunk * R <= 256.  The result does not depend on the chunk beyond float
+ * rounding: inside a chunk the recurrence is evaluated in its parallel
+ * (structured-mask) form -- the decay matrix times the 2-band trapezoid
+ * matrix (Mamba-3 paper translation, sz-guanghua.com.cn, section 3.1,
+ * equation 7) with B and C rotated by the cumulative angles (data-dependent
+ * RoPE, paper summary Proposition 3) -- and chunks are chained by the
+ * recurrence on the state (explainer: parallel inside a chunk, recurrent
+ * across chunks).  T need not be a multiple of chunk.
+ *
+ * Alignment: x 16 bytes; B and C two elements; y, dt, lam, theta, A and
+ * h_final one element.
+ *
+ * workspace: device scratch of at least m3_prefill_workspace_size() bytes,
+ * 256-byte aligned, owned by the caller, not read before being written.
+ * Concurrent calls need distinct workspaces.
+ *
+ * Returns M3_SUCCESS once all kernels are enqueued.  y and h_final must not
+ * overlap the inputs.  batch == 0 or seqlen == 0 enqueues nothing (h_final,
+ * if given, is then zero-filled when seqlen == 0 and batch > 0).
+ */
+m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void* x,
+                     const float* dt, const float* A, const float* lam, const float* theta,
+                     const void* B, const void* C, void* y, float* h_final, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step for `batch` independent sequences (dims->seqlen ignored):
+ *
+ *   h_out = alpha R (h_in + (1-lam) dt B_prev x_prev^T) + lam dt B_t x_t^T
+ *   y_t   = C_t^T h_out
+ *
+ * (the same recurrence, one token; the previous token's x and B are what the
+ * trapezoid's beta term needs -- explainer, "first improvement"; the rank-R
+ * product is the MIMO update -- paper summary, item 3).
+ *
+ * Layouts: h_in, h_out [batch, H, N, P] float, in the unrotated frame, and
+ * h_out may equal h_in (in-place update); x_t, x_prev, y_t [batch, H, R, P];
+ * B_t, B_prev, C_t [batch, H, R, N] (storage type from dtype); dt, lam
+ * [batch, H]; theta [batch, H, N/2]; A [H].
+ *
+ * Alignment: h_in, h_out 16 bytes; x_t, x_prev four elements; B_t, B_prev,
+ * C_t two elements; y_t, dt, lam, theta, A one element.
+ *
+ * First step of a fresh sequence: h_in = 0 and x_prev = B_prev = 0.  After a
+ * prefill of T tokens: h_in = that call's h_final, x_prev = x_{T-1},
+ * B_prev = B_{T-1} (the raw, unrotated inputs of the last prefilled token).
+ */
+m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in, float* h_out,
+                         const void* x_t, const void* x_prev, const void* B_t,
+                         const void* B_prev, const void* C_t, const float* dt, const float* A,
+                         const float* lam, const float* theta, void* y_t, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M3SSM_H_ */

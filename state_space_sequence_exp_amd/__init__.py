@@ -1,0 +1,24 @@
+"""libm3ssm: the Mamba-3 SSM layer recurrence (exponential-trapezoidal
+discretisation, complex state as a data-dependent RoPE, rank-R MIMO) as
+hand-written HIP kernels for AMD Instinct MI355X (gfx950), behind a C ABI
+(include/m3ssm.h).
+
+Python entry points (ctypes; PyTorch tensors supply device memory and the
+current stream):
+
+    prefill(x, dt, A, lam, theta, B, C, chunk) -> (y, h_final)
+    decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta) -> (y_t, h)
+    prefill_workspace_size(...), version(), status_string(code)
+
+``inputs`` draws the seeded synthetic workloads.  Build the library with
+``python -m state_space_sequence_exp_amd.build``.
+"""
+from ._binding import (ABI_SYMBOLS, LIB_PATH, M3_BF16, M3_ERR_HIP, M3_ERR_INVALID_VALUE,
+                       M3_ERR_NOT_SUPPORTED, M3_ERR_WORKSPACE, M3_F32, M3_SUCCESS, M3Dims,
+                       M3Error, decode_step, load_library, prefill, prefill_workspace_size,
+                       status_string, version)
+
+__all__ = ["prefill", "decode_step", "prefill_workspace_size", "version", "status_string",
+           "load_library", "M3Error", "M3Dims", "ABI_SYMBOLS", "LIB_PATH", "M3_SUCCESS",
+           "M3_ERR_INVALID_VALUE", "M3_ERR_NOT_SUPPORTED", "M3_ERR_WORKSPACE", "M3_ERR_HIP",
+           "M3_F32", "M3_BF16"]

@@ -1,0 +1,212 @@
+"""ctypes binding of libm3ssm (include/m3ssm.h).
+
+Argument marshalling only: every step of the recurrence runs in the HIP
+kernels of libm3ssm.so.  PyTorch supplies device memory and the current
+stream.  If the library is not built this module raises on first use; there
+is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libm3ssm.so")
+
+M3_SUCCESS = 0
+M3_ERR_INVALID_VALUE = 1
+M3_ERR_NOT_SUPPORTED = 2
+M3_ERR_WORKSPACE = 3
+M3_ERR_HIP = 4
+M3_F32 = 0
+M3_BF16 = 1
+
+# every function declared in include/m3ssm.h
+ABI_SYMBOLS = ("m3_version", "m3_status_string", "m3_prefill_workspace_size", "m3_prefill",
+               "m3_decode_step")
+
+
+class M3Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s" % (where, status_string(status)))
+
+
+class M3Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim_p", ctypes.c_int64),
+                ("dstate_n", ctypes.c_int64), ("rank_r", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libm3ssm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libm3ssm.so not found at %s; build it with "
+                           "`python -m state_space_sequence_exp_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    vp = ctypes.c_void_p
+    dp = ctypes.POINTER(M3Dims)
+    lib.m3_version.restype = ctypes.c_int
+    lib.m3_version.argtypes = []
+    lib.m3_status_string.restype = ctypes.c_char_p
+    lib.m3_status_string.argtypes = [ctypes.c_int]
+    lib.m3_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.m3_prefill_workspace_size.argtypes = [dp, ctypes.c_int, ctypes.c_int]
+    lib.m3_prefill.restype = ctypes.c_int
+    lib.m3_prefill.argtypes = [dp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp,
+                               vp, vp, ctypes.c_size_t, vp]
+    lib.m3_decode_step.restype = ctypes.c_int
+    lib.m3_decode_step.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   vp, vp]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def version() -> int:
+    return load_library().m3_version()
+
+
+def status_string(status: int) -> str:
+    return load_library().m3_status_string(int(status)).decode()
+
+
+def _dims(batch, seqlen, nheads, P, N, R) -> M3Dims:
+    return M3Dims(int(batch), int(seqlen), int(nheads), int(P), int(N), int(R))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return M3_F32
+    if t.dtype == torch.bfloat16:
+        return M3_BF16
+    raise TypeError("x, B, C must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.device != device:
+        raise ValueError("%s: on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def prefill_workspace_size(batch, seqlen, nheads, P, N, R, chunk, dtype) -> int:
+    """Bytes of workspace m3_prefill needs (0: nothing to do, or unsupported)."""
+    import torch
+    code = dtype if isinstance(dtype, int) else (M3_BF16 if dtype == torch.bfloat16 else M3_F32)
+    d = _dims(batch, seqlen, nheads, P, N, R)
+    return int(load_library().m3_prefill_workspace_size(ctypes.byref(d), int(chunk), code))
+
+
+def prefill(x, dt, A, lam, theta, B, C, chunk: int, *, y=None, h_final=None,
+            want_h_final: bool = True, workspace=None, stream=None) -> Tuple:
+    """Chunked prefill on the GPU.
+
+    x [Bt,T,H,R,P] (or [Bt,T,H,P] for R=1); B, C [Bt,T,H,R,N] (or [Bt,T,H,N]);
+    dt, lam [Bt,T,H]; theta [Bt,T,H,N/2]; A [H].  x, B, C float32 or
+    bfloat16 (same dtype), the rest float32, all contiguous on one GPU.
+    Returns (y with x's shape and dtype, h_final [Bt,H,N,P] float32 or None).
+    """
+    import torch
+    lib = load_library()
+    squeeze = x.dim() == 4
+    x5 = x.unsqueeze(3) if squeeze else x
+    B5 = B.unsqueeze(3) if B.dim() == 4 else B
+    C5 = C.unsqueeze(3) if C.dim() == 4 else C
+    nb, nt, nh, nr, npd = x5.shape
+    nn = B5.shape[-1]
+    dev = x.device
+    code = _dtype_code(x)
+    _check(x5, "x", x.dtype, (nb, nt, nh, nr, npd), dev)
+    _check(B5, "B", x.dtype, (nb, nt, nh, nr, nn), dev)
+    _check(C5, "C", x.dtype, (nb, nt, nh, nr, nn), dev)
+    _check(dt, "dt", torch.float32, (nb, nt, nh), dev)
+    _check(lam, "lam", torch.float32, (nb, nt, nh), dev)
+    _check(theta, "theta", torch.float32, (nb, nt, nh, nn // 2), dev)
+    _check(A, "A", torch.float32, (nh,), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _check(y, "y", x.dtype, tuple(x.shape), dev)
+    if h_final is None and want_h_final:
+        h_final = torch.empty((nb, nh, nn, npd), dtype=torch.float32, device=dev)
+    elif h_final is not None:
+        _check(h_final, "h_final", torch.float32, (nb, nh, nn, npd), dev)
+    d = _dims(nb, nt, nh, npd, nn, nr)
+    need = int(lib.m3_prefill_workspace_size(ctypes.byref(d), int(chunk), code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.m3_prefill(ctypes.byref(d), code, int(chunk), _ptr(x5), _ptr(dt), _ptr(A), _ptr(lam),
+                        _ptr(theta), _ptr(B5), _ptr(C5), _ptr(y), _ptr(h_final),
+                        _ptr(workspace), ws_bytes, _stream(stream))
+    if st != M3_SUCCESS:
+        raise M3Error(st, "m3_prefill")
+    return y, h_final
+
+
+def decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta, *, h_out=None, y=None,
+                stream=None) -> Tuple:
+    """One decode step on the GPU.
+
+    h [S,H,N,P] float32; x_t, x_prev [S,H,R,P]; B_t, B_prev, C_t [S,H,R,N]
+    (float32 or bfloat16); dt, lam [S,H]; theta [S,H,N/2]; A [H].
+    h_out defaults to h itself (in-place update).  Returns (y_t [S,H,R,P],
+    h_out).
+    """
+    import torch
+    lib = load_library()
+    ns, nh, nn, npd = h.shape
+    nr = x_t.shape[2]
+    dev = h.device
+    code = _dtype_code(x_t)
+    _check(h, "h", torch.float32, (ns, nh, nn, npd), dev)
+    for name, t in (("x_t", x_t), ("x_prev", x_prev)):
+        _check(t, name, x_t.dtype, (ns, nh, nr, npd), dev)
+    for name, t in (("B_t", B_t), ("B_prev", B_prev), ("C_t", C_t)):
+        _check(t, name, x_t.dtype, (ns, nh, nr, nn), dev)
+    _check(dt, "dt", torch.float32, (ns, nh), dev)
+    _check(lam, "lam", torch.float32, (ns, nh), dev)
+    _check(theta, "theta", torch.float32, (ns, nh, nn // 2), dev)
+    _check(A, "A", torch.float32, (nh,), dev)
+    if h_out is None:
+        h_out = h
+    else:
+        _check(h_out, "h_out", torch.float32, (ns, nh, nn, npd), dev)
+    if y is None:
+        y = torch.empty((ns, nh, nr, npd), dtype=x_t.dtype, device=dev)
+    else:
+        _check(y, "y", x_t.dtype, (ns, nh, nr, npd), dev)
+    d = _dims(ns, 1, nh, npd, nn, nr)
+    st = lib.m3_decode_step(ctypes.byref(d), code, _ptr(h), _ptr(h_out), _ptr(x_t), _ptr(x_prev),
+                            _ptr(B_t), _ptr(B_prev), _ptr(C_t), _ptr(dt), _ptr(A), _ptr(lam),
+                            _ptr(theta), _ptr(y), _stream(stream))
+    if st != M3_SUCCESS:
+        raise M3Error(st, "m3_decode_step")
+    return y, h_out

@@ -1,0 +1,140 @@
+// m3_device.h -- device-side building blocks shared by the libm3ssm kernels
+// (gfx950 / CDNA4 only): storage types, conversions, 16x16 MFMA fragments,
+// fast sine/cosine and wave-level scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m3 {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
+
+// Two adjacent storage elements (a rotation pair) as floats.
+__device__ __forceinline__ float2 load_pair(const float* p) {
+  return *reinterpret_cast<const float2*>(p);
+}
+__device__ __forceinline__ float2 load_pair(const bf16* p) {
+  bf16x2 v = *reinterpret_cast<const bf16x2*>(p);
+  return make_float2(static_cast<float>(v.x), static_cast<float>(v.y));
+}
+
+constexpr float kInv2Pi = 0.15915494309189535f;
+// 2*pi split in two floats (Cody-Waite): kTwoPiHi is the float nearest 2*pi.
+constexpr float kTwoPiHi = 6.28318548202514648f;
+constexpr float kTwoPiLo = -1.7484555314695172e-7f;
+
+// a + b reduced to about [-pi, pi].  Running angles are kept reduced at every
+// step so that they never grow (a float near 100 rad has a 7.6e-6 ulp) and the
+// reduction itself adds no systematic error.
+__device__ __forceinline__ float angle_add(float a, float b) {
+#pragma clang fp contract(off)
+  float s = a + b;
+  const float k = __builtin_rintf(s * kInv2Pi);
+  s = __builtin_fmaf(-k, kTwoPiHi, s);
+  return __builtin_fmaf(-k, kTwoPiLo, s);
+}
+
+// An angle in revolutions held as an unevaluated float sum hi + lo, kept
+// reduced to |hi| <= 1/2.  Sums of many angles stay exact to about 2^-40
+// revolutions (error-free two-sum plus a split conversion from radians);
+// a plain float sum of angles near pi drifts by about 1e-6 rad per 64 terms.
+struct RevSum {
+  float hi = 0.f, lo = 0.f;
+
+  // Error-free transformations: FMA contraction would break them.
+  __device__ __forceinline__ void add(float b_hi, float b_lo) {
+#pragma clang fp contract(off)
+    const float t = hi + b_hi;
+    const float bp = t - hi;
+    const float e = (hi - (t - bp)) + (b_hi - bp);
+    lo += e + b_lo;
+    hi = t - __builtin_rintf(t);  // exact: t and its nearest integer are close
+  }
+  // add an angle given in radians
+  __device__ __forceinline__ void add_rad(float rad) {
+#pragma clang fp contract(off)
+    constexpr float kInvHi = 0.15915493667125702f;   // float nearest 1/(2 pi)
+    constexpr float kInvLo = 6.4206382432985265e-09f; // 1/(2 pi) - kInvHi
+    const float p_hi = rad * kInvHi;
+    const float p_lo = __builtin_fmaf(rad, kInvHi, -p_hi) + rad * kInvLo;
+    add(p_hi, p_lo);
+  }
+  __device__ __forceinline__ void add(const RevSum& o) { add(o.hi, o.lo); }
+  __device__ __forceinline__ float revolutions() const { return hi + lo; }
+  __device__ __forceinline__ float radians() const { return (hi + lo) * kTwoPiHi; }
+};
+
+// sin and cos of an angle already reduced to about [-pi, pi], on the hardware
+// sine/cosine (which take revolutions).
+__device__ __forceinline__ void fast_sincos(float a, float* s, float* c) {
+  const float r = a * kInv2Pi;
+  *s = __builtin_amdgcn_sinf(r);
+  *c = __builtin_amdgcn_cosf(r);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    float o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// 16x16 MFMA tiles.  Lane l holds, for A (16 x K, row-major in LDS) row l%16
+// and K-slots [g*KPL, g*KPL+KPL) with g = l/16; for B (K x 16) column l%16
+// and the same K-slots; the 16x16 fp32 result holds rows 4g..4g+3 of column
+// l%16 (element j = row 4g+j).
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<bf16> {
+  static constexpr int KPL = 8;
+  static constexpr int K = 32;
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // Fragment from a row-major matrix: row `row`, K-slots starting at k0.
+  __device__ __forceinline__ static frag load(const bf16* base, int ld, int row, int k0) {
+    const int g = (threadIdx.x & 63) >> 4;
+    return *reinterpret_cast<const bf16x8*>(base + (size_t)row * ld + k0 + g * KPL);
+  }
+};
+
+template <>
+struct Mfma<float> {
+  static constexpr int KPL = 1;
+  static constexpr int K = 4;
+  typedef float frag;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const float* base, int ld, int row, int k0) {
+    const int g = (threadIdx.x & 63) >> 4;
+    return base[(size_t)row * ld + k0 + g];
+  }
+};
+
+}  // namespace m3

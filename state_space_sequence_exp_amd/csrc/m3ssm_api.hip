@@ -1,0 +1,203 @@
+// m3ssm_api.hip -- the C ABI of libm3ssm (declared in include/m3ssm.h):
+// argument validation, workspace carving and kernel dispatch.  Everything is
+// checked on the host before any HIP call, so an invalid call enqueues
+// nothing.
+#include <limits.h>
+#include <stdint.h>
+
+#include "m3_internal.h"
+#include "m3ssm.h"
+
+namespace {
+
+using m3::ChunkLayout;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+bool valid_p(int64_t P) { return P == 16 || P == 32 || P == 64 || P == 128; }
+bool valid_r(int64_t R) { return R == 1 || R == 2 || R == 4; }
+
+size_t esize_of(m3_dtype d) { return d == M3_BF16 ? 2 : 4; }
+
+// Shape checks shared by prefill and its workspace query.
+m3_status check_prefill_shape(const m3_dims* d, int chunk, m3_dtype dtype) {
+  if (!d) return M3_ERR_INVALID_VALUE;
+  if (dtype != M3_F32 && dtype != M3_BF16) return M3_ERR_INVALID_VALUE;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->headdim_p < 1 || d->dstate_n < 2 ||
+      d->rank_r < 1 || (d->dstate_n % 2) != 0)
+    return M3_ERR_INVALID_VALUE;
+  if (chunk < 1) return M3_ERR_INVALID_VALUE;
+  if (!valid_p(d->headdim_p) || !valid_r(d->rank_r)) return M3_ERR_NOT_SUPPORTED;
+  const int nmul = dtype == M3_BF16 ? 32 : 16;
+  if (d->dstate_n < 16 || d->dstate_n > 256 || d->dstate_n % nmul != 0) return M3_ERR_NOT_SUPPORTED;
+  if (chunk % 16 != 0 || chunk > m3::kLMax || chunk * d->rank_r > m3::kLRMax)
+    return M3_ERR_NOT_SUPPORTED;
+  const int64_t nC = (d->seqlen + chunk - 1) / chunk;
+  if (d->seqlen > INT_MAX || d->batch > INT_MAX || d->nheads > INT_MAX ||
+      d->batch * d->nheads * (nC > 0 ? nC : 1) > INT_MAX)
+    return M3_ERR_NOT_SUPPORTED;
+  const int es = (int)esize_of(dtype);
+  const ChunkLayout lo = m3::chunk_layout(chunk, (int)d->rank_r, (int)d->dstate_n,
+                                          (int)d->headdim_p, es, true);
+  const ChunkLayout ls = m3::chunk_layout(chunk, (int)d->rank_r, (int)d->dstate_n,
+                                          (int)d->headdim_p, es, false);
+  if (lo.total > m3::kLdsLimit || ls.total > m3::kLdsLimit) return M3_ERR_NOT_SUPPORTED;
+  return M3_SUCCESS;
+}
+
+struct WsCarve {
+  size_t off_S, off_G, off_decay, off_rot, total;
+};
+
+WsCarve carve(const m3_dims* d, int chunk, m3_dtype dtype) {
+  WsCarve w;
+  const size_t nC = (size_t)((d->seqlen + chunk - 1) / chunk);
+  const size_t units = (size_t)d->batch * d->nheads * nC;
+  const size_t st = (size_t)d->headdim_p * d->dstate_n;
+  size_t o = 0;
+  w.off_S = o;
+  o = round256(o + units * st * sizeof(float));
+  w.off_G = o;
+  o = round256(o + units * st * esize_of(dtype));
+  w.off_decay = o;
+  o = round256(o + units * sizeof(float));
+  w.off_rot = o;
+  o = round256(o + units * (size_t)(d->dstate_n / 2) * 2 * sizeof(float));
+  w.total = o;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int m3_version(void) { return M3SSM_VERSION; }
+
+const char* m3_status_string(m3_status s) {
+  switch (s) {
+    case M3_SUCCESS: return "M3_SUCCESS: no error";
+    case M3_ERR_INVALID_VALUE:
+      return "M3_ERR_INVALID_VALUE: null pointer, bad size, misaligned pointer or bad chunk";
+    case M3_ERR_NOT_SUPPORTED: return "M3_ERR_NOT_SUPPORTED: shape outside the compiled set";
+    case M3_ERR_WORKSPACE: return "M3_ERR_WORKSPACE: workspace missing or too small";
+    case M3_ERR_HIP: return "M3_ERR_HIP: a HIP runtime call or kernel launch failed";
+  }
+  return "unknown m3_status";
+}
+
+size_t m3_prefill_workspace_size(const m3_dims* dims, int chunk, m3_dtype dtype) {
+  if (check_prefill_shape(dims, chunk, dtype) != M3_SUCCESS) return 0;
+  if (dims->batch == 0 || dims->seqlen == 0) return 0;
+  return carve(dims, chunk, dtype).total;
+}
+
+m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void* x,
+                     const float* dt, const float* A, const float* lam, const float* theta,
+                     const void* B, const void* C, void* y, float* h_final, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  const m3_status st = check_prefill_shape(dims, chunk, dtype);
+  if (st != M3_SUCCESS) return st;
+  const bool work = dims->batch > 0 && dims->seqlen > 0;
+  const uintptr_t es = esize_of(dtype);
+  if (work) {
+    if (!x || !dt || !A || !lam || !theta || !B || !C || !y) return M3_ERR_INVALID_VALUE;
+    // x is read in 16-byte vectors, B and C in rotation pairs
+    if (!aligned(x, 16) || !aligned(B, 2 * es) || !aligned(C, 2 * es) || !aligned(y, es) ||
+        !aligned(dt, 4) || !aligned(A, 4) || !aligned(lam, 4) || !aligned(theta, 4))
+      return M3_ERR_INVALID_VALUE;
+  }
+  if (h_final && !aligned(h_final, 4)) return M3_ERR_INVALID_VALUE;
+  size_t need = 0;
+  WsCarve w = {};
+  if (work) {
+    w = carve(dims, chunk, dtype);
+    need = w.total;
+    if (!workspace || workspace_bytes < need) return M3_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return M3_ERR_INVALID_VALUE;
+  }
+  if (dims->batch == 0) return M3_SUCCESS;
+
+  m3::PrefillArgs a = {};
+  a.nb = (int)dims->batch;
+  a.T = (int)dims->seqlen;
+  a.H = (int)dims->nheads;
+  a.P = (int)dims->headdim_p;
+  a.N = (int)dims->dstate_n;
+  a.R = (int)dims->rank_r;
+  a.L = chunk;
+  a.nC = (int)((dims->seqlen + chunk - 1) / chunk);
+  a.x = x;
+  a.dt = dt;
+  a.A = A;
+  a.lam = lam;
+  a.theta = theta;
+  a.B = B;
+  a.C = C;
+  a.y = y;
+  a.h_final = h_final;
+  if (work) {
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    a.S = reinterpret_cast<float*>(ws + w.off_S);
+    a.G = ws + w.off_G;
+    a.decay = reinterpret_cast<float*>(ws + w.off_decay);
+    a.rot = reinterpret_cast<float2*>(ws + w.off_rot);
+  }
+  const hipError_t e = m3::launch_prefill(a, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;
+}
+
+m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in, float* h_out,
+                         const void* x_t, const void* x_prev, const void* B_t,
+                         const void* B_prev, const void* C_t, const float* dt, const float* A,
+                         const float* lam, const float* theta, void* y_t, void* stream) {
+  if (!dims) return M3_ERR_INVALID_VALUE;
+  if (dtype != M3_F32 && dtype != M3_BF16) return M3_ERR_INVALID_VALUE;
+  const m3_dims* d = dims;
+  if (d->batch < 0 || d->nheads < 1 || d->headdim_p < 1 || d->dstate_n < 2 || d->rank_r < 1 ||
+      (d->dstate_n % 2) != 0)
+    return M3_ERR_INVALID_VALUE;
+  if (!valid_p(d->headdim_p) || !valid_r(d->rank_r)) return M3_ERR_NOT_SUPPORTED;
+  if (d->dstate_n > 256 || d->dstate_n > m3::decode_max_n((int)d->headdim_p))
+    return M3_ERR_NOT_SUPPORTED;
+  if (d->batch * d->nheads > INT_MAX) return M3_ERR_NOT_SUPPORTED;
+  if (d->batch == 0) return M3_SUCCESS;
+  const void* ptrs[] = {h_in, h_out, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta, y_t};
+  for (const void* p : ptrs)
+    if (!p) return M3_ERR_INVALID_VALUE;
+  // state rows in float4, x in 4-element vectors, B and C in rotation pairs
+  const uintptr_t es = esize_of(dtype);
+  if (!aligned(h_in, 16) || !aligned(h_out, 16) || !aligned(x_t, 4 * es) ||
+      !aligned(x_prev, 4 * es) || !aligned(B_t, 2 * es) || !aligned(B_prev, 2 * es) ||
+      !aligned(C_t, 2 * es) || !aligned(y_t, es) || !aligned(dt, 4) || !aligned(A, 4) ||
+      !aligned(lam, 4) || !aligned(theta, 4))
+    return M3_ERR_INVALID_VALUE;
+  // h_out may equal h_in but must not partially overlap it
+  const size_t hbytes = (size_t)d->batch * d->nheads * d->dstate_n * d->headdim_p * sizeof(float);
+  const uintptr_t hi = reinterpret_cast<uintptr_t>(h_in), ho = reinterpret_cast<uintptr_t>(h_out);
+  if (hi != ho && hi < ho + hbytes && ho < hi + hbytes) return M3_ERR_INVALID_VALUE;
+
+  m3::DecodeArgs a = {};
+  a.S = (int)d->batch;
+  a.H = (int)d->nheads;
+  a.P = (int)d->headdim_p;
+  a.N = (int)d->dstate_n;
+  a.R = (int)d->rank_r;
+  a.h_in = h_in;
+  a.h_out = h_out;
+  a.x_t = x_t;
+  a.x_prev = x_prev;
+  a.B_t = B_t;
+  a.B_prev = B_prev;
+  a.C_t = C_t;
+  a.dt = dt;
+  a.A = A;
+  a.lam = lam;
+  a.theta = theta;
+  a.y = y_t;
+  const hipError_t e = m3::launch_decode(a, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;
+}
+
+}  // extern "C"

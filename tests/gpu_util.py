@@ -1,0 +1,82 @@
+"""Helpers shared by the GPU tests: upload seeded inputs, run the GPU path
+through the C ABI binding, run the oracle on the same values, compare."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def torch_dev():
+    import torch
+    return torch, torch.device("cuda:0")
+
+
+def to_gpu_storage(raw, dtype):
+    """numpy storage array (float32 or uint16 bf16 bits) -> device tensor."""
+    torch, dev = torch_dev()
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(raw, dtype=np.float32))
+    return t.to(dev)
+
+
+def to_gpu_f32(a):
+    torch, dev = torch_dev()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def from_gpu(t):
+    import torch
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def upload_prefill(inp):
+    return dict(
+        x=to_gpu_storage(inp["x_raw"], inp["dtype"]),
+        B=to_gpu_storage(inp["B_raw"], inp["dtype"]),
+        C=to_gpu_storage(inp["C_raw"], inp["dtype"]),
+        dt=to_gpu_f32(inp["dt"]), lam=to_gpu_f32(inp["lam"]),
+        theta=to_gpu_f32(inp["theta"]), A=to_gpu_f32(inp["A"]))
+
+
+def gpu_prefill(inp, chunk, dev_inp=None):
+    import state_space_sequence_exp_amd as m3
+    g = dev_inp or upload_prefill(inp)
+    y, hf = m3.prefill(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"], chunk)
+    return y, hf
+
+
+def oracle_prefill(inp, units=None):
+    import oracle
+    return oracle.prefill(inp["x"], inp["dt"], inp["A"], inp["lam"], inp["theta"], inp["B"],
+                          inp["C"], units=units, nthreads=oracle_threads())
+
+
+def oracle_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def rel_l2(a, ref):
+    a = np.asarray(a, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    return float(np.linalg.norm(a - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def worst_unit_rel(y, y_ref):
+    """Worst rel-L2 over (b, h) units of a [B,T,H,...] output."""
+    nb, _, nh = y.shape[:3]
+    return max(rel_l2(y[b, :, h], y_ref[b, :, h]) for b in range(nb) for h in range(nh))
+
+
+def log(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()

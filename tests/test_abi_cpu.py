@@ -1,0 +1,173 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function
+include/m3ssm.h declares, and rejects invalid calls on the host before any
+HIP call (so no GPU is needed for these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import state_space_sequence_exp_amd as m3
+from state_space_sequence_exp_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "m3ssm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(m3.LIB_PATH):
+        from state_space_sequence_exp_amd import build
+        build.build()
+    return m3.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(m3_[a-z_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(_binding.ABI_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.m3_version() == 100
+    for code in range(5):
+        s = m3.status_string(code)
+        assert s.startswith("M3_")
+    assert "unknown" in m3.status_string(99)
+
+
+def dims(b=1, t=64, h=1, p=16, n=16, r=1):
+    return _binding.M3Dims(b, t, h, p, n, r)
+
+
+def ws(d, chunk=32, dtype=m3.M3_F32):
+    return _binding.load_library().m3_prefill_workspace_size(ctypes.byref(d), chunk, dtype)
+
+
+def test_workspace_size(lib):
+    d = dims(2, 100, 3, 16, 32, 2)
+    nC = 4  # ceil(100 / 32)
+    units = 2 * 3 * nC
+    r256 = lambda v: (v + 255) // 256 * 256
+    expect = (r256(units * 16 * 32 * 4) + r256(units * 16 * 32 * 4) + r256(units * 4)
+              + r256(units * 16 * 8))
+    assert ws(d, 32, m3.M3_F32) == expect
+    expect_bf = (r256(units * 16 * 32 * 4) + r256(units * 16 * 32 * 2) + r256(units * 4)
+                 + r256(units * 16 * 8))
+    assert ws(d, 32, m3.M3_BF16) == expect_bf
+    assert ws(dims(0, 100), 32) == 0
+    assert ws(dims(1, 0), 32) == 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n=15), m3.M3_ERR_INVALID_VALUE),      # odd N
+    (dict(r=0), m3.M3_ERR_INVALID_VALUE),       # R < 1
+    (dict(h=0), m3.M3_ERR_INVALID_VALUE),       # no heads
+    (dict(t=-1), m3.M3_ERR_INVALID_VALUE),
+    (dict(p=24), m3.M3_ERR_NOT_SUPPORTED),      # P outside {16,32,64,128}
+    (dict(r=3), m3.M3_ERR_NOT_SUPPORTED),
+    (dict(n=18), m3.M3_ERR_NOT_SUPPORTED),      # N not a multiple of 16
+    (dict(n=512), m3.M3_ERR_NOT_SUPPORTED),
+])
+def test_prefill_shape_validation(lib, bad, code):
+    d = dims(**bad)
+    fake = ctypes.c_void_p(0x10000)
+    st = lib.m3_prefill(ctypes.byref(d), m3.M3_F32, 32, fake, fake, fake, fake, fake, fake, fake,
+                        fake, None, fake, 1 << 30, None)
+    assert st == code
+    assert ws(d) == 0
+
+
+def test_prefill_chunk_validation(lib):
+    d = dims()
+    fake = ctypes.c_void_p(0x10000)
+    call = lambda chunk, dtype=m3.M3_F32, dd=d: lib.m3_prefill(
+        ctypes.byref(dd), dtype, chunk, fake, fake, fake, fake, fake, fake, fake, fake, None,
+        fake, 1 << 30, None)
+    assert call(0) == m3.M3_ERR_INVALID_VALUE
+    assert call(-16) == m3.M3_ERR_INVALID_VALUE
+    assert call(24) == m3.M3_ERR_NOT_SUPPORTED       # not a multiple of 16
+    assert call(256) == m3.M3_ERR_NOT_SUPPORTED      # above 128
+    assert call(128, dd=dims(r=4)) == m3.M3_ERR_NOT_SUPPORTED   # chunk * R > 256
+    assert call(32, dtype=7) == m3.M3_ERR_INVALID_VALUE
+    assert call(32, dtype=m3.M3_BF16) == m3.M3_ERR_NOT_SUPPORTED  # bf16 needs N % 32 == 0
+
+
+def test_prefill_pointer_and_workspace_validation(lib):
+    d = dims()
+    ok = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10001)
+    need = ws(d)
+    assert need > 0
+    args = [ok] * 8
+    base = lambda a, h=None, w=ok, wb=need: lib.m3_prefill(
+        ctypes.byref(d), m3.M3_F32, 32, *a, h, w, wb, None)
+    for i in range(8):  # each input / output pointer null or misaligned
+        a = list(args)
+        a[i] = None
+        assert base(a) == m3.M3_ERR_INVALID_VALUE
+        a[i] = mis
+        assert base(a) == m3.M3_ERR_INVALID_VALUE
+    assert base(args, h=mis) == m3.M3_ERR_INVALID_VALUE
+    a = list(args)
+    a[0] = ctypes.c_void_p(0x10004)   # x must be 16-byte aligned
+    assert base(a) == m3.M3_ERR_INVALID_VALUE
+    assert base(args, w=None) == m3.M3_ERR_WORKSPACE
+    assert base(args, wb=need - 1) == m3.M3_ERR_WORKSPACE
+    assert base(args, w=ctypes.c_void_p(0x10010)) == m3.M3_ERR_INVALID_VALUE  # not 256-aligned
+    # nothing to do: succeeds without touching the device
+    d0 = dims(b=0)
+    assert lib.m3_prefill(ctypes.byref(d0), m3.M3_F32, 32, None, None, None, None, None, None,
+                          None, None, None, None, 0, None) == m3.M3_SUCCESS
+    assert lib.m3_prefill(None, m3.M3_F32, 32, *args, None, ok, need, None) == m3.M3_ERR_INVALID_VALUE
+
+
+def test_decode_validation(lib):
+    fake = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10001)
+
+    def call(d, dtype=m3.M3_BF16, h_in=fake, h_out=fake, others=None):
+        o = others or [fake] * 10
+        return lib.m3_decode_step(ctypes.byref(d), dtype, h_in, h_out, *o, None)
+
+    assert call(dims(b=2, n=15)) == m3.M3_ERR_INVALID_VALUE
+    assert call(dims(b=2, r=3)) == m3.M3_ERR_NOT_SUPPORTED
+    assert call(dims(b=2, p=128, n=256)) == m3.M3_ERR_NOT_SUPPORTED
+    assert call(dims(b=2), dtype=5) == m3.M3_ERR_INVALID_VALUE
+    assert call(dims(b=0)) == m3.M3_SUCCESS
+    for i in range(10):
+        o = [fake] * 10
+        o[i] = None
+        assert call(dims(b=2), others=o) == m3.M3_ERR_INVALID_VALUE
+        o[i] = mis
+        assert call(dims(b=2), others=o) == m3.M3_ERR_INVALID_VALUE
+    # partial overlap of h_in and h_out is rejected
+    d = dims(b=2, n=16, p=16)
+    assert call(d, h_in=ctypes.c_void_p(0x10000), h_out=ctypes.c_void_p(0x10010)) == \
+        m3.M3_ERR_INVALID_VALUE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not found"):
+        _binding.load_library(str(tmp_path / "missing.so"))
+
+
+def test_prefill_lds_limit(lib):
+    """float32 with N=128, P=64 and chunk 128 needs more than 160 KB of LDS."""
+    d = dims(t=256, p=64, n=128)
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.m3_prefill(ctypes.byref(d), m3.M3_F32, 128, fake, fake, fake, fake, fake, fake,
+                          fake, fake, None, fake, 1 << 40, None) == m3.M3_ERR_NOT_SUPPORTED
+    assert ws(d, 128, m3.M3_F32) == 0
+    assert ws(d, 64, m3.M3_F32) > 0
