@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Benchmark of libm3ssm on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints ONE JSON line.  The headline `value` is SISO chunked-prefill
+throughput (tokens/s, a token = one position of one sequence through all
+heads of the layer) on the SISO prefill workload (batch 4, T=2048, 16 heads,
+N=64, P=64, R=1, bf16 x/B/C, chunk 64): each timed step is one m3_prefill
+call (all prefill kernels) on inputs already resident in HBM, with a 512 MB
+scratch write between steps so that the 256 MB last-level cache (MALL) holds
+none of the step's data, timed with HIP events on the stream the kernels run
+on.  The same line carries, measured in the same run:
+
+  roofline      the prefill path against the HBM roofline (algorithmic bytes
+                per call / measured call duration, peak 8 TB/s)
+  cpu_baseline  the fp64 oracle on the host cores for the same workload
+  secondary     MIMO R=4 prefill (B4 T4096 H16 N64 P64), long-context SISO
+                prefill (B1 T16384 H64 N128 P64) and the decode step
+                (256 sequences x 32 heads, N128 P64 R4; us/step and HBM GB/s
+                with its own roofline)
+
+Inputs follow the seeded recipe of state_space_sequence_exp_amd.inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+METRIC = "SSM prefill tokens/s (SISO, MIMO R=4); decode µs/step and HBM GB/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def kernel_source_hash() -> str:
+    d = os.path.join(ROOT, "state_space_sequence_exp_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as fh:
+            h.update(name.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(key)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def prefill_bytes(cfg) -> int:
+    es = 2 if cfg.dtype == "bf16" else 4
+    tokhead = cfg.batch * cfg.seqlen * cfg.nheads
+    return (tokhead * cfg.R * cfg.P * es * 2          # x in, y out
+            + tokhead * cfg.R * cfg.N * es * 2        # B, C
+            + tokhead * 4 * 2                         # dt, lam
+            + tokhead * (cfg.N // 2) * 4              # theta
+            + cfg.nheads * 4                          # A
+            + cfg.batch * cfg.nheads * cfg.N * cfg.P * 4)  # h_final
+
+
+def prefill_flops(cfg) -> int:
+    tokhead = cfg.batch * cfg.seqlen * cfg.nheads
+    return tokhead * (2 * cfg.chunk * cfg.R * cfg.R * (cfg.N + cfg.P) + 4 * cfg.N * cfg.P * cfg.R)
+
+
+def decode_bytes(cfg) -> int:
+    es = 2 if cfg.dtype == "bf16" else 4
+    per = (2 * cfg.N * cfg.P * 4 + 2 * cfg.R * cfg.P * es + 3 * cfg.R * cfg.N * es
+           + (cfg.N // 2) * 4 + 8 + cfg.R * cfg.P * es)
+    return cfg.batch * cfg.nheads * per + cfg.nheads * 4
+
+
+def upload(inp):
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+
+    def st(raw):
+        if inp["dtype"] == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(raw, dtype=np.float32)).to(dev)
+
+    g = {k: st(inp[k + "_raw"]) for k in ("x", "B", "C")}
+    for k in ("dt", "lam", "theta", "A"):
+        g[k] = torch.from_numpy(np.ascontiguousarray(inp[k], dtype=np.float32)).to(dev)
+    if "h0" in inp:
+        g["h0"] = torch.from_numpy(np.ascontiguousarray(inp["h0"], dtype=np.float32)).to(dev)
+    return g
+
+
+def time_prefill(cfg, g, steps, warmup, flush=True):
+    """Per-call durations (ms) of m3_prefill with HIP events on the current
+    stream; a 512 MB scratch fill between calls evicts the MALL."""
+    import torch
+    import state_space_sequence_exp_amd as m3
+    dev = torch.device("cuda:0")
+    ws_bytes = m3.prefill_workspace_size(cfg.batch, cfg.seqlen, cfg.nheads, cfg.P, cfg.N, cfg.R,
+                                         cfg.chunk, g["x"].dtype)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(g["x"])
+    hf = torch.empty((cfg.batch, cfg.nheads, cfg.N, cfg.P), dtype=torch.float32, device=dev)
+    scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) if flush else None
+
+    def call():
+        m3.prefill(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"], cfg.chunk,
+                   y=y, h_final=hf, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for s, e in evs:
+        if flush:
+            scratch.fill_(1.0)
+        s.record()
+        call()
+        e.record()
+    torch.cuda.synchronize()
+    times = [s.elapsed_time(e) for s, e in evs]
+    # back-to-back (no flush) for reference
+    s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(steps):
+        call()
+    e0.record()
+    torch.cuda.synchronize()
+    b2b = s0.elapsed_time(e0) / steps
+    del scratch
+    return times, b2b
+
+
+def time_decode(cfg, g, steps, warmup):
+    import torch
+    import state_space_sequence_exp_amd as m3
+    K = g["x"].shape[0]
+    h = g["h0"].clone()
+    y = torch.empty((cfg.batch, cfg.nheads, cfg.R, cfg.P), dtype=g["x"].dtype, device=h.device)
+
+    def step(t):
+        cur, prev = t % K, (t - 1) % K
+        m3.decode_step(h, g["x"][cur], g["x"][prev], g["B"][cur], g["B"][prev], g["C"][cur],
+                       g["dt"][cur], g["A"], g["lam"][cur], g["theta"][cur], y=y)
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(3):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for t in range(steps):
+            step(t)
+        e.record()
+        torch.cuda.synchronize()
+        reps.append(s.elapsed_time(e) / steps)
+    reps.sort()
+    return reps[len(reps) // 2]
+
+
+def cpu_baseline(cfg, inp, budget_s=20.0):
+    """The fp64 oracle on the host cores: whole (b, h) units of the same
+    workload, as many as fit the time budget; scaled to tokens/s of the full
+    workload (units are independent)."""
+    import oracle
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    nunits = cfg.batch * cfg.nheads
+    # calibrate with one wave of `cores` units, then run a sample within budget
+    n = min(nunits, cores)
+    t0 = time.perf_counter()
+    oracle.prefill(inp["x"], inp["dt"], inp["A"], inp["lam"], inp["theta"], inp["B"], inp["C"],
+                   units=list(range(n)), nthreads=cores)
+    dt = time.perf_counter() - t0
+    waves = max(1, min(nunits // cores, int(budget_s / max(dt, 1e-6))))
+    n2 = min(nunits, waves * cores)
+    if n2 > n:
+        t0 = time.perf_counter()
+        oracle.prefill(inp["x"], inp["dt"], inp["A"], inp["lam"], inp["theta"], inp["B"],
+                       inp["C"], units=list(range(n2)), nthreads=cores)
+        dt = time.perf_counter() - t0
+        n = n2
+    full_time = dt * nunits / n
+    return {"value": cfg.batch * cfg.seqlen / full_time, "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d of %d (batch, head) units over all %d tokens, fp64 C oracle, %.1f s"
+                      % (n, nunits, cfg.seqlen, dt)}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict the MALL between steps")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every (batch, head) unit is independent; sharding is described in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import state_space_sequence_exp_amd as m3
+    from state_space_sequence_exp_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    m3.load_library()
+
+    # ---- headline: SISO prefill (configuration 1) ----
+    cfg = I.CONFIGS[1]
+    log("generating %s" % cfg.name)
+    inp = I.config_inputs(1)
+    g = upload(inp)
+    log("timing prefill %s: %d warmup + %d steps" % (cfg.name, args.warmup, args.steps))
+    times, b2b = time_prefill(cfg, g, args.steps, args.warmup, flush=not args.no_flush)
+    ms = float(np.mean(times))
+    tokens = cfg.batch * cfg.seqlen
+    value = tokens / (ms * 1e-3)
+    nbytes = prefill_bytes(cfg)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    traffic = measured_traffic("prefill_config1")
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "SISO prefill: batch 4, T=2048, 16 heads, N=64, P=64, R=1, "
+                               "bf16 x/B/C, fp32 state, chunk 64",
+                   "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "none"},
+        "roofline": {"kernel": "m3_prefill (chunk_state + state_scan + chunk_out)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": nbytes,
+                     "mfma_frac": prefill_flops(cfg) / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "prefill_ms_back_to_back_no_flush": b2b,
+    }
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        line["cpu_baseline"] = cpu_baseline(cfg, inp)
+    del g, inp
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        sec = {}
+        for idx in (2, 3):
+            c = I.CONFIGS[idx]
+            log("generating %s" % c.name)
+            ii = I.config_inputs(idx)
+            gg = upload(ii)
+            del ii
+            steps = max(3, args.steps // 2)
+            log("timing prefill %s" % c.name)
+            tt, bb = time_prefill(c, gg, steps, max(1, args.warmup // 2), flush=not args.no_flush)
+            m = float(np.mean(tt))
+            nb = prefill_bytes(c)
+            sec[c.name] = {"tokens_per_s": c.batch * c.seqlen / (m * 1e-3), "ms": m,
+                           "ms_back_to_back_no_flush": bb, "hbm_gbs": nb / (m * 1e-3) / 1e9,
+                           "hbm_frac": nb / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "mfma_frac": prefill_flops(c) / (m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                           "algorithmic_bytes": nb, "chunk": c.chunk}
+            del gg
+            torch.cuda.empty_cache()
+        c = I.CONFIGS[4]
+        log("generating %s" % c.name)
+        ii = I.decode_config_inputs()
+        gg = upload(ii)
+        del ii
+        log("timing decode: %d steps x 3" % args.decode_steps)
+        us = time_decode(c, gg, args.decode_steps, 10) * 1e3
+        nb = decode_bytes(c)
+        gbs = nb / (us * 1e-6) / 1e9
+        sec[c.name] = {"us_per_step": us, "hbm_gbs": gbs,
+                       "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": gbs,
+                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": gbs / HBM_PEAK_GBS,
+                                    "traffic": measured_traffic("decode_config4"),
+                                    "algorithmic_bytes": nb}}
+        line["secondary"] = sec
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

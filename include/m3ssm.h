@@ -104,8 +104,8 @@ size_t m3_prefill_workspace_size(const m3_dims* dims, int chunk, m3_dtype dtype)
  * recurrence on the state (explainer: parallel inside a chunk, recurrent
  * across chunks).  T need not be a multiple of chunk.
  *
- * Alignment: x 16 bytes; B and C two elements; y, dt, lam, theta, A and
- * h_final one element.
+ * Alignment: x, B, C and theta 16 bytes; y, dt, lam, A and h_final one
+ * element.
  *
  * workspace: device scratch of at least m3_prefill_workspace_size() bytes,
  * 256-byte aligned, owned by the caller, not read before being written.

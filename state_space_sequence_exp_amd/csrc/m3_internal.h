@@ -10,14 +10,17 @@
 
 namespace m3 {
 
-constexpr int kThreads = 256;     // threads per block of every prefill kernel
+constexpr int kThreads = 512;     // threads per prefill workgroup (8 waves)
 constexpr int kLMax = 128;        // largest chunk (tokens)
 constexpr int kLRMax = 256;       // largest chunk * R (rows of a chunk tile)
 constexpr size_t kLdsLimit = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr int kMaxStTiles = 4;    // 16x16 state tiles per wave (N * P <= 8192)
 
 // Shape of one prefill problem plus device pointers (all validated).
 struct PrefillArgs {
   int nb, T, H, P, N, R, L, nC;
+  int K;     // chunks per segment (one workgroup walks one segment)
+  int nSeg;  // segments per sequence
   const void* x;
   const float* dt;
   const float* A;
@@ -28,10 +31,10 @@ struct PrefillArgs {
   void* y;
   float* h_final;
   // workspace carve
-  float* S;       // [B*H][nC][P][N] chunk-local states (float)
-  void* G;        // [B*H][nC][P][N] chunk entry states (storage type)
-  float* decay;   // [B*H][nC]       exp of the chunk's summed log-decay
-  float2* rot;    // [B*H][nC][N/2]  (cos, sin) of the chunk's summed angle
+  float* ring;   // [B*H][2][N][P] exit states of the two most recent segments
+  int* flags;    // [B*H] segments of each sequence whose exit state is published
+  int* ticket;   // [1]   next segment ticket (work order)
+  int* err;      // [1]   nonzero if a wait for a predecessor timed out
 };
 
 struct DecodeArgs {
@@ -43,23 +46,30 @@ struct DecodeArgs {
   void* y;
 };
 
-// LDS layout of one chunk tile, identical on host and device.
-struct ChunkLayout {
-  int LR;      // rows of the chunk tile (tokens * R)
-  int LRpad;   // LR rounded up to 32
-  int ldN;     // leading dim of [rows][N] tiles (elements)
-  int ldK;     // leading dim of [cols][LRpad] tiles (elements)
-  uint32_t off_scal, off_part, off_a, off_b, off_xt, total;  // byte offsets
-};
-
 __host__ __device__ inline uint32_t align_up_u32(uint32_t v, uint32_t a) {
   return (v + a - 1) / a * a;
 }
 
-// out_kernel: tiles C~ [LRpad][ldN] (off_a), B~ [LRpad][ldN] (off_b), X^T [P][ldK].
-// state kernel: (B~ * coef)^T [N][ldK] (off_a), X^T [P][ldK]; off_b unused.
-__host__ __device__ inline ChunkLayout chunk_layout(int L, int R, int N, int P, int esize,
-                                                    bool out_kernel) {
+// LDS layout of the prefill workgroup, identical on host and device.
+struct ChunkLayout {
+  int LR;      // rows of the chunk tile (tokens * R)
+  int LRpad;   // LR rounded up to 32
+  int ldN;     // leading dim of [rows][N] tiles and of the [P][N] state copy
+  int ldK;     // leading dim of the [P][LRpad] X^T tile
+  // byte offsets
+  uint32_t off_dtr, off_lamr, off_cs, off_gam, off_om, off_dt, off_w;  // per-token floats
+  uint32_t off_part;     // 2 * kThreads floats: angle partial sums (hi, lo)
+  uint32_t off_crot;     // N/2 float2: (cos, sin) of the chunk's total angle
+  uint32_t off_srot;     // N/2 float2: (cos, sin) of the segment's total angle
+  uint32_t off_sang;     // N floats: segment angle sums (hi[N/2], lo[N/2])
+  uint32_t off_th;       // [L][N/2] floats: theta of the chunk
+  uint32_t off_C, off_B; // [LRpad][ldN] C~ and B~
+  uint32_t off_XT;       // [P][ldK] X^T
+  uint32_t off_G;        // [P][ldN] state copy for the inter-chunk term
+  uint32_t total;
+};
+
+__host__ __device__ inline ChunkLayout chunk_layout(int L, int R, int N, int P, int esize) {
   ChunkLayout c;
   c.LR = L * R;
   c.LRpad = (c.LR + 31) / 32 * 32;
@@ -67,23 +77,46 @@ __host__ __device__ inline ChunkLayout chunk_layout(int L, int R, int N, int P, 
   c.ldN = N + pad;
   c.ldK = c.LRpad + pad;
   uint32_t o = 0;
-  c.off_scal = o;
-  o += 4 * kLMax * 4;
-  c.off_part = o;
-  o += 2 * kThreads * 4;
-  c.off_a = o;
-  if (out_kernel) {
-    o = align_up_u32(o + (uint32_t)c.LRpad * c.ldN * esize, 16);
-    c.off_b = o;
-    o = align_up_u32(o + (uint32_t)c.LRpad * c.ldN * esize, 16);
-  } else {
-    o = align_up_u32(o + (uint32_t)N * c.ldK * esize, 16);
-    c.off_b = o;
-  }
-  c.off_xt = o;
-  o = align_up_u32(o + (uint32_t)P * c.ldK * esize, 16);
+  const uint32_t tokf = (kLMax + 4) * 4;
+  c.off_dtr = o; o += tokf;
+  c.off_lamr = o; o += tokf;
+  c.off_cs = o; o += tokf;
+  c.off_gam = o; o += tokf;
+  c.off_om = o; o += tokf;
+  c.off_dt = o; o += tokf;
+  c.off_w = o; o += tokf;
+  c.off_part = o; o += 2 * kThreads * 4;
+  c.off_crot = o; o += (uint32_t)(N / 2) * 8;
+  c.off_srot = o; o += (uint32_t)(N / 2) * 8;
+  c.off_sang = o; o += (uint32_t)N * 4;
+  o = align_up_u32(o, 16);
+  c.off_th = o; o = align_up_u32(o + (uint32_t)L * (N / 2) * 4, 16);
+  c.off_C = o; o = align_up_u32(o + (uint32_t)c.LRpad * c.ldN * esize, 16);
+  c.off_B = o; o = align_up_u32(o + (uint32_t)c.LRpad * c.ldN * esize, 16);
+  c.off_XT = o; o = align_up_u32(o + (uint32_t)P * c.ldK * esize, 16);
+  c.off_G = o; o = align_up_u32(o + (uint32_t)P * c.ldN * esize, 16);
   c.total = o;
   return c;
+}
+
+// 16-byte vectors per thread needed to stage the largest input tile of a
+// chunk (B/C, x or theta).
+__host__ __device__ inline int chunk_stage_vectors(int L, int R, int N, int P, int esize) {
+  const int vecN = L * R * N * esize / 16, vecP = L * R * P * esize / 16;
+  const int vecTh = L * (N / 2) * 4 / 16;
+  int m = vecN > vecP ? vecN : vecP;
+  m = m > vecTh ? m : vecTh;
+  return (m + kThreads - 1) / kThreads;
+}
+
+// Shapes the prefill kernel handles: staging of at most four vectors per
+// thread per tile, at most four state tiles per wave, rows of whole 16-byte
+// vectors that evenly divide the workgroup.
+__host__ __device__ inline bool chunk_fits_registers(int L, int R, int N, int P, int esize) {
+  const int vprN = N * esize / 16, vprP = P * esize / 16, vprT = N / 8;
+  return chunk_stage_vectors(L, R, N, P, esize) <= 4 &&
+         (N / 16) * (P / 16) <= kMaxStTiles * (kThreads / 64) && (N / 2) % 4 == 0 &&
+         kThreads % vprN == 0 && kThreads % vprP == 0 && kThreads % vprT == 0;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, m3_dtype dtype, hipStream_t stream);
@@ -91,5 +124,8 @@ hipError_t launch_decode(const DecodeArgs& a, m3_dtype dtype, hipStream_t stream
 
 // Largest N the decode kernel handles for a given P.
 int decode_max_n(int P);
+
+// Chunks per segment (one prefill workgroup walks one segment).
+int prefill_segment_chunks(int nb, int H, int nC);
 
 }  // namespace m3

@@ -39,32 +39,29 @@ m3_status check_prefill_shape(const m3_dims* d, int chunk, m3_dtype dtype) {
       d->batch * d->nheads * (nC > 0 ? nC : 1) > INT_MAX)
     return M3_ERR_NOT_SUPPORTED;
   const int es = (int)esize_of(dtype);
-  const ChunkLayout lo = m3::chunk_layout(chunk, (int)d->rank_r, (int)d->dstate_n,
-                                          (int)d->headdim_p, es, true);
-  const ChunkLayout ls = m3::chunk_layout(chunk, (int)d->rank_r, (int)d->dstate_n,
-                                          (int)d->headdim_p, es, false);
-  if (lo.total > m3::kLdsLimit || ls.total > m3::kLdsLimit) return M3_ERR_NOT_SUPPORTED;
+  const ChunkLayout lay = m3::chunk_layout(chunk, (int)d->rank_r, (int)d->dstate_n,
+                                           (int)d->headdim_p, es);
+  if (lay.total > m3::kLdsLimit) return M3_ERR_NOT_SUPPORTED;
+  if (!m3::chunk_fits_registers(chunk, (int)d->rank_r, (int)d->dstate_n, (int)d->headdim_p, es))
+    return M3_ERR_NOT_SUPPORTED;
   return M3_SUCCESS;
 }
 
 struct WsCarve {
-  size_t off_S, off_G, off_decay, off_rot, total;
+  size_t off_ring, off_flags, total;
 };
 
-WsCarve carve(const m3_dims* d, int chunk, m3_dtype dtype) {
+// ring: exit states of the two latest segments of every sequence;
+// flags: per-sequence published-segment counters, then the ticket counter
+// and the error word.
+WsCarve carve(const m3_dims* d, int /*chunk*/, m3_dtype /*dtype*/) {
   WsCarve w;
-  const size_t nC = (size_t)((d->seqlen + chunk - 1) / chunk);
-  const size_t units = (size_t)d->batch * d->nheads * nC;
-  const size_t st = (size_t)d->headdim_p * d->dstate_n;
+  const size_t units = (size_t)d->batch * d->nheads;
   size_t o = 0;
-  w.off_S = o;
-  o = round256(o + units * st * sizeof(float));
-  w.off_G = o;
-  o = round256(o + units * st * esize_of(dtype));
-  w.off_decay = o;
-  o = round256(o + units * sizeof(float));
-  w.off_rot = o;
-  o = round256(o + units * (size_t)(d->dstate_n / 2) * 2 * sizeof(float));
+  w.off_ring = o;
+  o = round256(o + units * 2 * (size_t)d->dstate_n * d->headdim_p * sizeof(float));
+  w.off_flags = o;
+  o = round256(o + (units + 2) * sizeof(int));
   w.total = o;
   return w;
 }
@@ -103,9 +100,9 @@ m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void*
   const uintptr_t es = esize_of(dtype);
   if (work) {
     if (!x || !dt || !A || !lam || !theta || !B || !C || !y) return M3_ERR_INVALID_VALUE;
-    // x is read in 16-byte vectors, B and C in rotation pairs
-    if (!aligned(x, 16) || !aligned(B, 2 * es) || !aligned(C, 2 * es) || !aligned(y, es) ||
-        !aligned(dt, 4) || !aligned(A, 4) || !aligned(lam, 4) || !aligned(theta, 4))
+    // x, B, C and theta are read in 16-byte vectors
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(theta, 16) ||
+        !aligned(y, es) || !aligned(dt, 4) || !aligned(A, 4) || !aligned(lam, 4))
       return M3_ERR_INVALID_VALUE;
   }
   if (h_final && !aligned(h_final, 4)) return M3_ERR_INVALID_VALUE;
@@ -128,6 +125,8 @@ m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void*
   a.R = (int)dims->rank_r;
   a.L = chunk;
   a.nC = (int)((dims->seqlen + chunk - 1) / chunk);
+  a.K = m3::prefill_segment_chunks(a.nb, a.H, a.nC > 0 ? a.nC : 1);
+  a.nSeg = (a.nC + a.K - 1) / a.K;
   a.x = x;
   a.dt = dt;
   a.A = A;
@@ -139,10 +138,10 @@ m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void*
   a.h_final = h_final;
   if (work) {
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    a.S = reinterpret_cast<float*>(ws + w.off_S);
-    a.G = ws + w.off_G;
-    a.decay = reinterpret_cast<float*>(ws + w.off_decay);
-    a.rot = reinterpret_cast<float2*>(ws + w.off_rot);
+    a.ring = reinterpret_cast<float*>(ws + w.off_ring);
+    a.flags = reinterpret_cast<int*>(ws + w.off_flags);
+    a.ticket = a.flags + a.nb * a.H;
+    a.err = a.ticket + 1;
   }
   const hipError_t e = m3::launch_prefill(a, dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;
