@@ -54,36 +54,6 @@ __device__ __forceinline__ float angle_add(float a, float b) {
   return __builtin_fmaf(-k, kTwoPiLo, s);
 }
 
-// An angle in revolutions held as an unevaluated float sum hi + lo, kept
-// reduced to |hi| <= 1/2.  Sums of many angles stay exact to about 2^-40
-// revolutions (error-free two-sum plus a split conversion from radians);
-// a plain float sum of angles near pi drifts by about 1e-6 rad per 64 terms.
-struct RevSum {
-  float hi = 0.f, lo = 0.f;
-
-  // Error-free transformations: FMA contraction would break them.
-  __device__ __forceinline__ void add(float b_hi, float b_lo) {
-#pragma clang fp contract(off)
-    const float t = hi + b_hi;
-    const float bp = t - hi;
-    const float e = (hi - (t - bp)) + (b_hi - bp);
-    lo += e + b_lo;
-    hi = t - __builtin_rintf(t);  // exact: t and its nearest integer are close
-  }
-  // add an angle given in radians
-  __device__ __forceinline__ void add_rad(float rad) {
-#pragma clang fp contract(off)
-    constexpr float kInvHi = 0.15915493667125702f;   // float nearest 1/(2 pi)
-    constexpr float kInvLo = 6.4206382432985265e-09f; // 1/(2 pi) - kInvHi
-    const float p_hi = rad * kInvHi;
-    const float p_lo = __builtin_fmaf(rad, kInvHi, -p_hi) + rad * kInvLo;
-    add(p_hi, p_lo);
-  }
-  __device__ __forceinline__ void add(const RevSum& o) { add(o.hi, o.lo); }
-  __device__ __forceinline__ float revolutions() const { return hi + lo; }
-  __device__ __forceinline__ float radians() const { return (hi + lo) * kTwoPiHi; }
-};
-
 // sin and cos of an angle already reduced to about [-pi, pi], on the hardware
 // sine/cosine (which take revolutions).
 __device__ __forceinline__ void fast_sincos(float a, float* s, float* c) {

@@ -15,6 +15,7 @@ constexpr int kLMax = 128;        // largest chunk (tokens)
 constexpr int kLRMax = 256;       // largest chunk * R (rows of a chunk tile)
 constexpr size_t kLdsLimit = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kMaxStTiles = 4;    // 16x16 state tiles per wave (N * P <= 8192)
+constexpr int kMaxSeg = 16;       // tokens per thread in the per-pair angle scan
 
 // Shape of one prefill problem plus device pointers (all validated).
 struct PrefillArgs {
@@ -58,10 +59,10 @@ struct ChunkLayout {
   int ldK;     // leading dim of the [P][LRpad] X^T tile
   // byte offsets
   uint32_t off_dtr, off_lamr, off_cs, off_gam, off_om, off_dt, off_w;  // per-token floats
-  uint32_t off_part;     // 2 * kThreads floats: angle partial sums (hi, lo)
+  uint32_t off_part;     // kThreads doubles: per-segment angle sums
   uint32_t off_crot;     // N/2 float2: (cos, sin) of the chunk's total angle
   uint32_t off_srot;     // N/2 float2: (cos, sin) of the segment's total angle
-  uint32_t off_sang;     // N floats: segment angle sums (hi[N/2], lo[N/2])
+  uint32_t off_sang;     // N/2 doubles: segment angle sums
   uint32_t off_th;       // [L][N/2] floats: theta of the chunk
   uint32_t off_C, off_B; // [LRpad][ldN] C~ and B~
   uint32_t off_XT;       // [P][ldK] X^T
@@ -85,10 +86,10 @@ __host__ __device__ inline ChunkLayout chunk_layout(int L, int R, int N, int P, 
   c.off_om = o; o += tokf;
   c.off_dt = o; o += tokf;
   c.off_w = o; o += tokf;
-  c.off_part = o; o += 2 * kThreads * 4;
+  c.off_part = o; o += kThreads * 8;
   c.off_crot = o; o += (uint32_t)(N / 2) * 8;
   c.off_srot = o; o += (uint32_t)(N / 2) * 8;
-  c.off_sang = o; o += (uint32_t)N * 4;
+  c.off_sang = o; o += (uint32_t)(N / 2) * 8;
   o = align_up_u32(o, 16);
   c.off_th = o; o = align_up_u32(o + (uint32_t)L * (N / 2) * 4, 16);
   c.off_C = o; o = align_up_u32(o + (uint32_t)c.LRpad * c.ldN * esize, 16);
@@ -114,7 +115,8 @@ __host__ __device__ inline int chunk_stage_vectors(int L, int R, int N, int P, i
 // vectors that evenly divide the workgroup.
 __host__ __device__ inline bool chunk_fits_registers(int L, int R, int N, int P, int esize) {
   const int vprN = N * esize / 16, vprP = P * esize / 16, vprT = N / 8;
-  return chunk_stage_vectors(L, R, N, P, esize) <= 4 &&
+  const int seglen = (L + kThreads / (N / 2) - 1) / (kThreads / (N / 2));
+  return chunk_stage_vectors(L, R, N, P, esize) <= 4 && seglen <= kMaxSeg &&
          (N / 16) * (P / 16) <= kMaxStTiles * (kThreads / 64) && (N / 2) % 4 == 0 &&
          kThreads % vprN == 0 && kThreads % vprP == 0 && kThreads % vprT == 0;
 }

@@ -30,9 +30,9 @@
 // is in the unrotated (API) frame, and the previous token's trapezoid term
 // omega B x^T is folded into it: G_c = h_{cL-1} + omega_{cL-1} B_{cL-1}
 // x_{cL-1}^T.  No halo token is needed inside a chunk and every angle stays
-// bounded by one chunk's sum.  Chunk and segment angle totals are exact
-// double-float sums whose sine/cosine come from sincospif, since the chain
-// multiplies them over the whole sequence.
+// bounded by one chunk's sum.  Chunk and segment angle totals are summed in
+// double and take the accurate sine/cosine, since the chain multiplies their
+// rotations over the whole sequence.
 //
 // Work order and the chain.  Workgroups take tickets from a counter; ticket
 // t is segment t / (B*H) of sequence t % (B*H).  A workgroup only waits for a
@@ -275,16 +275,38 @@ __device__ __forceinline__ void chunk_scalars(const PrefillArgs& a, const ChunkL
   __syncthreads();
   if (tid >= kWave && tid < 2 * kWave) s_cs[tid] += s_cs[kWave - 1];
   __syncthreads();
-  // weight of token u in the chunk's state: exp(cs_end - cs_u) (gamma_u + omega_u)
-  if (tid < a.L) s_w[tid] = __expf(s_cs[a.L - 1] - s_cs[tid]) * (s_gam[tid] + s_om[tid]);
+  // weight of token u in the chunk's state: exp(cs_end - cs_u) (gamma_u + omega_u);
+  // zero past L so that whole-vector reads need no bounds check
+  if (tid < kLMax) s_w[tid] = tid < a.L ? __expf(s_cs[a.L - 1] - s_cs[tid]) * (s_gam[tid] + s_om[tid]) : 0.f;
   __syncthreads();
+}
+
+// R(phi)^T applied in place to the rotation pair at p (two adjacent elements).
+__device__ __forceinline__ void rotate_pair_T(bf16* p, float cn, float sn) {
+  const bf16x2 v = *reinterpret_cast<const bf16x2*>(p);
+  const float x = static_cast<float>(v.x), y = static_cast<float>(v.y);
+  const bf16x2 o = {from_f32<bf16>(cn * x + sn * y), from_f32<bf16>(-sn * x + cn * y)};
+  *reinterpret_cast<bf16x2*>(p) = o;
+}
+__device__ __forceinline__ void rotate_pair_T(float* p, float cn, float sn) {
+  const float2 v = *reinterpret_cast<const float2*>(p);
+  *reinterpret_cast<float2*>(p) = make_float2(cn * v.x + sn * v.y, -sn * v.x + cn * v.y);
+}
+
+// An angle in radians (a double sum of float angles) reduced to [-pi, pi].
+__device__ __forceinline__ double reduce_angle(double a) {
+  constexpr double kTwoPi = 6.283185307179586476925;
+  return a - kTwoPi * __builtin_rint(a * (1.0 / kTwoPi));
 }
 
 // Chunk-local cumulative angles and rotated inputs, in place in LDS: B~
 // (and C~) overwrite the raw rows; the chunk's total rotation goes to crot;
 // with kAccumSeg the chunk's total angle is added to the segment sum.  Thread
-// (pair kp, segment sg) scans tokens [sg*seglen, (sg+1)*seglen).  Ends with a
-// barrier.
+// (pair kp, segment sg) scans tokens [sg*seglen, (sg+1)*seglen): the
+// per-segment and per-chunk angle sums are accumulated in double (they feed
+// the chain, which multiplies the rotations over the whole sequence); the
+// running angle within the segment is a float reduced at every step.  Ends
+// with a barrier.
 template <class C, bool kWithC, bool kAccumSeg>
 __device__ __forceinline__ void chunk_rotate(const PrefillArgs& a, const ChunkLayout& lay,
                                              int len, unsigned char* smem) {
@@ -298,58 +320,40 @@ __device__ __forceinline__ void chunk_rotate(const PrefillArgs& a, const ChunkLa
   const int u0 = sg * seglen, u1 = min(a.L, u0 + seglen);
   const float* s_dt = reinterpret_cast<const float*>(smem + lay.off_dt);
   const float* s_th = reinterpret_cast<const float*>(smem + lay.off_th);
-  float* s_part = reinterpret_cast<float*>(smem + lay.off_part);
+  double* s_part = reinterpret_cast<double*>(smem + lay.off_part);
   float2* s_crot = reinterpret_cast<float2*>(smem + lay.off_crot);
-  float* s_sang = reinterpret_cast<float*>(smem + lay.off_sang);
+  double* s_sang = reinterpret_cast<double*>(smem + lay.off_sang);
   T* sB = reinterpret_cast<T*>(smem + lay.off_B);
   T* sC = reinterpret_cast<T*>(smem + lay.off_C);
 
-  RevSum sum;
   const int ulen = min(u1, len);
-  if (active) {
-    for (int u = u0; u < ulen; ++u) sum.add_rad(s_dt[u] * s_th[u * npair + kp]);
-    s_part[sg * npair + kp] = sum.hi;
-    s_part[(nseg + sg) * npair + kp] = sum.lo;
-  }
+  double sum = 0.0;
+  if (active)
+    for (int u = u0; u < ulen; ++u) sum += static_cast<double>(s_dt[u] * s_th[u * npair + kp]);
+  if (active) s_part[sg * npair + kp] = sum;
   __syncthreads();
   if (active) {
-    RevSum pre;
-    for (int q = 0; q < sg; ++q) pre.add(s_part[q * npair + kp], s_part[(nseg + q) * npair + kp]);
-    float phi = pre.radians();
+    double pre = 0.0;
+    for (int q = 0; q < sg; ++q) pre += s_part[q * npair + kp];
+    float phi = static_cast<float>(reduce_angle(pre));
     for (int u = u0; u < ulen; ++u) {
       phi = angle_add(phi, s_dt[u] * s_th[u * npair + kp]);
       float sn, cn;
       fast_sincos(phi, &sn, &cn);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int row = u * R + r;
-        // R(phi)^T applied to the pair
-        T* pb = sB + row * lay.ldN + 2 * kp;
-        const float2 bv = load_pair(pb);
-        pb[0] = from_f32<T>(cn * bv.x + sn * bv.y);
-        pb[1] = from_f32<T>(-sn * bv.x + cn * bv.y);
-        if constexpr (kWithC) {
-          T* pc = sC + row * lay.ldN + 2 * kp;
-          const float2 cv = load_pair(pc);
-          pc[0] = from_f32<T>(cn * cv.x + sn * cv.y);
-          pc[1] = from_f32<T>(-sn * cv.x + cn * cv.y);
-        }
+        rotate_pair_T(sB + (u * R + r) * lay.ldN + 2 * kp, cn, sn);
+        if constexpr (kWithC) rotate_pair_T(sC + (u * R + r) * lay.ldN + 2 * kp, cn, sn);
       }
     }
     if (u1 == a.L && u0 < a.L) {
-      // total angle of the chunk: exact sum of the segment partial sums
-      pre.add(sum);
+      // the chunk's total angle; the chain multiplies its rotation over the
+      // whole sequence, so it takes the accurate sine/cosine
+      const double tot = pre + sum;
       float sn, cn;
-      sincospif(2.f * pre.revolutions(), &sn, &cn);
+      sincosf(static_cast<float>(reduce_angle(tot)), &sn, &cn);
       s_crot[kp] = make_float2(cn, sn);
-      if constexpr (kAccumSeg) {
-        RevSum sa;
-        sa.hi = s_sang[kp];
-        sa.lo = s_sang[npair + kp];
-        sa.add(pre);
-        s_sang[kp] = sa.hi;
-        s_sang[npair + kp] = sa.lo;
-      }
+      if constexpr (kAccumSeg) s_sang[kp] = reduce_angle(s_sang[kp] + tot);
     }
   }
   __syncthreads();
@@ -370,28 +374,52 @@ __device__ __forceinline__ float load_frag_T(const float* sB, int ldN, int n, in
   return sB[(k0 + g) * ldN + n];
 }
 
+// The 8 token weights of chunk rows row0 .. row0+7 (row0 a multiple of 8);
+// the weights are zero-padded past the chunk.
+template <int R>
+__device__ __forceinline__ void row_weights8(const float* s_w, int row0, float (&w)[8]) {
+  if constexpr (R == 1) {
+    const float4 a = *reinterpret_cast<const float4*>(s_w + row0);
+    const float4 b = *reinterpret_cast<const float4*>(s_w + row0 + 4);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  } else if constexpr (R == 2) {
+    const float4 a = *reinterpret_cast<const float4*>(s_w + row0 / 2);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = e < 2 ? a.x : e < 4 ? a.y : e < 6 ? a.z : a.w;
+  } else {
+    const float2 a = *reinterpret_cast<const float2*>(s_w + row0 / 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = e < 4 ? a.x : a.y;
+  }
+}
+
 // Fragment of X^T row p with every K-slot (a chunk row) scaled by its token's
-// state weight (rows past LR carry zeros in X^T and get weight zero).
+// state weight (rows past LR are zero in X^T and have weight zero).
 template <int R>
 __device__ __forceinline__ bf16x8 load_frag_xw(const bf16* sXT, int ldK, int p, int k0,
-                                               const float* s_w, int LR) {
+                                               const float* s_w) {
   const int g = (threadIdx.x & 63) >> 4;
   const int row0 = k0 + g * 8;
   const bf16x8 x = *reinterpret_cast<const bf16x8*>(sXT + p * ldK + row0);
+  float w[8];
+  row_weights8<R>(s_w, row0, w);
   bf16x8 f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float w = row0 + e < LR ? s_w[(row0 + e) / R] : 0.f;
-    f[e] = from_f32<bf16>(static_cast<float>(x[e]) * w);
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2 h = {from_f32<bf16>(static_cast<float>(x[e]) * w[e]),
+                      from_f32<bf16>(static_cast<float>(x[e + 1]) * w[e + 1])};
+    f[e] = h.x;
+    f[e + 1] = h.y;
   }
   return f;
 }
 template <int R>
 __device__ __forceinline__ float load_frag_xw(const float* sXT, int ldK, int p, int k0,
-                                              const float* s_w, int LR) {
+                                              const float* s_w) {
   const int g = (threadIdx.x & 63) >> 4;
   const int row = k0 + g;
-  return row < LR ? sXT[p * ldK + row] * s_w[row / R] : 0.f;
+  return sXT[p * ldK + row] * s_w[row / R];
 }
 
 // Chunk state S_c = sum_u w_u B~_u x_u^T (MFMA) folded into the running state
@@ -418,7 +446,7 @@ __device__ __forceinline__ void state_update(const PrefillArgs& a, const ChunkLa
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int k0 = 0; k0 < lay.LRpad; k0 += M::K) {
         const typename M::frag fa = load_frag_T(sB, lay.ldN, nt * 16 + li, k0);
-        const typename M::frag fb = load_frag_xw<C::R>(sXT, lay.ldK, pt * 16 + li, k0, s_w, lay.LR);
+        const typename M::frag fb = load_frag_xw<C::R>(sXT, lay.ldK, pt * 16 + li, k0, s_w);
         acc = M::mma(fa, fb, acc);
       }
       const int kq = nt * 8 + 2 * g;
@@ -449,8 +477,44 @@ __device__ __forceinline__ void state_to_lds(const PrefillArgs& a, const ChunkLa
     if (i < ntiles) {
       const int nt = i % ntn, pt = i / ntn;
       T* dst = sG + (pt * 16 + li) * lay.ldN + nt * 16 + 4 * g;
+      if constexpr (sizeof(T) == 2) {
+        const bf16x4 v = {from_f32<bf16>(stt[m][0]), from_f32<bf16>(stt[m][1]),
+                          from_f32<bf16>(stt[m][2]), from_f32<bf16>(stt[m][3])};
+        *reinterpret_cast<bf16x4*>(dst) = v;
+      } else {
+        *reinterpret_cast<f32x4*>(dst) = stt[m];
+      }
+    }
+  }
+}
+
+// cs, gamma, omega of the tokens of chunk rows row0 .. row0+3 (row0 a
+// multiple of 4), as whole-vector LDS reads.
+template <int R>
+__device__ __forceinline__ void key_scalars4(const float* s_cs, const float* s_gam,
+                                             const float* s_om, int row0, float (&cs)[4],
+                                             float (&ga)[4], float (&om)[4]) {
+  if constexpr (R == 1) {
+    const float4 c = *reinterpret_cast<const float4*>(s_cs + row0);
+    const float4 g = *reinterpret_cast<const float4*>(s_gam + row0);
+    const float4 o = *reinterpret_cast<const float4*>(s_om + row0);
+    cs[0] = c.x; cs[1] = c.y; cs[2] = c.z; cs[3] = c.w;
+    ga[0] = g.x; ga[1] = g.y; ga[2] = g.z; ga[3] = g.w;
+    om[0] = o.x; om[1] = o.y; om[2] = o.z; om[3] = o.w;
+  } else if constexpr (R == 2) {
+    const float2 c = *reinterpret_cast<const float2*>(s_cs + row0 / 2);
+    const float2 g = *reinterpret_cast<const float2*>(s_gam + row0 / 2);
+    const float2 o = *reinterpret_cast<const float2*>(s_om + row0 / 2);
+    cs[0] = cs[1] = c.x; cs[2] = cs[3] = c.y;
+    ga[0] = ga[1] = g.x; ga[2] = ga[3] = g.y;
+    om[0] = om[1] = o.x; om[2] = om[3] = o.y;
+  } else {
+    const float c = s_cs[row0 / 4], g = s_gam[row0 / 4], o = s_om[row0 / 4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[j] = from_f32<T>(stt[m][j]);
+    for (int j = 0; j < 4; ++j) {
+      cs[j] = c;
+      ga[j] = g;
+      om[j] = o;
     }
   }
 }
@@ -524,14 +588,16 @@ __device__ __forceinline__ void chunk_output(const PrefillArgs& a, const ChunkLa
       }
 #pragma unroll
       for (int i = 0; i < KB; ++i) {
+        float kcs[4], kga[4], kom[4];
+        key_scalars4<R>(s_cs, s_gam, s_om, (kb + i) * 16 + 4 * g, kcs, kga, kom);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int tk = ((kb + i) * 16 + 4 * g + j) / R;
           float w = 0.f;
           if (tk < tq)
-            w = __expf(csq - s_cs[tk]) * (s_gam[tk] + s_om[tk]);
+            w = __expf(csq - kcs[j]) * (kga[j] + kom[j]);
           else if (tk == tq)
-            w = s_gam[tk];
+            w = kga[j];
           sc[i][j] *= w;
         }
       }
@@ -649,10 +715,10 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   const int npair = a.N / 2;
   const int ntn = a.N / 16, ntiles = ntn * (P / 16);
   const Maps mp = {vec_map(a.N / C::vec), vec_map(P / C::vec), vec_map(a.N / 8)};
-  float* s_sang = reinterpret_cast<float*>(smem + lay.off_sang);
+  double* s_sang = reinterpret_cast<double*>(smem + lay.off_sang);
   float2* s_srot = reinterpret_cast<float2*>(smem + lay.off_srot);
 
-  for (int i = tid; i < a.N; i += kThreads) s_sang[i] = 0.f;
+  for (int i = tid; i < npair; i += kThreads) s_sang[i] = 0.0;
 
   f32x4 stt[kMaxStTiles];
 #pragma unroll
@@ -671,11 +737,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   // ---- phase 2: chain ------------------------------------------------------
   __syncthreads();
   for (int kp = tid; kp < npair; kp += kThreads) {
-    RevSum sa;
-    sa.hi = s_sang[kp];
-    sa.lo = s_sang[npair + kp];
     float sn, cn;
-    sincospif(2.f * sa.revolutions(), &sn, &cn);
+    sincosf(static_cast<float>(s_sang[kp]), &sn, &cn);
     s_srot[kp] = make_float2(cn, sn);
   }
   const float segD = __expf(seg_logdecay);
