@@ -215,6 +215,35 @@ def cpu_baseline(cfg, inp, budget_s=20.0):
                       % (n, nunits, cfg.seqlen, dt)}
 
 
+def counter_sequence():
+    """Fixed, untimed workload for hardware-counter runs (see --counters)."""
+    import torch
+    import state_space_sequence_exp_amd as m3
+    from state_space_sequence_exp_amd import inputs as I
+    for idx, reps in ((1, 3), (3, 1)):
+        cfg = I.CONFIGS[idx]
+        g = upload(I.config_inputs(idx))
+        for _ in range(reps):
+            m3.prefill(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"], cfg.chunk)
+        torch.cuda.synchronize()
+        del g
+    c = I.CONFIGS[4]
+    g = upload(I.decode_config_inputs(ring=2))
+    h = g["h0"].clone()
+    for t in range(10):
+        cur, prev = t % 2, (t + 1) % 2
+        m3.decode_step(h, g["x"][cur], g["x"][prev], g["B"][cur], g["B"][prev], g["C"][cur],
+                       g["dt"][cur], g["A"], g["lam"][cur], g["theta"][cur])
+    torch.cuda.synchronize()
+    del g, h
+    src = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("counter sequence done (copy of %d bytes)" % (src.numel() * 4))
+
+
 # ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -225,6 +254,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the MALL between steps")
+    ap.add_argument("--counters", action="store_true",
+                    help="short untimed sequence for rocprofv3 counter runs: SISO prefill x3, "
+                         "long SISO prefill x1, 10 decode steps, and a 512 MiB device copy x3 "
+                         "(the copy calibrates the byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -242,6 +275,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     m3.load_library()
+    if args.counters:
+        counter_sequence()
+        return
 
     # ---- headline: SISO prefill (configuration 1) ----
     cfg = I.CONFIGS[1]
