@@ -10,12 +10,11 @@
 
 namespace m3 {
 
-constexpr int kThreads = 512;     // threads per prefill workgroup (8 waves)
-constexpr int kLMax = 128;        // largest chunk (tokens)
-constexpr int kLRMax = 256;       // largest chunk * R (rows of a chunk tile)
+constexpr int kPrefillThreads = 1024;     // threads per prefill workgroup (16 waves, one per CU)
+constexpr int kLMax = 128;                // largest chunk (tokens)
+constexpr int kLRMax = 256;               // largest chunk * R (rows of a chunk tile)
 constexpr size_t kLdsLimit = 160 * 1024;  // LDS per workgroup on gfx950
-constexpr int kMaxStTiles = 4;    // 16x16 state tiles per wave (N * P <= 8192)
-constexpr int kMaxSeg = 16;       // tokens per thread in the per-pair angle scan
+constexpr int kMaxStTiles = 2;            // 16x16 state tiles per wave (N * P <= 8192)
 
 // Shape of one prefill problem plus device pointers (all validated).
 struct PrefillArgs {
@@ -51,78 +50,86 @@ __host__ __device__ inline uint32_t align_up_u32(uint32_t v, uint32_t a) {
   return (v + a - 1) / a * a;
 }
 
-// LDS layout of the prefill workgroup, identical on host and device.
-struct ChunkLayout {
-  int LR;      // rows of the chunk tile (tokens * R)
-  int LRpad;   // LR rounded up to 32
-  int ldN;     // leading dim of [rows][N] tiles and of the [P][N] state copy
-  int ldK;     // leading dim of the [P][LRpad] X^T tile
-  // byte offsets
-  uint32_t off_dtr, off_lamr, off_cs, off_gam, off_om, off_dt, off_w;  // per-token floats
-  uint32_t off_part;     // kThreads doubles: per-segment angle sums
-  uint32_t off_crot;     // N/2 float2: (cos, sin) of the chunk's total angle
-  uint32_t off_srot;     // N/2 float2: (cos, sin) of the segment's total angle
-  uint32_t off_sang;     // N/2 doubles: segment angle sums
-  uint32_t off_th;       // [L][N/2] floats: theta of the chunk
-  uint32_t off_C, off_B; // [LRpad][ldN] C~ and B~
-  uint32_t off_XT;       // [P][ldK] X^T
-  uint32_t off_G;        // [P][ldN] state copy for the inter-chunk term
+// Tokens per rotation item: one thread rotates one pair of B (and C) rows
+// over this many consecutive tokens (and all R ranks of each token).
+__host__ __device__ constexpr int prefill_item_tokens(int esize, int R) {
+  return esize == 2 ? (R == 1 ? 4 : 2) : (R == 4 ? 1 : 4 / R);
+}
+
+// Per-token scalars of one chunk, one of two alternating buffers:
+// cs, gamma, gamma + omega and the state weight w (kLMax floats each), then
+// the chunk's log-decay.
+constexpr uint32_t kScalBytes = (4 * kLMax + 4) * 4;
+
+// LDS layout of the prefill workgroup, identical on host and device.  The
+// five chunk tiles are stored without padding; their 16-byte columns are
+// XOR-swizzled by row (see the kernel) so MFMA fragment reads do not
+// collide in the LDS banks.
+struct PrefillLayout {
+  int LR;      // rows of a chunk tile (tokens * R)
+  int LRp;     // LR rounded up to the MFMA contraction length
+  int S;       // tokens per rotation item
+  int npair;   // N / 2
+  int nblk;    // token blocks per chunk (L / S)
+  int items;   // rotation items (npair * nblk)
+  int xitems;  // x items ((P / 2) * nblk)
+  uint32_t off_scal;   // 2 x kScalBytes
+  uint32_t off_part;   // items doubles: per-item angle sums
+  uint32_t off_crot;   // npair float2: (cos, sin) of the chunk's total angle
+  uint32_t off_srot;   // npair float2: (cos, sin) of the segment's total angle
+  uint32_t off_sang;   // npair doubles: segment angle sums
+  uint32_t off_misc;   // 16 bytes: the workgroup's ticket
+  uint32_t off_Cr;     // [LR][N]   C~ (rotated C)
+  uint32_t off_Br;     // [LR][N]   B~ (rotated B)
+  uint32_t off_BwT;    // [N][LRp]  B~ weighted by each token's state weight, transposed
+  uint32_t off_XT;     // [P][LRp]  x transposed
+  uint32_t off_GT;     // [P][N]    chunk entry state, transposed
   uint32_t total;
 };
 
-__host__ __device__ inline ChunkLayout chunk_layout(int L, int R, int N, int P, int esize) {
-  ChunkLayout c;
+__host__ __device__ inline PrefillLayout prefill_layout(int L, int R, int N, int P, int esize) {
+  PrefillLayout c;
   c.LR = L * R;
-  c.LRpad = (c.LR + 31) / 32 * 32;
-  const int pad = 16 / esize;
-  c.ldN = N + pad;
-  c.ldK = c.LRpad + pad;
+  c.LRp = esize == 2 ? (c.LR + 31) / 32 * 32 : c.LR;
+  c.S = prefill_item_tokens(esize, R);
+  c.npair = N / 2;
+  c.nblk = L / c.S;
+  c.items = c.npair * c.nblk;
+  c.xitems = (P / 2) * c.nblk;
   uint32_t o = 0;
-  const uint32_t tokf = (kLMax + 4) * 4;
-  c.off_dtr = o; o += tokf;
-  c.off_lamr = o; o += tokf;
-  c.off_cs = o; o += tokf;
-  c.off_gam = o; o += tokf;
-  c.off_om = o; o += tokf;
-  c.off_dt = o; o += tokf;
-  c.off_w = o; o += tokf;
-  c.off_part = o; o += kThreads * 8;
-  c.off_crot = o; o += (uint32_t)(N / 2) * 8;
-  c.off_srot = o; o += (uint32_t)(N / 2) * 8;
-  c.off_sang = o; o += (uint32_t)(N / 2) * 8;
+  c.off_scal = o; o += 2 * kScalBytes;
+  c.off_part = o; o += (uint32_t)c.items * 8;
+  c.off_crot = o; o += (uint32_t)c.npair * 8;
+  c.off_srot = o; o += (uint32_t)c.npair * 8;
+  c.off_sang = o; o += (uint32_t)c.npair * 8;
+  c.off_misc = o; o += 16;
   o = align_up_u32(o, 16);
-  c.off_th = o; o = align_up_u32(o + (uint32_t)L * (N / 2) * 4, 16);
-  c.off_C = o; o = align_up_u32(o + (uint32_t)c.LRpad * c.ldN * esize, 16);
-  c.off_B = o; o = align_up_u32(o + (uint32_t)c.LRpad * c.ldN * esize, 16);
-  c.off_XT = o; o = align_up_u32(o + (uint32_t)P * c.ldK * esize, 16);
-  c.off_G = o; o = align_up_u32(o + (uint32_t)P * c.ldN * esize, 16);
+  c.off_Cr = o; o += (uint32_t)c.LR * N * esize;
+  c.off_Br = o; o += (uint32_t)c.LR * N * esize;
+  c.off_BwT = o; o += (uint32_t)N * c.LRp * esize;
+  c.off_XT = o; o += (uint32_t)P * c.LRp * esize;
+  c.off_GT = o; o += (uint32_t)P * N * esize;
   c.total = o;
   return c;
 }
 
-// 16-byte vectors per thread needed to stage the largest input tile of a
-// chunk (B/C, x or theta).
-__host__ __device__ inline int chunk_stage_vectors(int L, int R, int N, int P, int esize) {
-  const int vecN = L * R * N * esize / 16, vecP = L * R * P * esize / 16;
-  const int vecTh = L * (N / 2) * 4 / 16;
-  int m = vecN > vecP ? vecN : vecP;
-  m = m > vecTh ? m : vecTh;
-  return (m + kThreads - 1) / kThreads;
-}
-
-// Shapes the prefill kernel handles: staging of at most four vectors per
-// thread per tile, at most four state tiles per wave, rows of whole 16-byte
-// vectors that evenly divide the workgroup.
-__host__ __device__ inline bool chunk_fits_registers(int L, int R, int N, int P, int esize) {
-  const int vprN = N * esize / 16, vprP = P * esize / 16, vprT = N / 8;
-  const int seglen = (L + kThreads / (N / 2) - 1) / (kThreads / (N / 2));
-  return chunk_stage_vectors(L, R, N, P, esize) <= 4 && seglen <= kMaxSeg &&
-         (N / 16) * (P / 16) <= kMaxStTiles * (kThreads / 64) && (N / 2) % 4 == 0 &&
-         kThreads % vprN == 0 && kThreads % vprP == 0 && kThreads % vprT == 0;
+// Shapes the prefill kernel handles beyond the LDS limit: at most two state
+// tiles per wave, at most one rotation item and one x item per thread, and
+// byte offsets within one chunk that fit 30 bits.
+__host__ __device__ inline bool prefill_shape_fits(int L, int R, int N, int P, int H, int esize) {
+  const PrefillLayout lay = prefill_layout(L, R, N, P, esize);
+  const long long row = (long long)H * R * (N > P ? N : P) * esize;
+  return (N / 16) * (P / 16) <= kMaxStTiles * (kPrefillThreads / 64) &&
+         lay.items <= kPrefillThreads && lay.xitems <= kPrefillThreads &&
+         (long long)L * row < (1ll << 30);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, m3_dtype dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, m3_dtype dtype, hipStream_t stream);
+
+// Per-dtype prefill launchers (one translation unit each).
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
 // Largest N the decode kernel handles for a given P.
 int decode_max_n(int P);

@@ -10,8 +10,6 @@
 
 namespace {
 
-using m3::ChunkLayout;
-
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 size_t round256(size_t v) { return (v + 255) / 256 * 256; }
@@ -39,10 +37,11 @@ m3_status check_prefill_shape(const m3_dims* d, int chunk, m3_dtype dtype) {
       d->batch * d->nheads * (nC > 0 ? nC : 1) > INT_MAX)
     return M3_ERR_NOT_SUPPORTED;
   const int es = (int)esize_of(dtype);
-  const ChunkLayout lay = m3::chunk_layout(chunk, (int)d->rank_r, (int)d->dstate_n,
-                                           (int)d->headdim_p, es);
+  const m3::PrefillLayout lay = m3::prefill_layout(chunk, (int)d->rank_r, (int)d->dstate_n,
+                                                   (int)d->headdim_p, es);
   if (lay.total > m3::kLdsLimit) return M3_ERR_NOT_SUPPORTED;
-  if (!m3::chunk_fits_registers(chunk, (int)d->rank_r, (int)d->dstate_n, (int)d->headdim_p, es))
+  if (!m3::prefill_shape_fits(chunk, (int)d->rank_r, (int)d->dstate_n, (int)d->headdim_p,
+                              (int)d->nheads, es))
     return M3_ERR_NOT_SUPPORTED;
   return M3_SUCCESS;
 }

@@ -1,0 +1,942 @@
+// prefill_impl.h -- the fused chunked prefill kernel of the Mamba-3
+// recurrence on gfx950, templated on storage type, MIMO rank and head
+// dimension.  Included by one translation unit per storage type.
+//
+// The sequence of each (batch b, head h) is cut into chunks of L tokens and
+// the chunks into segments of K chunks.  One workgroup (1024 threads, one per
+// CU) owns one segment and runs three phases:
+//
+//  1. Local pass.  For each chunk: per-token log-decay prefix sums cs_u,
+//     trapezoid weights gamma_u = lam_u dt_u and omega_u = (1 - lam_{u+1})
+//     dt_{u+1}, chunk-local cumulative angles phi_u[k] (per rotation pair),
+//     rotated inputs B~_u = R(phi_u)^T B_u (the data-dependent RoPE of
+//     Proposition 3, Mamba-3 paper summary), the chunk state
+//     S_c = sum_u exp(cs_e - cs_u)(gamma_u + omega_u) B~_u x_u^T on MFMA, and
+//     the chunk-level recurrence G <- R(Phi_c)(exp(cs_e) G + S_c) from G = 0.
+//     The result is the segment's exit state for a zero entry state, plus the
+//     segment's total decay and total angle.
+//  2. Chain.  Wait for the exit state of the previous segment of the same
+//     sequence, combine (the recurrence is linear: E_exit = R(Phi)(D E_entry)
+//     + E_local), publish this segment's exit state.
+//  3. Output pass.  Walk the chunks again from the true entry state:
+//         y_t = exp(cs_t) C~_t^T G_c
+//             + sum_{u<=t} exp(cs_t - cs_u)(gamma_u + [u<t] omega_u)(C~_t^T B~_u) x_u^T
+//     i.e. the chunk's structured mask (decay matrix x 2-band trapezoid
+//     matrix; Mamba-3 paper translation, section 3.1, equation 7) applied to
+//     C~ B~^T on MFMA, plus the inter-chunk term, then the same chunk-level
+//     recurrence to the next chunk.
+//
+// Frames.  Angles restart at every chunk, so the entry state G_c of a chunk
+// is in the unrotated (API) frame, and the previous token's trapezoid term
+// omega B x^T is folded into it: G_c = h_{cL-1} + omega_{cL-1} B_{cL-1}
+// x_{cL-1}^T.  No halo token is needed inside a chunk.  Running angles inside
+// a chunk are kept in revolutions, reduced to [0, 1) at every token (the
+// hardware sine takes revolutions); chunk and segment totals are summed in
+// double and take the accurate sine/cosine, since the chain multiplies their
+// rotations over the whole sequence.
+//
+// One chunk step, per workgroup:
+//   [P] every thread sums dt*theta over its rotation item (one rotation pair,
+//       S consecutive tokens) from registers staged a chunk ahead; wave 0
+//       computes the per-token scalars.                          -- barrier
+//   [R] every thread finishes its item's angles from the other items' sums,
+//       rotates its B (and C) pairs and writes B~, C~ and the weighted,
+//       transposed B~ into LDS; x goes to LDS transposed; the next chunk's
+//       inputs are requested.                                     -- barrier
+//   [F] MFMA: outputs (phase 3) and the chunk state, folded into the state
+//       tiles held in registers.
+// The per-token scalars alternate between two LDS buffers, so [P] of the next
+// chunk does not wait for [F] of this one.
+//
+// Memory.  Inputs are read with buffer loads whose range ends at the last
+// valid byte of the chunk's sequence, so rows past the end of a sequence
+// read as zero and y rows past it are dropped by the buffer store.  The five
+// chunk tiles live unpadded in LDS with each 16-byte column XOR-swizzled by
+// row, so the MFMA fragment reads (16 lanes on 16 rows of one column) hit
+// distinct banks.
+//
+// Work order and the chain.  Workgroups take tickets from a counter; ticket
+// t is segment t / (B*H) of sequence t % (B*H).  A workgroup only waits for a
+// smaller ticket, which is held by a running workgroup, so the grid always
+// drains.  Exit states travel through a two-slot ring per sequence with
+// device-coherent (sc1) stores and loads, and a per-sequence counter that is
+// raised only after the stores have completed; the wait is bounded and
+// raises an error word instead of hanging.
+#pragma once
+
+#include "m3_device.h"
+#include "m3_internal.h"
+
+namespace m3 {
+namespace pf {
+
+constexpr int kT = kPrefillThreads;
+constexpr int kW = kT / kWave;             // waves per workgroup
+constexpr int kSpinLimit = 1 << 18;        // bounded wait (a few hundred ms)
+constexpr int kRsrcWord3 = 0x00020000;     // raw buffer descriptor, gfx9 family
+constexpr uint32_t kOOB = 0x7ff00000u;     // a buffer offset past every range
+constexpr double kInv2PiD = 0.15915494309189533577;
+
+typedef __amdgpu_buffer_rsrc_t rsrc;
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ uint32_t ld32(rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 ld64(rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2 v = {from_f32<bf16>(lo), from_f32<bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// A [rows][row_bytes] tile in LDS whose 16-byte columns are XOR-swizzled by
+// row within aligned groups of up to 8 columns.
+struct Tile {
+  unsigned char* base;
+  uint32_t rowb, mask;
+  __device__ __forceinline__ uint32_t at(uint32_t row, uint32_t byte) const {
+    return row * rowb + ((((byte >> 4) ^ (row & mask)) << 4) | (byte & 15u));
+  }
+  template <typename V>
+  __device__ __forceinline__ V& ref(uint32_t row, uint32_t byte) const {
+    return *reinterpret_cast<V*>(base + at(row, byte));
+  }
+};
+__device__ __forceinline__ Tile make_tile(unsigned char* base, uint32_t rowb) {
+  const uint32_t ncol = rowb >> 4;
+  const uint32_t low = ncol & (0u - ncol);
+  return Tile{base, rowb, (low < 8u ? low : 8u) - 1u};
+}
+
+template <typename T_, int R_, int P_>
+struct Cfg {
+  using T = T_;
+  using M = Mfma<T_>;
+  static constexpr int R = R_, P = P_;
+  static constexpr int es = (int)sizeof(T_);
+  static constexpr int S = prefill_item_tokens(es, R_);  // tokens per rotation item
+  static constexpr int KR = S * R_;                      // chunk rows per item
+  static constexpr int PW = es / 2;                      // 32-bit words per pair
+  static constexpr int NPT = P_ / 16;                    // p-tiles
+};
+
+// Raw inputs of one chunk for this thread, staged in registers.
+template <class C>
+struct Stage {
+  float th[C::S], dt[C::S];                                  // rotation item
+  uint32_t b[C::KR * C::PW], c[C::KR * C::PW], x[C::KR * C::PW];
+  float wd[3], wl[3];                                        // wave 0: dt, lam
+};
+
+// Uniform per-workgroup values.
+struct Ctx {
+  int b, h, bh, seg, c0, c1;
+  uint32_t rowB, rowTh, rowDt, rowX;  // token strides in bytes
+  float Ah;
+};
+
+// This thread's rotation item (pair kp, token block blk) and x item (column
+// pair jp, token block xblk).
+struct Map {
+  int kp, blk, jp, xblk;
+  bool act, xact;
+};
+
+struct ChunkRes {
+  rsrc B, C, th, dt, x;
+  int t0, len;
+};
+
+template <class C>
+__device__ __forceinline__ ChunkRes chunk_res(const PrefillArgs& a, const Ctx& s, int c) {
+  ChunkRes r;
+  r.t0 = c * a.L;
+  r.len = min(a.L, a.T - r.t0);
+  const size_t hrow = ((size_t)s.b * a.T + r.t0) * a.H + s.h;  // [B,T,H] row of token t0
+  const uint32_t last = (uint32_t)(r.len - 1);
+  const uint32_t bcb = (uint32_t)(C::R * a.N * C::es);
+  r.B = make_rsrc(static_cast<const unsigned char*>(a.B) + hrow * bcb, last * s.rowB + bcb);
+  r.C = make_rsrc(static_cast<const unsigned char*>(a.C) + hrow * bcb, last * s.rowB + bcb);
+  r.th = make_rsrc(a.theta + hrow * (a.N / 2), last * s.rowTh + (uint32_t)(a.N / 2) * 4);
+  r.dt = make_rsrc(a.dt + hrow, last * s.rowDt + 4);
+  const uint32_t xb = (uint32_t)(C::R * C::P * C::es);
+  r.x = make_rsrc(static_cast<const unsigned char*>(a.x) + hrow * xb, last * s.rowX + xb);
+  return r;
+}
+
+// Rotation-item inputs (theta, dt, B and optionally C) of item (kp, blk).
+template <class C, bool kWithC>
+__device__ __forceinline__ void load_item(const PrefillArgs& a, const Ctx& s, const ChunkRes& r,
+                                          uint32_t vB, uint32_t vTh, uint32_t vDt,
+                                          float (&th)[C::S], float (&dt)[C::S],
+                                          uint32_t (&bv)[C::KR * C::PW],
+                                          uint32_t (&cv)[C::KR * C::PW]) {
+#pragma unroll
+  for (int j = 0; j < C::S; ++j) {
+    th[j] = __uint_as_float(ld32(r.th, vTh + j * s.rowTh));
+    dt[j] = __uint_as_float(ld32(r.dt, vDt + j * s.rowDt));
+  }
+#pragma unroll
+  for (int j = 0; j < C::S; ++j)
+#pragma unroll
+    for (int q = 0; q < C::R; ++q) {
+      const uint32_t o = vB + j * s.rowB + (uint32_t)(q * a.N * C::es);
+      const int i = j * C::R + q;
+      if constexpr (C::PW == 1) {
+        bv[i] = ld32(r.B, o);
+        if constexpr (kWithC) cv[i] = ld32(r.C, o);
+      } else {
+        const u32x2 v = ld64(r.B, o);
+        bv[2 * i] = v.x;
+        bv[2 * i + 1] = v.y;
+        if constexpr (kWithC) {
+          const u32x2 w = ld64(r.C, o);
+          cv[2 * i] = w.x;
+          cv[2 * i + 1] = w.y;
+        }
+      }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void load_x_item(const Ctx& s, const ChunkRes& r, uint32_t vX,
+                                            uint32_t (&xv)[C::KR * C::PW]) {
+#pragma unroll
+  for (int j = 0; j < C::S; ++j)
+#pragma unroll
+    for (int q = 0; q < C::R; ++q) {
+      const uint32_t o = vX + j * s.rowX + (uint32_t)(q * C::P * C::es);
+      const int i = j * C::R + q;
+      if constexpr (C::PW == 1) {
+        xv[i] = ld32(r.x, o);
+      } else {
+        const u32x2 v = ld64(r.x, o);
+        xv[2 * i] = v.x;
+        xv[2 * i + 1] = v.y;
+      }
+    }
+}
+
+// Request all of this thread's inputs of chunk c.
+template <class C, bool kWithC>
+__device__ __forceinline__ void issue_loads(const PrefillArgs& a, const Ctx& s, const Map& m,
+                                            int c, Stage<C>& st) {
+  const ChunkRes r = chunk_res<C>(a, s, c);
+  // chunk-relative byte offsets of this thread's items (past every range if
+  // it has none, so the loads return zeros)
+  const uint32_t tb = (uint32_t)(m.blk * C::S);
+  const uint32_t vB = m.act ? tb * s.rowB + (uint32_t)(2 * m.kp * C::es) : kOOB;
+  const uint32_t vTh = m.act ? tb * s.rowTh + (uint32_t)(m.kp * 4) : kOOB;
+  const uint32_t vDt = m.act ? tb * s.rowDt : kOOB;
+  const uint32_t vX = m.xact ? (uint32_t)(m.xblk * C::S) * s.rowX + (uint32_t)(2 * m.jp * C::es)
+                             : kOOB;
+  load_item<C, kWithC>(a, s, r, vB, vTh, vDt, st.th, st.dt, st.b, st.c);
+  load_x_item<C>(s, r, vX, st.x);
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) {
+    // dt and lam of tokens lane, lane + 64, lane + 128, up to the end of the
+    // sequence (the token after the chunk feeds omega of its last token)
+    const size_t hrow = ((size_t)s.b * a.T + r.t0) * a.H + s.h;
+    const uint32_t bytes = (uint32_t)(a.T - r.t0 - 1) * s.rowDt + 4;
+    const rsrc rw = make_rsrc(a.dt + hrow, bytes), rl = make_rsrc(a.lam + hrow, bytes);
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj) {
+      const uint32_t o = (uint32_t)((threadIdx.x & 63) + jj * 64) * s.rowDt;
+      st.wd[jj] = __uint_as_float(ld32(rw, o));
+      st.wl[jj] = __uint_as_float(ld32(rl, o));
+    }
+  }
+}
+
+// Per-token scalars of the chunk (wave 0): cs (inclusive prefix of dt*A),
+// gamma, gamma + omega, the state weight w_u = exp(cs_e - cs_u)(gamma_u +
+// omega_u) and the chunk's log-decay cs_e.  Tokens past the sequence get
+// zeros (and a flat cs).
+__device__ __forceinline__ void chunk_scalars(const PrefillArgs& a, int t0, int len, float Ah,
+                                              const float (&wd)[3], const float (&wl)[3],
+                                              float* sc) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float cs[2], ga[2], gom[2];
+  float carry = 0.f;
+  const int nj = a.L > kWave ? 2 : 1;
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    if (jj < nj) {
+      const int u = lane + kWave * jj;
+      const float d = u < len ? wd[jj] : 0.f;
+      float dn = __shfl_down(wd[jj], 1, kWave), ln = __shfl_down(wl[jj], 1, kWave);
+      const float dn2 = __shfl(wd[jj + 1], 0, kWave), ln2 = __shfl(wl[jj + 1], 0, kWave);
+      if (lane == kWave - 1) {
+        dn = dn2;
+        ln = ln2;
+      }
+      const float g = u < len ? wl[jj] * d : 0.f;
+      const float om = (u < len && t0 + u + 1 < a.T) ? (1.f - ln) * dn : 0.f;
+      cs[jj] = wave_incl_scan(d * Ah) + carry;
+      carry = __shfl(cs[jj], kWave - 1, kWave);
+      ga[jj] = g;
+      gom[jj] = g + om;
+    }
+  }
+  const float cse = __shfl(a.L > kWave ? cs[1] : cs[0], (a.L - 1) & (kWave - 1), kWave);
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int u = lane + kWave * jj;
+    if (jj < nj && u < a.L) {
+      sc[u] = cs[jj];
+      sc[kLMax + u] = ga[jj];
+      sc[2 * kLMax + u] = gom[jj];
+      sc[3 * kLMax + u] = __expf(cse - cs[jj]) * gom[jj];
+    }
+  }
+  if (lane == 0) sc[4 * kLMax] = cse;
+}
+
+// An angle in radians (a double sum of float angles) reduced to [-pi, pi].
+__device__ __forceinline__ double reduce_angle(double x) {
+  constexpr double kTwoPi = 6.283185307179586476925;
+  return x - kTwoPi * __builtin_rint(x * kInv2PiD);
+}
+
+// KR values of one row of a K-major tile (BwT or XT) at byte offset kb.
+template <typename T, int KR>
+__device__ __forceinline__ void store_krow(const Tile& t, uint32_t row, uint32_t kb,
+                                           const float (&v)[KR]) {
+  if constexpr (sizeof(T) == 2) {
+    static_assert(KR == 4 || KR == 8, "row of 8 or 16 bytes");
+    if constexpr (KR == 4) {
+      const u32x2 w = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      t.ref<u32x2>(row, kb) = w;
+    } else {
+      const u32x4 w = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
+                       pack_bf16(v[6], v[7])};
+      t.ref<u32x4>(row, kb) = w;
+    }
+  } else {
+    static_assert(KR == 4, "row of 16 bytes");
+    t.ref<f32x4>(row, kb) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+
+// Sum of dt*theta over one item's tokens, in double.
+template <int S>
+__device__ __forceinline__ double item_angle_sum(const float (&th)[S], const float (&dt)[S]) {
+  double sum = 0.0;
+#pragma unroll
+  for (int j = 0; j < S; ++j) sum += static_cast<double>(dt[j] * th[j]);
+  return sum;
+}
+
+// Rotation item (pair kp, token block blk): angles from the preceding blocks'
+// sums, rotated B~ (and C~) pairs, the weighted transposed B~ rows, and for
+// the last block the chunk's total rotation (and the segment angle sum).
+template <class C, bool kWithC, bool kAccumSeg>
+__device__ __forceinline__ void rotate_item(const PrefillLayout& lay, int kp, int blk,
+                                            const float (&th)[C::S], const float (&dt)[C::S],
+                                            const uint32_t (&bv)[C::KR * C::PW],
+                                            const uint32_t (&cv)[C::KR * C::PW],
+                                            const float* s_w, const Tile& tB, const Tile& tC,
+                                            const Tile& tW, unsigned char* smem) {
+  using T = typename C::T;
+  constexpr int R = C::R;
+  const double* s_part = reinterpret_cast<const double*>(smem + lay.off_part);
+  double pre = 0.0;
+  for (int q = 0; q < blk; ++q) pre += s_part[q * lay.npair + kp];
+  double rv = pre * kInv2PiD;
+  rv -= __builtin_rint(rv);
+  float r = static_cast<float>(rv);  // revolutions
+  float wb0[C::KR], wb1[C::KR];
+  const uint32_t pb = (uint32_t)(2 * kp * C::es);  // byte column of the pair
+#pragma unroll
+  for (int j = 0; j < C::S; ++j) {
+    const int u = blk * C::S + j;
+    r = __builtin_amdgcn_fractf(__builtin_fmaf(dt[j] * th[j], kInv2Pi, r));
+    const float sn = __builtin_amdgcn_sinf(r), cn = __builtin_amdgcn_cosf(r);
+    const float w = s_w[u];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int i = j * R + q;
+      const uint32_t row = (uint32_t)(u * R + q);
+      float b0, b1;
+      if constexpr (C::PW == 1) {
+        b0 = lo_bf16(bv[i]);
+        b1 = hi_bf16(bv[i]);
+      } else {
+        b0 = __uint_as_float(bv[2 * i]);
+        b1 = __uint_as_float(bv[2 * i + 1]);
+      }
+      const float rb0 = cn * b0 + sn * b1, rb1 = cn * b1 - sn * b0;
+      wb0[i] = w * rb0;
+      wb1[i] = w * rb1;
+      if constexpr (kWithC) {
+        float c0, c1;
+        if constexpr (C::PW == 1) {
+          c0 = lo_bf16(cv[i]);
+          c1 = hi_bf16(cv[i]);
+        } else {
+          c0 = __uint_as_float(cv[2 * i]);
+          c1 = __uint_as_float(cv[2 * i + 1]);
+        }
+        const float rc0 = cn * c0 + sn * c1, rc1 = cn * c1 - sn * c0;
+        if constexpr (C::PW == 1) {
+          tB.ref<uint32_t>(row, pb) = pack_bf16(rb0, rb1);
+          tC.ref<uint32_t>(row, pb) = pack_bf16(rc0, rc1);
+        } else {
+          tB.ref<float2>(row, pb) = make_float2(rb0, rb1);
+          tC.ref<float2>(row, pb) = make_float2(rc0, rc1);
+        }
+      }
+    }
+  }
+  const uint32_t kb = (uint32_t)(blk * C::KR * C::es);
+  store_krow<T, C::KR>(tW, (uint32_t)(2 * kp), kb, wb0);
+  store_krow<T, C::KR>(tW, (uint32_t)(2 * kp + 1), kb, wb1);
+  if (blk == lay.nblk - 1) {
+    // the chunk's total angle; the chain multiplies its rotation over the
+    // whole sequence, so it takes the accurate sine/cosine
+    const double tot = pre + item_angle_sum<C::S>(th, dt);
+    float sn, cn;
+    sincosf(static_cast<float>(reduce_angle(tot)), &sn, &cn);
+    reinterpret_cast<float2*>(smem + lay.off_crot)[kp] = make_float2(cn, sn);
+    if constexpr (kAccumSeg) {
+      double* s_sang = reinterpret_cast<double*>(smem + lay.off_sang);
+      s_sang[kp] = reduce_angle(s_sang[kp] + tot);
+    }
+  }
+}
+
+// x item (pair of columns jp, token block xb) -> two rows of X^T.
+template <class C>
+__device__ __forceinline__ void write_x_item(int jp, int xb, const uint32_t (&xv)[C::KR * C::PW],
+                                             const Tile& tX) {
+  const uint32_t kb = (uint32_t)(xb * C::KR * C::es);
+  if constexpr (C::PW == 1) {
+    if constexpr (C::KR == 4) {
+      const u32x2 r0 = {__builtin_amdgcn_perm(xv[1], xv[0], 0x05040100u),
+                        __builtin_amdgcn_perm(xv[3], xv[2], 0x05040100u)};
+      const u32x2 r1 = {__builtin_amdgcn_perm(xv[1], xv[0], 0x07060302u),
+                        __builtin_amdgcn_perm(xv[3], xv[2], 0x07060302u)};
+      tX.ref<u32x2>((uint32_t)(2 * jp), kb) = r0;
+      tX.ref<u32x2>((uint32_t)(2 * jp + 1), kb) = r1;
+    } else {
+      static_assert(C::KR == 8, "x item of 4 or 8 rows");
+      u32x4 r0, r1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r0[i] = __builtin_amdgcn_perm(xv[2 * i + 1], xv[2 * i], 0x05040100u);
+        r1[i] = __builtin_amdgcn_perm(xv[2 * i + 1], xv[2 * i], 0x07060302u);
+      }
+      tX.ref<u32x4>((uint32_t)(2 * jp), kb) = r0;
+      tX.ref<u32x4>((uint32_t)(2 * jp + 1), kb) = r1;
+    }
+  } else {
+    static_assert(C::KR == 4, "fp32 x item of 4 rows");
+    tX.ref<u32x4>((uint32_t)(2 * jp), kb) = u32x4{xv[0], xv[2], xv[4], xv[6]};
+    tX.ref<u32x4>((uint32_t)(2 * jp + 1), kb) = u32x4{xv[1], xv[3], xv[5], xv[7]};
+  }
+}
+
+// MFMA fragment of a swizzled tile: row `row`, contraction slots from k0.
+__device__ __forceinline__ bf16x8 load_frag(const Tile& t, uint32_t row, int k0, const bf16*) {
+  const int g = (threadIdx.x & 63) >> 4;
+  return t.ref<bf16x8>(row, (uint32_t)(k0 + 8 * g) * 2u);
+}
+__device__ __forceinline__ float load_frag(const Tile& t, uint32_t row, int k0, const float*) {
+  const int g = (threadIdx.x & 63) >> 4;
+  return t.ref<float>(row, (uint32_t)(k0 + g) * 4u);
+}
+
+// State tiles -> LDS copy G^T [P][N] (the B operand of the inter-chunk MFMA).
+template <class C>
+__device__ __forceinline__ void state_to_lds(const PrefillArgs& a, const f32x4 (&stt)[kMaxStTiles],
+                                             const Tile& tG) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int ntn = a.N / 16, ntiles = ntn * C::NPT;
+#pragma unroll
+  for (int m = 0; m < kMaxStTiles; ++m) {
+    const int i = wave + m * kW;
+    if (i < ntiles) {
+      const int nt = i % ntn, pt = i / ntn;
+      const uint32_t row = (uint32_t)(pt * 16 + li), nb = (uint32_t)((nt * 16 + 4 * g) * C::es);
+      if constexpr (C::es == 2) {
+        const u32x2 w = {pack_bf16(stt[m][0], stt[m][1]), pack_bf16(stt[m][2], stt[m][3])};
+        tG.ref<u32x2>(row, nb) = w;
+      } else {
+        tG.ref<f32x4>(row, nb) = stt[m];
+      }
+    }
+  }
+}
+
+// Chunk state S_c = sum_u w_u B~_u x_u^T (MFMA, both operands read straight
+// from the K-major tiles) folded into the state tiles: st <- R(Phi_c)(d st +
+// S_c).  Tile m of this wave is i = wave + m*kW: n-tile i % (N/16), p-tile
+// i / (N/16); lane holds rows n = 4g..4g+3.
+template <class C>
+__device__ __forceinline__ void state_update(const PrefillArgs& a, const PrefillLayout& lay,
+                                             float d, f32x4 (&stt)[kMaxStTiles],
+                                             const Tile& tW, const Tile& tX,
+                                             const unsigned char* smem) {
+  using T = typename C::T;
+  using M = typename C::M;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int ntn = a.N / 16, ntiles = ntn * C::NPT;
+  const bool share = (kW % ntn) == 0;  // both tiles of this wave share their n-tile
+  const float2* s_crot = reinterpret_cast<const float2*>(smem + lay.off_crot);
+  f32x4 acc[kMaxStTiles];
+#pragma unroll
+  for (int m = 0; m < kMaxStTiles; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int i0 = wave, i1 = wave + kW;
+  if (i0 < ntiles) {
+    const uint32_t nrow0 = (uint32_t)((i0 % ntn) * 16 + li), prow0 = (uint32_t)((i0 / ntn) * 16 + li);
+    const uint32_t nrow1 = (uint32_t)((i1 % ntn) * 16 + li), prow1 = (uint32_t)((i1 / ntn) * 16 + li);
+    const bool two = i1 < ntiles;
+    for (int k0 = 0; k0 < lay.LRp; k0 += M::K) {
+      const typename M::frag fa = load_frag(tW, nrow0, k0, (const T*)nullptr);
+      const typename M::frag fb = load_frag(tX, prow0, k0, (const T*)nullptr);
+      acc[0] = M::mma(fa, fb, acc[0]);
+      if (two) {
+        const typename M::frag fa1 = share ? fa : load_frag(tW, nrow1, k0, (const T*)nullptr);
+        const typename M::frag fb1 = load_frag(tX, prow1, k0, (const T*)nullptr);
+        acc[1] = M::mma(fa1, fb1, acc[1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kMaxStTiles; ++m) {
+    const int i = wave + m * kW;
+    if (i < ntiles) {
+      const int kq = (i % ntn) * 8 + 2 * g;
+      const float2 r0 = s_crot[kq], r1 = s_crot[kq + 1];
+      const float v0 = d * stt[m][0] + acc[m][0], v1 = d * stt[m][1] + acc[m][1];
+      const float v2 = d * stt[m][2] + acc[m][2], v3 = d * stt[m][3] + acc[m][3];
+      stt[m][0] = r0.x * v0 - r0.y * v1;
+      stt[m][1] = r0.y * v0 + r0.x * v1;
+      stt[m][2] = r1.x * v2 - r1.y * v3;
+      stt[m][3] = r1.y * v2 + r1.x * v3;
+    }
+  }
+}
+
+// cs, gamma and gamma + omega of the tokens of chunk rows row0 .. row0+3
+// (row0 a multiple of 4), as whole-vector LDS reads.
+template <int R>
+__device__ __forceinline__ void key_scalars4(const float* sc, int row0, float (&cs)[4],
+                                             float (&ga)[4], float (&gom)[4]) {
+  const float* s_cs = sc;
+  const float* s_ga = sc + kLMax;
+  const float* s_gom = sc + 2 * kLMax;
+  if constexpr (R == 1) {
+    const float4 c = *reinterpret_cast<const float4*>(s_cs + row0);
+    const float4 g = *reinterpret_cast<const float4*>(s_ga + row0);
+    const float4 o = *reinterpret_cast<const float4*>(s_gom + row0);
+    cs[0] = c.x; cs[1] = c.y; cs[2] = c.z; cs[3] = c.w;
+    ga[0] = g.x; ga[1] = g.y; ga[2] = g.z; ga[3] = g.w;
+    gom[0] = o.x; gom[1] = o.y; gom[2] = o.z; gom[3] = o.w;
+  } else if constexpr (R == 2) {
+    const float2 c = *reinterpret_cast<const float2*>(s_cs + row0 / 2);
+    const float2 g = *reinterpret_cast<const float2*>(s_ga + row0 / 2);
+    const float2 o = *reinterpret_cast<const float2*>(s_gom + row0 / 2);
+    cs[0] = cs[1] = c.x; cs[2] = cs[3] = c.y;
+    ga[0] = ga[1] = g.x; ga[2] = ga[3] = g.y;
+    gom[0] = gom[1] = o.x; gom[2] = gom[3] = o.y;
+  } else {
+    const float c = s_cs[row0 / 4], g = s_ga[row0 / 4], o = s_gom[row0 / 4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cs[j] = c;
+      ga[j] = g;
+      gom[j] = o;
+    }
+  }
+}
+
+// y of one chunk: units (query block qb, p-group pg) over the waves.
+template <class C>
+__device__ __forceinline__ void chunk_output(const PrefillArgs& a, const PrefillLayout& lay,
+                                             const Ctx& s, const ChunkRes& cr, const float* sc,
+                                             const Tile& tC, const Tile& tB, const Tile& tX,
+                                             const Tile& tG) {
+  using T = typename C::T;
+  using M = typename C::M;
+  constexpr int R = C::R, P = C::P, NPT = C::NPT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int N = a.N;
+  const float* s_cs = sc;
+  const size_t hrow = ((size_t)s.b * a.T + cr.t0) * a.H + s.h;
+  const uint32_t yb = (uint32_t)(R * P * C::es);
+  const rsrc ry = make_rsrc(static_cast<unsigned char*>(a.y) + hrow * yb,
+                            (uint32_t)(cr.len - 1) * s.rowX + yb);
+  // units (query block, pair of p-tiles); wave w takes units w, 2kW-1-w,
+  // 2kW+w, ... so the causal (growing) cost per query block balances
+  constexpr int PPG = NPT < 2 ? NPT : 2;
+  constexpr int NPG = NPT / PPG;
+  const int nqb = lay.LR / 16;
+  const int nunits = nqb * NPG;
+
+  for (int k = 0;; ++k) {
+    const int unit = (k & 1) ? (k + 1) * kW - 1 - wave : k * kW + wave;
+    if (unit >= nunits) break;
+    const int qb = unit / NPG, p_lo = (unit % NPG) * PPG;
+    f32x4 acc[PPG];
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t qrow = (uint32_t)(qb * 16 + li);
+
+    // inter-chunk term: C~ G_c, rows scaled by exp(cs_t)
+    for (int n0 = 0; n0 < N; n0 += M::K) {
+      const typename M::frag fa = load_frag(tC, qrow, n0, (const T*)nullptr);
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) {
+        const typename M::frag fb =
+            load_frag(tG, (uint32_t)((p_lo + pp) * 16 + li), n0, (const T*)nullptr);
+        acc[pp] = M::mma(fa, fb, acc[pp]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float scl = __expf(s_cs[(qb * 16 + 4 * g + j) / R]);
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) acc[pp][j] *= scl;
+    }
+
+    // intra-chunk term over key blocks up to the diagonal
+    const int tq = (qb * 16 + li) / R;
+    const float csq = s_cs[tq];
+    constexpr int KB = (sizeof(T) == 2) ? 2 : 1;  // 16-row key blocks per step
+    for (int kb = 0; kb * 16 <= qb * 16 + 15; kb += KB) {
+      f32x4 sct[KB];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) sct[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int n0 = 0; n0 < N; n0 += M::K) {
+        const typename M::frag fq = load_frag(tC, qrow, n0, (const T*)nullptr);
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+          const typename M::frag fk =
+              load_frag(tB, (uint32_t)((kb + i) * 16 + li), n0, (const T*)nullptr);
+          sct[i] = M::mma(fk, fq, sct[i]);  // rows = keys, cols = queries
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        float kcs[4], kga[4], kgom[4];
+        key_scalars4<R>(sc, (kb + i) * 16 + 4 * g, kcs, kga, kgom);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int tk = ((kb + i) * 16 + 4 * g + j) / R;
+          float w = 0.f;
+          if (tk < tq)
+            w = __expf(csq - kcs[j]) * kgom[j];
+          else if (tk == tq)
+            w = kga[j];
+          sct[i][j] *= w;
+        }
+      }
+      if constexpr (sizeof(T) == 2) {
+        bf16x8 fa;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          fa[j] = from_f32<bf16>(sct[0][j]);
+          fa[4 + j] = from_f32<bf16>(sct[1][j]);
+        }
+#pragma unroll
+        for (int pp = 0; pp < PPG; ++pp) {
+          const uint32_t xr = (uint32_t)((p_lo + pp) * 16 + li);
+          const bf16x4 lo = tX.ref<bf16x4>(xr, (uint32_t)(kb * 16 + 4 * g) * 2u);
+          const bf16x4 hi = tX.ref<bf16x4>(xr, (uint32_t)((kb + 1) * 16 + 4 * g) * 2u);
+          bf16x8 fb;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            fb[j] = lo[j];
+            fb[4 + j] = hi[j];
+          }
+          acc[pp] = Mfma<bf16>::mma(fa, fb, acc[pp]);
+        }
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < PPG; ++pp) {
+          const f32x4 xv =
+              tX.ref<f32x4>((uint32_t)((p_lo + pp) * 16 + li), (uint32_t)(kb * 16 + 4 * g) * 4u);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[pp] = Mfma<float>::mma(sct[0][j], xv[j], acc[pp]);
+        }
+      }
+    }
+
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = qb * 16 + 4 * g + j;
+      const uint32_t u = (uint32_t)(row / R), q = (uint32_t)(row % R);
+      const uint32_t off = u * s.rowX + (q * P + (uint32_t)li) * C::es;
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) {
+        const uint32_t o = off + (uint32_t)((p_lo + pp) * 16 * C::es);
+        if constexpr (C::es == 2)
+          __builtin_amdgcn_raw_buffer_store_b16(
+              __builtin_bit_cast(unsigned short, from_f32<bf16>(acc[pp][j])), ry, (int)o, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[pp][j]), ry, (int)o, 0, 0);
+      }
+    }
+  }
+}
+
+// Tiles of the workgroup's LDS.
+struct Tiles {
+  Tile C, B, W, X, G;
+};
+
+template <class C>
+__device__ __forceinline__ Tiles make_tiles(const PrefillArgs& a, const PrefillLayout& lay,
+                                            unsigned char* smem) {
+  const uint32_t nb = (uint32_t)(a.N * C::es), kb = (uint32_t)(lay.LRp * C::es);
+  return Tiles{make_tile(smem + lay.off_Cr, nb), make_tile(smem + lay.off_Br, nb),
+               make_tile(smem + lay.off_BwT, kb), make_tile(smem + lay.off_XT, kb),
+               make_tile(smem + lay.off_GT, nb)};
+}
+
+// [P]: this thread's items' angle sums and (wave 0) the per-token scalars.
+template <class C>
+__device__ __forceinline__ void step_partials(const PrefillArgs& a, const PrefillLayout& lay,
+                                              const Ctx& s, const Map& m, int c,
+                                              const Stage<C>& st, float* sc,
+                                              unsigned char* smem) {
+  double* s_part = reinterpret_cast<double*>(smem + lay.off_part);
+  if (m.act) s_part[m.blk * lay.npair + m.kp] = item_angle_sum<C::S>(st.th, st.dt);
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) {
+    const int t0 = c * a.L;
+    chunk_scalars(a, t0, min(a.L, a.T - t0), s.Ah, st.wd, st.wl, sc);
+  }
+}
+
+// [R]: rotation items and x items into LDS (consumes the staged registers).
+template <class C, bool kWithC, bool kAccumSeg>
+__device__ __forceinline__ void step_rotate(const PrefillArgs& a, const PrefillLayout& lay,
+                                            const Ctx& s, const Map& m, int c, Stage<C>& st,
+                                            const float* sc, const Tiles& t,
+                                            unsigned char* smem) {
+  const float* s_w = sc + 3 * kLMax;
+  if (m.xact) write_x_item<C>(m.jp, m.xblk, st.x, t.X);
+  if (m.act)
+    rotate_item<C, kWithC, kAccumSeg>(lay, m.kp, m.blk, st.th, st.dt, st.b, st.c, s_w, t.B, t.C,
+                                      t.W, smem);
+}
+
+template <class C>
+__global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int P = C::P;
+  const PrefillLayout lay = prefill_layout(a.L, C::R, a.N, P, C::es);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+
+  int* s_ticket = reinterpret_cast<int*>(smem + lay.off_misc);
+  if (tid == 0) *s_ticket = atomicAdd(a.ticket, 1);
+  __syncthreads();
+  const int ticket = *s_ticket;
+  const int BH = a.nb * a.H;
+  Ctx s;
+  s.seg = ticket / BH;
+  s.bh = ticket % BH;
+  s.b = s.bh / a.H;
+  s.h = s.bh % a.H;
+  s.c0 = s.seg * a.K;
+  s.c1 = min(a.nC, s.c0 + a.K);
+  s.rowB = (uint32_t)(a.H * C::R * a.N * C::es);
+  s.rowTh = (uint32_t)(a.H * (a.N / 2) * 4);
+  s.rowDt = (uint32_t)(a.H * 4);
+  s.rowX = (uint32_t)(a.H * C::R * P * C::es);
+  s.Ah = a.A[s.h];
+
+  Map m;
+  m.act = tid < lay.items;
+  m.kp = tid % lay.npair;
+  m.blk = tid / lay.npair;
+  m.xact = tid < lay.xitems;
+  m.jp = tid % (P / 2);
+  m.xblk = tid / (P / 2);
+
+  const Tiles t = make_tiles<C>(a, lay, smem);
+  float* s_scal = reinterpret_cast<float*>(smem + lay.off_scal);
+  double* s_sang = reinterpret_cast<double*>(smem + lay.off_sang);
+  float2* s_srot = reinterpret_cast<float2*>(smem + lay.off_srot);
+  const int npair = lay.npair;
+  const int ntn = a.N / 16, ntiles = ntn * (P / 16);
+
+  // zero the contraction padding of the K-major tiles (never written again)
+  if (lay.LRp > lay.LR) {
+    const int padb = (lay.LRp - lay.LR) * C::es;  // bytes per row, a multiple of 16
+    const int per = padb / 16;
+    for (int i = tid; i < (a.N + P) * per; i += kT) {
+      const int row = i / per, col = i % per;
+      const Tile& tt = row < a.N ? t.W : t.X;
+      const int rr = row < a.N ? row : row - a.N;
+      tt.ref<u32x4>((uint32_t)rr, (uint32_t)(lay.LR * C::es + col * 16)) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  for (int i = tid; i < npair; i += kT) s_sang[i] = 0.0;
+
+  f32x4 stt[kMaxStTiles];
+#pragma unroll
+  for (int q = 0; q < kMaxStTiles; ++q) stt[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- phase 1: local exit state of the segment --------------------------
+  Stage<C> stg;
+  issue_loads<C, false>(a, s, m, s.c0, stg);
+  float seg_logdecay = 0.f;
+  int buf = 0;
+  for (int c = s.c0; c < s.c1; ++c) {
+    float* sc = s_scal + buf * (kScalBytes / 4);
+    step_partials<C>(a, lay, s, m, c, stg, sc, smem);
+    __syncthreads();
+    step_rotate<C, false, true>(a, lay, s, m, c, stg, sc, t, smem);
+    // prefetch the next chunk; the last step prefetches the first chunk
+    // again, with C, for phase 3
+    if (c + 1 < s.c1)
+      issue_loads<C, false>(a, s, m, c + 1, stg);
+    else
+      issue_loads<C, true>(a, s, m, s.c0, stg);
+    __syncthreads();
+    const float lc = sc[4 * kLMax];
+    seg_logdecay += lc;
+    state_update<C>(a, lay, __expf(lc), stt, t.W, t.X, smem);
+    buf ^= 1;
+  }
+
+  // ---- phase 2: chain ------------------------------------------------------
+  __syncthreads();
+  for (int kp = tid; kp < npair; kp += kT) {
+    float sn, cn;
+    sincosf(static_cast<float>(s_sang[kp]), &sn, &cn);
+    s_srot[kp] = make_float2(cn, sn);
+  }
+  const float segD = __expf(seg_logdecay);
+  f32x4 ent[kMaxStTiles];
+#pragma unroll
+  for (int q = 0; q < kMaxStTiles; ++q) ent[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (s.seg > 0) {
+    if (tid == 0) {
+      int spins = 0;
+      while (__hip_atomic_load(a.flags + s.bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+             s.seg) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > kSpinLimit) {
+          __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    const float* src = a.ring + ((size_t)s.bh * 2 + ((s.seg - 1) & 1)) * a.N * P;
+#pragma unroll
+    for (int q = 0; q < kMaxStTiles; ++q) {
+      const int i = wave + q * kW;
+      if (i < ntiles) {
+        const int nt = i % ntn, pt = i / ntn;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ent[q][j] = __hip_atomic_load(src + (size_t)(nt * 16 + 4 * g + j) * P + pt * 16 + li,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  } else {
+    __syncthreads();
+  }
+  // exit state = R(Phi_seg) (D_seg * entry) + local
+  const bool last = s.seg == a.nSeg - 1;
+  float* dst = a.ring + ((size_t)s.bh * 2 + (s.seg & 1)) * a.N * P;
+#pragma unroll
+  for (int q = 0; q < kMaxStTiles; ++q) {
+    const int i = wave + q * kW;
+    if (i < ntiles) {
+      const int nt = i % ntn, pt = i / ntn;
+      const int kq = nt * 8 + 2 * g;
+      const float2 r0 = s_srot[kq], r1 = s_srot[kq + 1];
+      f32x4 e;
+      const float v0 = segD * ent[q][0], v1 = segD * ent[q][1];
+      const float v2 = segD * ent[q][2], v3 = segD * ent[q][3];
+      e[0] = r0.x * v0 - r0.y * v1 + stt[q][0];
+      e[1] = r0.y * v0 + r0.x * v1 + stt[q][1];
+      e[2] = r1.x * v2 - r1.y * v3 + stt[q][2];
+      e[3] = r1.y * v2 + r1.x * v3 + stt[q][3];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const size_t off = (size_t)(nt * 16 + 4 * g + j) * P + pt * 16 + li;
+        if (!last)
+          __hip_atomic_store(dst + off, e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else if (a.h_final)
+          a.h_final[(size_t)s.bh * a.N * P + off] = e[j];
+      }
+    }
+  }
+  if (!last) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's ring stores have completed
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(a.flags + s.bh, s.seg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int q = 0; q < kMaxStTiles; ++q) stt[q] = ent[q];
+
+  // ---- phase 3: outputs from the true entry state -------------------------
+  for (int c = s.c0; c < s.c1; ++c) {
+    float* sc = s_scal + buf * (kScalBytes / 4);
+    const bool more = c + 1 < s.c1;
+    step_partials<C>(a, lay, s, m, c, stg, sc, smem);
+    __syncthreads();
+    step_rotate<C, true, false>(a, lay, s, m, c, stg, sc, t, smem);
+    state_to_lds<C>(a, stt, t.G);
+    if (more) issue_loads<C, true>(a, s, m, c + 1, stg);
+    __syncthreads();
+    chunk_output<C>(a, lay, s, chunk_res<C>(a, s, c), sc, t.C, t.B, t.X, t.G);
+    if (more) state_update<C>(a, lay, __expf(sc[4 * kLMax]), stt, t.W, t.X, smem);
+    buf ^= 1;
+  }
+}
+
+template <class C>
+hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
+  const PrefillLayout lay = prefill_layout(a.L, C::R, a.N, C::P, C::es);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<C>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.total);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((prefill_kernel<C>), dim3(a.nb * a.H * a.nSeg), dim3(kT), lay.total, stream,
+                     a);
+  return hipGetLastError();
+}
+
+template <typename T, int R>
+hipError_t launch_tr(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.P) {
+    case 16: return launch_cfg<Cfg<T, R, 16>>(a, stream);
+    case 32: return launch_cfg<Cfg<T, R, 32>>(a, stream);
+    case 64: return launch_cfg<Cfg<T, R, 64>>(a, stream);
+    case 128: return launch_cfg<Cfg<T, R, 128>>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.R) {
+    case 1: return launch_tr<T, 1>(a, stream);
+    case 2: return launch_tr<T, 2>(a, stream);
+    case 4: return launch_tr<T, 4>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pf
+}  // namespace m3
