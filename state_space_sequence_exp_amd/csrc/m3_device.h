@@ -62,15 +62,40 @@ __device__ __forceinline__ void fast_sincos(float a, float* s, float* c) {
   *c = __builtin_amdgcn_cosf(r);
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
+// A DPP lane move of a float (lanes whose source is outside the row, or
+// whose row is masked off, read 0).
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xf, false));
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave, in DPP steps: shifts by
+// 1, 2, 4 and 8 within each row of 16 lanes, then the last lane of row 0 (and
+// of row 2) added to row 1 (row 3), then the last lane of row 1 added to rows
+// 2 and 3.
 __device__ __forceinline__ float wave_incl_scan(float v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    float o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
+  v += dpp_move<0x111>(v);        // row_shr:1
+  v += dpp_move<0x112>(v);        // row_shr:2
+  v += dpp_move<0x114>(v);        // row_shr:4
+  v += dpp_move<0x118>(v);        // row_shr:8
+  v += dpp_move<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_move<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
   return v;
+}
+
+// The value of lane l + 1, and `last` in lane 63 (DPP wave_shl:1; the lane
+// without a source keeps the old value).  No lane condition is involved, so
+// the move always runs on the whole wave (a DPP move reading a disabled lane
+// would return the old value instead).
+__device__ __forceinline__ float wave_next_lane(float v, float last) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(last), __float_as_int(v), 0x130, 0xf, 0xf, false));
+}
+
+// Value of lane `lane` (uniform) broadcast to the wave.
+__device__ __forceinline__ float wave_read_lane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
 // ---------------------------------------------------------------------------

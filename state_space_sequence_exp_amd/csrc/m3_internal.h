@@ -10,11 +10,14 @@
 
 namespace m3 {
 
-constexpr int kPrefillThreads = 1024;     // threads per prefill workgroup (16 waves, one per CU)
+#ifndef M3_PREFILL_THREADS
+#define M3_PREFILL_THREADS 512
+#endif
+constexpr int kPrefillThreads = M3_PREFILL_THREADS;  // threads per prefill workgroup (one per CU)
 constexpr int kLMax = 128;                // largest chunk (tokens)
 constexpr int kLRMax = 256;               // largest chunk * R (rows of a chunk tile)
 constexpr size_t kLdsLimit = 160 * 1024;  // LDS per workgroup on gfx950
-constexpr int kMaxStTiles = 2;            // 16x16 state tiles per wave (N * P <= 8192)
+constexpr int kMaxStTiles = 8192 / 256 / (kPrefillThreads / 64);  // 16x16 state tiles per wave (N * P <= 8192)
 
 // Shape of one prefill problem plus device pointers (all validated).
 struct PrefillArgs {
@@ -53,7 +56,7 @@ __host__ __device__ inline uint32_t align_up_u32(uint32_t v, uint32_t a) {
 // Tokens per rotation item: one thread rotates one pair of B (and C) rows
 // over this many consecutive tokens (and all R ranks of each token).
 __host__ __device__ constexpr int prefill_item_tokens(int esize, int R) {
-  return esize == 2 ? (R == 1 ? 4 : 2) : (R == 4 ? 1 : 4 / R);
+  return (kPrefillThreads == 512 ? 2 : 1) * (esize == 2 ? (R == 1 ? 4 : 2) : (R == 4 ? 1 : 4 / R));
 }
 
 // Per-token scalars of one chunk, one of two alternating buffers:
@@ -113,13 +116,40 @@ __host__ __device__ inline PrefillLayout prefill_layout(int L, int R, int N, int
   return c;
 }
 
-// Shapes the prefill kernel handles beyond the LDS limit: at most two state
-// tiles per wave, at most one rotation item and one x item per thread, and
-// byte offsets within one chunk that fit 30 bits.
+// Roles of the waves in a chunk's MFMA phase.  The outputs are split into
+// units of one 16-row query block and a group of at most four p-tiles; with
+// few query blocks a unit covers as many p-tiles as it can (each query
+// block's scores are then computed once), otherwise two, and units are dealt
+// to the waves from wave 0.  The state tiles are spread over all waves
+// (tile i on wave i % waves).
+struct WaveRoles {
+  int ppg;   // p-tiles per unit
+  int npg;   // units per query block
+  int nout;  // output units
+  int sw0;   // first wave holding state tiles
+  int nsw;   // waves holding state tiles
+};
+__host__ __device__ inline WaveRoles prefill_wave_roles(int LR, int P) {
+  constexpr int kW = kPrefillThreads / 64;
+  const int nqb = LR / 16, npt = P / 16;
+  WaveRoles w;
+  const int cap = nqb * 2 <= kW ? 4 : 2;
+  w.ppg = npt < cap ? npt : cap;
+  w.npg = npt / w.ppg;
+  w.nout = nqb * w.npg;
+  w.sw0 = 0;
+  w.nsw = kW - w.sw0;
+  return w;
+}
+
+// Shapes the prefill kernel handles beyond the LDS limit: at most
+// kMaxStTiles state tiles per state wave, at most one rotation item and one x
+// item per thread, and byte offsets within one chunk that fit 30 bits.
 __host__ __device__ inline bool prefill_shape_fits(int L, int R, int N, int P, int H, int esize) {
   const PrefillLayout lay = prefill_layout(L, R, N, P, esize);
+  const WaveRoles w = prefill_wave_roles(lay.LR, P);
   const long long row = (long long)H * R * (N > P ? N : P) * esize;
-  return (N / 16) * (P / 16) <= kMaxStTiles * (kPrefillThreads / 64) &&
+  return (N / 16) * (P / 16) <= 32 && (N / 16) * (P / 16) <= kMaxStTiles * w.nsw &&
          lay.items <= kPrefillThreads && lay.xitems <= kPrefillThreads &&
          (long long)L * row < (1ll << 30);
 }
@@ -127,8 +157,11 @@ __host__ __device__ inline bool prefill_shape_fits(int L, int R, int N, int P, i
 hipError_t launch_prefill(const PrefillArgs& a, m3_dtype dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, m3_dtype dtype, hipStream_t stream);
 
-// Per-dtype prefill launchers (one translation unit each).
-hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+// Per-type (and, for bfloat16, per-rank) prefill launchers, one translation
+// unit each.
+hipError_t launch_prefill_bf16_r1(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bf16_r2(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bf16_r4(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
 // Largest N the decode kernel handles for a given P.

@@ -1,7 +1,6 @@
 // prefill.hip -- host side of the chunked prefill: chain-counter reset,
-// segment sizing and dispatch to the per-storage-type kernels
-// (prefill_bf16.hip, prefill_f32.hip; the kernel itself is in
-// prefill_impl.h).
+// segment sizing and dispatch to the per-type kernels (prefill_bf16_r*.hip,
+// prefill_f32.hip; the kernel itself is in prefill_impl.h).
 #include "m3_internal.h"
 
 namespace m3 {
@@ -21,11 +20,12 @@ __global__ void fill_zero_kernel(float* p, size_t n) {
 
 }  // namespace
 
-// Chunks per segment: enough segments to give about four workgroups per CU
-// across all sequences.
+// Chunks per segment: enough segments for about one workgroup per CU (256 on
+// MI355X) across all sequences; longer segments amortise each segment's
+// extra local pass and chain step.
 int prefill_segment_chunks(int nb, int H, int nC) {
   const long units = (long)nb * H;
-  const long target = 1024;
+  const long target = 256;
   long k = (nC * units + target - 1) / target;
   if (k < 1) k = 1;
   if (k > nC) k = nC;
@@ -44,7 +44,13 @@ hipError_t launch_prefill(const PrefillArgs& a, m3_dtype dtype, hipStream_t stre
   hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(256), 0, stream, a.flags, a.nb * a.H);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return dtype == M3_BF16 ? launch_prefill_bf16(a, stream) : launch_prefill_f32(a, stream);
+  if (dtype != M3_BF16) return launch_prefill_f32(a, stream);
+  switch (a.R) {
+    case 1: return launch_prefill_bf16_r1(a, stream);
+    case 2: return launch_prefill_bf16_r2(a, stream);
+    case 4: return launch_prefill_bf16_r4(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace m3

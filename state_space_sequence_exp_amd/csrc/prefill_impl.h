@@ -78,6 +78,16 @@ constexpr uint32_t kOOB = 0x7ff00000u;     // a buffer offset past every range
 constexpr double kInv2PiD = 0.15915494309189533577;
 
 typedef __amdgpu_buffer_rsrc_t rsrc;
+
+// A uniform value the compiler treats as unknown from here on.  Applied at the
+// top of every chunk step to the strides and LDS offsets that per-thread
+// addresses derive from, so those addresses are recomputed in each step (a
+// few VALU) instead of being hoisted out of the chunk loops and kept in
+// registers for the whole kernel, which would spill.
+__device__ __forceinline__ uint32_t opaque_u(uint32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ rsrc make_rsrc(const void* base, uint32_t bytes) {
@@ -97,8 +107,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// A [rows][row_bytes] tile in LDS whose 16-byte columns are XOR-swizzled by
-// row within aligned groups of up to 8 columns.
+// A [rows][row_bytes] tile in LDS.  For 2-byte types its 16-byte columns are
+// XOR-swizzled by row within aligned groups of four columns (64 bytes), so
+// the 16 rows an MFMA fragment read touches spread over the banks, while a
+// byte offset that is a multiple of 64 still adds straight to the address of
+// the first group (fragment addresses are one per-lane base plus an
+// immediate).  4-byte tiles are not swizzled.
 struct Tile {
   unsigned char* base;
   uint32_t rowb, mask;
@@ -109,18 +123,26 @@ struct Tile {
   __device__ __forceinline__ V& ref(uint32_t row, uint32_t byte) const {
     return *reinterpret_cast<V*>(base + at(row, byte));
   }
+  // element at byte `lane_byte` (< 64) of the first group plus `group_byte`
+  // (a multiple of 64)
+  template <typename V>
+  __device__ __forceinline__ const V& ref2(uint32_t row, uint32_t lane_byte,
+                                           uint32_t group_byte) const {
+    return *reinterpret_cast<const V*>(base + at(row, lane_byte) + group_byte);
+  }
 };
-__device__ __forceinline__ Tile make_tile(unsigned char* base, uint32_t rowb) {
+__device__ __forceinline__ Tile make_tile(unsigned char* base, uint32_t rowb, int esize) {
   const uint32_t ncol = rowb >> 4;
   const uint32_t low = ncol & (0u - ncol);
-  return Tile{base, rowb, (low < 8u ? low : 8u) - 1u};
+  return Tile{base, rowb, esize == 2 ? (low < 4u ? low : 4u) - 1u : 0u};
 }
 
-template <typename T_, int R_, int P_>
+template <typename T_, int R_, int P_, int N_>
 struct Cfg {
   using T = T_;
   using M = Mfma<T_>;
   static constexpr int R = R_, P = P_;
+  static constexpr int NC = N_;  // state size if fixed at compile time, else 0
   static constexpr int es = (int)sizeof(T_);
   static constexpr int S = prefill_item_tokens(es, R_);  // tokens per rotation item
   static constexpr int KR = S * R_;                      // chunk rows per item
@@ -133,8 +155,11 @@ template <class C>
 struct Stage {
   float th[C::S], dt[C::S];                                  // rotation item
   uint32_t b[C::KR * C::PW], c[C::KR * C::PW], x[C::KR * C::PW];
-  float wd[3], wl[3];                                        // wave 0: dt, lam
 };
+
+// The wave that computes the per-token scalars of the next chunk during the
+// MFMA phase (it holds no output unit when the outputs fit in few waves).
+constexpr int kScalarWave = kW - 1;
 
 // Uniform per-workgroup values.
 struct Ctx {
@@ -240,22 +265,25 @@ __device__ __forceinline__ void issue_loads(const PrefillArgs& a, const Ctx& s, 
                              : kOOB;
   load_item<C, kWithC>(a, s, r, vB, vTh, vDt, st.th, st.dt, st.b, st.c);
   load_x_item<C>(s, r, vX, st.x);
-  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) {
-    // dt and lam of tokens lane, lane + 64, lane + 128, up to the end of the
-    // sequence (the token after the chunk feeds omega of its last token)
-    const size_t hrow = ((size_t)s.b * a.T + r.t0) * a.H + s.h;
-    const uint32_t bytes = (uint32_t)(a.T - r.t0 - 1) * s.rowDt + 4;
-    const rsrc rw = make_rsrc(a.dt + hrow, bytes), rl = make_rsrc(a.lam + hrow, bytes);
+}
+
+// dt and lam of tokens lane, lane + 64, lane + 128 of chunk c, up to the end
+// of the sequence (the token after the chunk feeds omega of its last token).
+__device__ __forceinline__ void scalar_loads(const PrefillArgs& a, const Ctx& s, int c,
+                                             float (&wd)[3], float (&wl)[3]) {
+  const int t0 = c * a.L;
+  const size_t hrow = ((size_t)s.b * a.T + t0) * a.H + s.h;
+  const uint32_t bytes = (uint32_t)(a.T - t0 - 1) * s.rowDt + 4;
+  const rsrc rw = make_rsrc(a.dt + hrow, bytes), rl = make_rsrc(a.lam + hrow, bytes);
 #pragma unroll
-    for (int jj = 0; jj < 3; ++jj) {
-      const uint32_t o = (uint32_t)((threadIdx.x & 63) + jj * 64) * s.rowDt;
-      st.wd[jj] = __uint_as_float(ld32(rw, o));
-      st.wl[jj] = __uint_as_float(ld32(rl, o));
-    }
+  for (int jj = 0; jj < 3; ++jj) {
+    const uint32_t o = (uint32_t)((threadIdx.x & 63) + jj * 64) * s.rowDt;
+    wd[jj] = __uint_as_float(ld32(rw, o));
+    wl[jj] = __uint_as_float(ld32(rl, o));
   }
 }
 
-// Per-token scalars of the chunk (wave 0): cs (inclusive prefix of dt*A),
+// Per-token scalars of the chunk (one wave): cs (inclusive prefix of dt*A),
 // gamma, gamma + omega, the state weight w_u = exp(cs_e - cs_u)(gamma_u +
 // omega_u) and the chunk's log-decay cs_e.  Tokens past the sequence get
 // zeros (and a flat cs).
@@ -263,7 +291,7 @@ __device__ __forceinline__ void chunk_scalars(const PrefillArgs& a, int t0, int 
                                               const float (&wd)[3], const float (&wl)[3],
                                               float* sc) {
   const int lane = threadIdx.x & (kWave - 1);
-  float cs[2], ga[2], gom[2];
+  float cs[2] = {0.f, 0.f}, ga[2] = {0.f, 0.f}, gom[2] = {0.f, 0.f};
   float carry = 0.f;
   const int nj = a.L > kWave ? 2 : 1;
 #pragma unroll
@@ -271,21 +299,19 @@ __device__ __forceinline__ void chunk_scalars(const PrefillArgs& a, int t0, int 
     if (jj < nj) {
       const int u = lane + kWave * jj;
       const float d = u < len ? wd[jj] : 0.f;
-      float dn = __shfl_down(wd[jj], 1, kWave), ln = __shfl_down(wl[jj], 1, kWave);
-      const float dn2 = __shfl(wd[jj + 1], 0, kWave), ln2 = __shfl(wl[jj + 1], 0, kWave);
-      if (lane == kWave - 1) {
-        dn = dn2;
-        ln = ln2;
-      }
+      // dt and lam of token u + 1: the next lane, or lane 0 of the next
+      // group of 64 tokens for the last lane
+      const float dn = wave_next_lane(wd[jj], wave_read_lane(wd[jj + 1], 0));
+      const float ln = wave_next_lane(wl[jj], wave_read_lane(wl[jj + 1], 0));
       const float g = u < len ? wl[jj] * d : 0.f;
       const float om = (u < len && t0 + u + 1 < a.T) ? (1.f - ln) * dn : 0.f;
       cs[jj] = wave_incl_scan(d * Ah) + carry;
-      carry = __shfl(cs[jj], kWave - 1, kWave);
+      carry = wave_read_lane(cs[jj], kWave - 1);
       ga[jj] = g;
       gom[jj] = g + om;
     }
   }
-  const float cse = __shfl(a.L > kWave ? cs[1] : cs[0], (a.L - 1) & (kWave - 1), kWave);
+  const float cse = wave_read_lane(a.L > kWave ? cs[1] : cs[0], (a.L - 1) & (kWave - 1));
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
     const int u = lane + kWave * jj;
@@ -305,23 +331,30 @@ __device__ __forceinline__ double reduce_angle(double x) {
   return x - kTwoPi * __builtin_rint(x * kInv2PiD);
 }
 
-// KR values of one row of a K-major tile (BwT or XT) at byte offset kb.
+// KR values of one row of a K-major tile (BwT or XT) at byte offset kb
+// (whole 16-byte pieces, or one 8-byte piece).
 template <typename T, int KR>
 __device__ __forceinline__ void store_krow(const Tile& t, uint32_t row, uint32_t kb,
                                            const float (&v)[KR]) {
   if constexpr (sizeof(T) == 2) {
-    static_assert(KR == 4 || KR == 8, "row of 8 or 16 bytes");
+    static_assert(KR == 4 || KR % 8 == 0, "row of 8 bytes or whole 16-byte pieces");
     if constexpr (KR == 4) {
       const u32x2 w = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
       t.ref<u32x2>(row, kb) = w;
     } else {
-      const u32x4 w = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
-                       pack_bf16(v[6], v[7])};
-      t.ref<u32x4>(row, kb) = w;
+#pragma unroll
+      for (int h = 0; h < KR / 8; ++h) {
+        const u32x4 w = {pack_bf16(v[8 * h], v[8 * h + 1]), pack_bf16(v[8 * h + 2], v[8 * h + 3]),
+                         pack_bf16(v[8 * h + 4], v[8 * h + 5]),
+                         pack_bf16(v[8 * h + 6], v[8 * h + 7])};
+        t.ref<u32x4>(row, kb + 16 * h) = w;
+      }
     }
   } else {
-    static_assert(KR == 4, "row of 16 bytes");
-    t.ref<f32x4>(row, kb) = f32x4{v[0], v[1], v[2], v[3]};
+    static_assert(KR % 4 == 0, "whole 16-byte pieces");
+#pragma unroll
+    for (int h = 0; h < KR / 4; ++h)
+      t.ref<f32x4>(row, kb + 16 * h) = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
   }
 }
 
@@ -347,7 +380,9 @@ __device__ __forceinline__ void rotate_item(const PrefillLayout& lay, int kp, in
   using T = typename C::T;
   constexpr int R = C::R;
   const double* s_part = reinterpret_cast<const double*>(smem + lay.off_part);
+  // sum of the preceding blocks' angles; unrolled so the LDS reads overlap
   double pre = 0.0;
+#pragma unroll 8
   for (int q = 0; q < blk; ++q) pre += s_part[q * lay.npair + kp];
   double rv = pre * kInv2PiD;
   rv -= __builtin_rint(rv);
@@ -426,44 +461,61 @@ __device__ __forceinline__ void write_x_item(int jp, int xb, const uint32_t (&xv
       tX.ref<u32x2>((uint32_t)(2 * jp), kb) = r0;
       tX.ref<u32x2>((uint32_t)(2 * jp + 1), kb) = r1;
     } else {
-      static_assert(C::KR == 8, "x item of 4 or 8 rows");
-      u32x4 r0, r1;
+      static_assert(C::KR % 8 == 0, "x item of 4 rows or whole 8-row pieces");
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        r0[i] = __builtin_amdgcn_perm(xv[2 * i + 1], xv[2 * i], 0x05040100u);
-        r1[i] = __builtin_amdgcn_perm(xv[2 * i + 1], xv[2 * i], 0x07060302u);
+      for (int h = 0; h < C::KR / 8; ++h) {
+        u32x4 r0, r1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          r0[i] = __builtin_amdgcn_perm(xv[8 * h + 2 * i + 1], xv[8 * h + 2 * i], 0x05040100u);
+          r1[i] = __builtin_amdgcn_perm(xv[8 * h + 2 * i + 1], xv[8 * h + 2 * i], 0x07060302u);
+        }
+        tX.ref<u32x4>((uint32_t)(2 * jp), kb + 16 * h) = r0;
+        tX.ref<u32x4>((uint32_t)(2 * jp + 1), kb + 16 * h) = r1;
       }
-      tX.ref<u32x4>((uint32_t)(2 * jp), kb) = r0;
-      tX.ref<u32x4>((uint32_t)(2 * jp + 1), kb) = r1;
     }
   } else {
-    static_assert(C::KR == 4, "fp32 x item of 4 rows");
-    tX.ref<u32x4>((uint32_t)(2 * jp), kb) = u32x4{xv[0], xv[2], xv[4], xv[6]};
-    tX.ref<u32x4>((uint32_t)(2 * jp + 1), kb) = u32x4{xv[1], xv[3], xv[5], xv[7]};
+    static_assert(C::KR % 4 == 0, "fp32 x item of whole 4-row pieces");
+#pragma unroll
+    for (int h = 0; h < C::KR / 4; ++h) {
+      tX.ref<u32x4>((uint32_t)(2 * jp), kb + 16 * h) =
+          u32x4{xv[8 * h], xv[8 * h + 2], xv[8 * h + 4], xv[8 * h + 6]};
+      tX.ref<u32x4>((uint32_t)(2 * jp + 1), kb + 16 * h) =
+          u32x4{xv[8 * h + 1], xv[8 * h + 3], xv[8 * h + 5], xv[8 * h + 7]};
+    }
   }
 }
 
-// MFMA fragment of a swizzled tile: row `row`, contraction slots from k0.
+// MFMA fragment of a tile: row `row`, contraction slots from k0 (a multiple
+// of 32 for bf16).
 __device__ __forceinline__ bf16x8 load_frag(const Tile& t, uint32_t row, int k0, const bf16*) {
   const int g = (threadIdx.x & 63) >> 4;
-  return t.ref<bf16x8>(row, (uint32_t)(k0 + 8 * g) * 2u);
+  return t.ref2<bf16x8>(row, 16u * g, (uint32_t)k0 * 2u);
 }
 __device__ __forceinline__ float load_frag(const Tile& t, uint32_t row, int k0, const float*) {
   const int g = (threadIdx.x & 63) >> 4;
-  return t.ref<float>(row, (uint32_t)(k0 + g) * 4u);
+  return t.ref2<float>(row, 4u * g, (uint32_t)k0 * 4u);
+}
+
+// State tile slot m of this wave: tile index i (n-tile i % (N/16), p-tile
+// i / (N/16)), or -1.  Tiles go to the state waves [sw0, sw0 + nsw) round
+// robin; lane holds rows n = 4g..4g+3 of its 16x16 tile.
+__device__ __forceinline__ int state_tile(const WaveRoles& wr, int wave, int m, int ntiles) {
+  const int i = (wave - wr.sw0) + m * wr.nsw;
+  return (wave >= wr.sw0 && i < ntiles) ? i : -1;
 }
 
 // State tiles -> LDS copy G^T [P][N] (the B operand of the inter-chunk MFMA).
 template <class C>
-__device__ __forceinline__ void state_to_lds(const PrefillArgs& a, const f32x4 (&stt)[kMaxStTiles],
-                                             const Tile& tG) {
+__device__ __forceinline__ void state_to_lds(const PrefillArgs& a, const WaveRoles& wr,
+                                             const f32x4 (&stt)[kMaxStTiles], const Tile& tG) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int ntn = a.N / 16, ntiles = ntn * C::NPT;
 #pragma unroll
   for (int m = 0; m < kMaxStTiles; ++m) {
-    const int i = wave + m * kW;
-    if (i < ntiles) {
+    const int i = state_tile(wr, wave, m, ntiles);
+    if (i >= 0) {
       const int nt = i % ntn, pt = i / ntn;
       const uint32_t row = (uint32_t)(pt * 16 + li), nb = (uint32_t)((nt * 16 + 4 * g) * C::es);
       if constexpr (C::es == 2) {
@@ -477,45 +529,44 @@ __device__ __forceinline__ void state_to_lds(const PrefillArgs& a, const f32x4 (
 }
 
 // Chunk state S_c = sum_u w_u B~_u x_u^T (MFMA, both operands read straight
-// from the K-major tiles) folded into the state tiles: st <- R(Phi_c)(d st +
-// S_c).  Tile m of this wave is i = wave + m*kW: n-tile i % (N/16), p-tile
-// i / (N/16); lane holds rows n = 4g..4g+3.
+// from the K-major tiles) folded into this wave's state tiles: st <- R(Phi_c)
+// (d st + S_c).
 template <class C>
 __device__ __forceinline__ void state_update(const PrefillArgs& a, const PrefillLayout& lay,
-                                             float d, f32x4 (&stt)[kMaxStTiles],
-                                             const Tile& tW, const Tile& tX,
-                                             const unsigned char* smem) {
+                                             const WaveRoles& wr, float d,
+                                             f32x4 (&stt)[kMaxStTiles], const Tile& tW,
+                                             const Tile& tX, const unsigned char* smem) {
   using T = typename C::T;
   using M = typename C::M;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int ntn = a.N / 16, ntiles = ntn * C::NPT;
-  const bool share = (kW % ntn) == 0;  // both tiles of this wave share their n-tile
+  if (state_tile(wr, wave, 0, ntiles) < 0) return;
   const float2* s_crot = reinterpret_cast<const float2*>(smem + lay.off_crot);
   f32x4 acc[kMaxStTiles];
+  int tile[kMaxStTiles];
+  uint32_t nrow[kMaxStTiles], prow[kMaxStTiles];
 #pragma unroll
-  for (int m = 0; m < kMaxStTiles; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int i0 = wave, i1 = wave + kW;
-  if (i0 < ntiles) {
-    const uint32_t nrow0 = (uint32_t)((i0 % ntn) * 16 + li), prow0 = (uint32_t)((i0 / ntn) * 16 + li);
-    const uint32_t nrow1 = (uint32_t)((i1 % ntn) * 16 + li), prow1 = (uint32_t)((i1 / ntn) * 16 + li);
-    const bool two = i1 < ntiles;
-    for (int k0 = 0; k0 < lay.LRp; k0 += M::K) {
-      const typename M::frag fa = load_frag(tW, nrow0, k0, (const T*)nullptr);
-      const typename M::frag fb = load_frag(tX, prow0, k0, (const T*)nullptr);
-      acc[0] = M::mma(fa, fb, acc[0]);
-      if (two) {
-        const typename M::frag fa1 = share ? fa : load_frag(tW, nrow1, k0, (const T*)nullptr);
-        const typename M::frag fb1 = load_frag(tX, prow1, k0, (const T*)nullptr);
-        acc[1] = M::mma(fa1, fb1, acc[1]);
+  for (int m = 0; m < kMaxStTiles; ++m) {
+    acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    tile[m] = state_tile(wr, wave, m, ntiles);
+    const int i = tile[m] < 0 ? 0 : tile[m];
+    nrow[m] = (uint32_t)((i % ntn) * 16 + li);
+    prow[m] = (uint32_t)((i / ntn) * 16 + li);
+  }
+  for (int k0 = 0; k0 < lay.LRp; k0 += M::K) {
+#pragma unroll
+    for (int m = 0; m < kMaxStTiles; ++m)
+      if (tile[m] >= 0) {
+        const typename M::frag fa = load_frag(tW, nrow[m], k0, (const T*)nullptr);
+        const typename M::frag fb = load_frag(tX, prow[m], k0, (const T*)nullptr);
+        acc[m] = M::mma(fa, fb, acc[m]);
       }
-    }
   }
 #pragma unroll
   for (int m = 0; m < kMaxStTiles; ++m) {
-    const int i = wave + m * kW;
-    if (i < ntiles) {
-      const int kq = (i % ntn) * 8 + 2 * g;
+    if (tile[m] >= 0) {
+      const int kq = (tile[m] % ntn) * 8 + 2 * g;
       const float2 r0 = s_crot[kq], r1 = s_crot[kq + 1];
       const float v0 = d * stt[m][0] + acc[m][0], v1 = d * stt[m][1] + acc[m][1];
       const float v2 = d * stt[m][2] + acc[m][2], v3 = d * stt[m][3] + acc[m][3];
@@ -560,12 +611,14 @@ __device__ __forceinline__ void key_scalars4(const float* sc, int row0, float (&
   }
 }
 
-// y of one chunk: units (query block qb, p-group pg) over the waves.
+// y of one chunk: units (query block qb, group of p-tiles) over the output
+// waves.  The scores of a query block are computed once per unit, so with one
+// p-group per query block nothing is recomputed.
 template <class C>
 __device__ __forceinline__ void chunk_output(const PrefillArgs& a, const PrefillLayout& lay,
-                                             const Ctx& s, const ChunkRes& cr, const float* sc,
-                                             const Tile& tC, const Tile& tB, const Tile& tX,
-                                             const Tile& tG) {
+                                             const WaveRoles& wr, const Ctx& s,
+                                             const ChunkRes& cr, const float* sc, const Tile& tC,
+                                             const Tile& tB, const Tile& tX, const Tile& tG) {
   using T = typename C::T;
   using M = typename C::M;
   constexpr int R = C::R, P = C::P, NPT = C::NPT;
@@ -577,37 +630,36 @@ __device__ __forceinline__ void chunk_output(const PrefillArgs& a, const Prefill
   const uint32_t yb = (uint32_t)(R * P * C::es);
   const rsrc ry = make_rsrc(static_cast<unsigned char*>(a.y) + hrow * yb,
                             (uint32_t)(cr.len - 1) * s.rowX + yb);
-  // units (query block, pair of p-tiles); wave w takes units w, 2kW-1-w,
-  // 2kW+w, ... so the causal (growing) cost per query block balances
-  constexpr int PPG = NPT < 2 ? NPT : 2;
-  constexpr int NPG = NPT / PPG;
-  const int nqb = lay.LR / 16;
-  const int nunits = nqb * NPG;
+  constexpr int PPGM = NPT < 4 ? NPT : 4;  // largest p-group
+  const int ppg = wr.ppg;
 
+  // wave w takes units w, 2kW-1-w, 2kW+w, ... so the causal (growing) cost
+  // per query block balances when the units outnumber the waves
   for (int k = 0;; ++k) {
     const int unit = (k & 1) ? (k + 1) * kW - 1 - wave : k * kW + wave;
-    if (unit >= nunits) break;
-    const int qb = unit / NPG, p_lo = (unit % NPG) * PPG;
-    f32x4 acc[PPG];
+    if (unit >= wr.nout) break;
+    const int qb = unit / wr.npg, p_lo = (unit % wr.npg) * ppg;
+    f32x4 acc[PPGM];
 #pragma unroll
-    for (int pp = 0; pp < PPG; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int pp = 0; pp < PPGM; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t qrow = (uint32_t)(qb * 16 + li);
 
     // inter-chunk term: C~ G_c, rows scaled by exp(cs_t)
     for (int n0 = 0; n0 < N; n0 += M::K) {
       const typename M::frag fa = load_frag(tC, qrow, n0, (const T*)nullptr);
 #pragma unroll
-      for (int pp = 0; pp < PPG; ++pp) {
-        const typename M::frag fb =
-            load_frag(tG, (uint32_t)((p_lo + pp) * 16 + li), n0, (const T*)nullptr);
-        acc[pp] = M::mma(fa, fb, acc[pp]);
-      }
+      for (int pp = 0; pp < PPGM; ++pp)
+        if (pp < ppg) {
+          const typename M::frag fb =
+              load_frag(tG, (uint32_t)((p_lo + pp) * 16 + li), n0, (const T*)nullptr);
+          acc[pp] = M::mma(fa, fb, acc[pp]);
+        }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float scl = __expf(s_cs[(qb * 16 + 4 * g + j) / R]);
 #pragma unroll
-      for (int pp = 0; pp < PPG; ++pp) acc[pp][j] *= scl;
+      for (int pp = 0; pp < PPGM; ++pp) acc[pp][j] *= scl;
     }
 
     // intra-chunk term over key blocks up to the diagonal
@@ -650,26 +702,29 @@ __device__ __forceinline__ void chunk_output(const PrefillArgs& a, const Prefill
           fa[4 + j] = from_f32<bf16>(sct[1][j]);
         }
 #pragma unroll
-        for (int pp = 0; pp < PPG; ++pp) {
-          const uint32_t xr = (uint32_t)((p_lo + pp) * 16 + li);
-          const bf16x4 lo = tX.ref<bf16x4>(xr, (uint32_t)(kb * 16 + 4 * g) * 2u);
-          const bf16x4 hi = tX.ref<bf16x4>(xr, (uint32_t)((kb + 1) * 16 + 4 * g) * 2u);
-          bf16x8 fb;
+        for (int pp = 0; pp < PPGM; ++pp)
+          if (pp < ppg) {
+            const uint32_t xr = (uint32_t)((p_lo + pp) * 16 + li);
+            // key rows kb*16 + 4g.. and (kb+1)*16 + 4g.. (kb even: 64-byte groups)
+            const bf16x4 lo = tX.ref2<bf16x4>(xr, 8u * g, (uint32_t)kb * 32u);
+            const bf16x4 hi = tX.ref2<bf16x4>(xr, 32u + 8u * g, (uint32_t)kb * 32u);
+            bf16x8 fb;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            fb[j] = lo[j];
-            fb[4 + j] = hi[j];
+            for (int j = 0; j < 4; ++j) {
+              fb[j] = lo[j];
+              fb[4 + j] = hi[j];
+            }
+            acc[pp] = Mfma<bf16>::mma(fa, fb, acc[pp]);
           }
-          acc[pp] = Mfma<bf16>::mma(fa, fb, acc[pp]);
-        }
       } else {
 #pragma unroll
-        for (int pp = 0; pp < PPG; ++pp) {
-          const f32x4 xv =
-              tX.ref<f32x4>((uint32_t)((p_lo + pp) * 16 + li), (uint32_t)(kb * 16 + 4 * g) * 4u);
+        for (int pp = 0; pp < PPGM; ++pp)
+          if (pp < ppg) {
+            const f32x4 xv =
+                tX.ref2<f32x4>((uint32_t)((p_lo + pp) * 16 + li), 16u * g, (uint32_t)kb * 64u);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[pp] = Mfma<float>::mma(sct[0][j], xv[j], acc[pp]);
-        }
+            for (int j = 0; j < 4; ++j) acc[pp] = Mfma<float>::mma(sct[0][j], xv[j], acc[pp]);
+          }
       }
     }
 
@@ -679,14 +734,15 @@ __device__ __forceinline__ void chunk_output(const PrefillArgs& a, const Prefill
       const uint32_t u = (uint32_t)(row / R), q = (uint32_t)(row % R);
       const uint32_t off = u * s.rowX + (q * P + (uint32_t)li) * C::es;
 #pragma unroll
-      for (int pp = 0; pp < PPG; ++pp) {
-        const uint32_t o = off + (uint32_t)((p_lo + pp) * 16 * C::es);
-        if constexpr (C::es == 2)
-          __builtin_amdgcn_raw_buffer_store_b16(
-              __builtin_bit_cast(unsigned short, from_f32<bf16>(acc[pp][j])), ry, (int)o, 0, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[pp][j]), ry, (int)o, 0, 0);
-      }
+      for (int pp = 0; pp < PPGM; ++pp)
+        if (pp < ppg) {
+          const uint32_t o = off + (uint32_t)((p_lo + pp) * 16 * C::es);
+          if constexpr (C::es == 2)
+            __builtin_amdgcn_raw_buffer_store_b16(
+                __builtin_bit_cast(unsigned short, from_f32<bf16>(acc[pp][j])), ry, (int)o, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[pp][j]), ry, (int)o, 0, 0);
+        }
     }
   }
 }
@@ -700,12 +756,33 @@ template <class C>
 __device__ __forceinline__ Tiles make_tiles(const PrefillArgs& a, const PrefillLayout& lay,
                                             unsigned char* smem) {
   const uint32_t nb = (uint32_t)(a.N * C::es), kb = (uint32_t)(lay.LRp * C::es);
-  return Tiles{make_tile(smem + lay.off_Cr, nb), make_tile(smem + lay.off_Br, nb),
-               make_tile(smem + lay.off_BwT, kb), make_tile(smem + lay.off_XT, kb),
-               make_tile(smem + lay.off_GT, nb)};
+  return Tiles{make_tile(smem + lay.off_Cr, nb, C::es), make_tile(smem + lay.off_Br, nb, C::es),
+               make_tile(smem + lay.off_BwT, kb, C::es), make_tile(smem + lay.off_XT, kb, C::es),
+               make_tile(smem + lay.off_GT, nb, C::es)};
 }
 
-// [P]: this thread's items' angle sums and (wave 0) the per-token scalars.
+// Per-step copies of the strides and tiles (see opaque_u).
+__device__ __forceinline__ Ctx step_ctx(const Ctx& s) {
+  Ctx r = s;
+  r.rowB = opaque_u(s.rowB);
+  r.rowTh = opaque_u(s.rowTh);
+  r.rowDt = opaque_u(s.rowDt);
+  r.rowX = opaque_u(s.rowX);
+  return r;
+}
+__device__ __forceinline__ Tiles step_tiles(const Tiles& t, unsigned char* smem) {
+  Tiles r;
+  const Tile* src[5] = {&t.C, &t.B, &t.W, &t.X, &t.G};
+  Tile* dst[5] = {&r.C, &r.B, &r.W, &r.X, &r.G};
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint32_t off = opaque_u((uint32_t)(src[i]->base - smem));
+    *dst[i] = Tile{smem + off, opaque_u(src[i]->rowb), opaque_u(src[i]->mask)};
+  }
+  return r;
+}
+
+// [P]: this thread's item's angle sum.
 template <class C>
 __device__ __forceinline__ void step_partials(const PrefillArgs& a, const PrefillLayout& lay,
                                               const Ctx& s, const Map& m, int c,
@@ -713,10 +790,6 @@ __device__ __forceinline__ void step_partials(const PrefillArgs& a, const Prefil
                                               unsigned char* smem) {
   double* s_part = reinterpret_cast<double*>(smem + lay.off_part);
   if (m.act) s_part[m.blk * lay.npair + m.kp] = item_angle_sum<C::S>(st.th, st.dt);
-  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) {
-    const int t0 = c * a.L;
-    chunk_scalars(a, t0, min(a.L, a.T - t0), s.Ah, st.wd, st.wl, sc);
-  }
 }
 
 // [R]: rotation items and x items into LDS (consumes the staged registers).
@@ -733,8 +806,12 @@ __device__ __forceinline__ void step_rotate(const PrefillArgs& a, const PrefillL
 }
 
 template <class C>
-__global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a_in) {
   extern __shared__ __align__(16) unsigned char smem[];
+  // with N fixed at compile time every contraction loop over N unrolls and
+  // the pair / block index arithmetic folds
+  PrefillArgs a = a_in;
+  if constexpr (C::NC != 0) a.N = C::NC;
   constexpr int P = C::P;
   const PrefillLayout lay = prefill_layout(a.L, C::R, a.N, P, C::es);
   const int tid = threadIdx.x;
@@ -746,7 +823,8 @@ __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a) {
   __syncthreads();
   const int ticket = *s_ticket;
   const int BH = a.nb * a.H;
-  Ctx s;
+  Ctx s0;
+  Ctx& s = s0;
   s.seg = ticket / BH;
   s.bh = ticket % BH;
   s.b = s.bh / a.H;
@@ -767,7 +845,9 @@ __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a) {
   m.jp = tid % (P / 2);
   m.xblk = tid / (P / 2);
 
-  const Tiles t = make_tiles<C>(a, lay, smem);
+  const Tiles tiles0 = make_tiles<C>(a, lay, smem);
+  const Tiles& t = tiles0;
+  const WaveRoles wr = prefill_wave_roles(lay.LR, P);
   float* s_scal = reinterpret_cast<float*>(smem + lay.off_scal);
   double* s_sang = reinterpret_cast<double*>(smem + lay.off_sang);
   float2* s_srot = reinterpret_cast<float2*>(smem + lay.off_srot);
@@ -794,10 +874,19 @@ __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a) {
   // ---- phase 1: local exit state of the segment --------------------------
   Stage<C> stg;
   issue_loads<C, false>(a, s, m, s.c0, stg);
+  const bool scal_wave = __builtin_amdgcn_readfirstlane(tid >> 6) == kScalarWave;
+  if (scal_wave) {
+    float wd[3], wl[3];
+    scalar_loads(a, s, s.c0, wd, wl);
+    const int t0c = s.c0 * a.L;
+    chunk_scalars(a, t0c, min(a.L, a.T - t0c), s.Ah, wd, wl, s_scal);
+  }
   float seg_logdecay = 0.f;
   int buf = 0;
   for (int c = s.c0; c < s.c1; ++c) {
     float* sc = s_scal + buf * (kScalBytes / 4);
+    const Ctx s = step_ctx(s0);
+    const Tiles t = step_tiles(tiles0, smem);
     step_partials<C>(a, lay, s, m, c, stg, sc, smem);
     __syncthreads();
     step_rotate<C, false, true>(a, lay, s, m, c, stg, sc, t, smem);
@@ -807,10 +896,18 @@ __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a) {
       issue_loads<C, false>(a, s, m, c + 1, stg);
     else
       issue_loads<C, true>(a, s, m, s.c0, stg);
+    // the scalar wave prepares the next chunk's scalars (the first chunk's
+    // again after the last, for phase 3) in the other buffer
+    const int nc = c + 1 < s.c1 ? c + 1 : s.c0;
+    float wd[3], wl[3];
+    if (scal_wave) scalar_loads(a, s, nc, wd, wl);
     __syncthreads();
     const float lc = sc[4 * kLMax];
     seg_logdecay += lc;
-    state_update<C>(a, lay, __expf(lc), stt, t.W, t.X, smem);
+    state_update<C>(a, lay, wr, __expf(lc), stt, t.W, t.X, smem);
+    if (scal_wave)
+      chunk_scalars(a, nc * a.L, min(a.L, a.T - nc * a.L), s.Ah, wd, wl,
+                    s_scal + (buf ^ 1) * (kScalBytes / 4));
     buf ^= 1;
   }
 
@@ -841,8 +938,8 @@ __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a) {
     const float* src = a.ring + ((size_t)s.bh * 2 + ((s.seg - 1) & 1)) * a.N * P;
 #pragma unroll
     for (int q = 0; q < kMaxStTiles; ++q) {
-      const int i = wave + q * kW;
-      if (i < ntiles) {
+      const int i = state_tile(wr, wave, q, ntiles);
+      if (i >= 0) {
         const int nt = i % ntn, pt = i / ntn;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -858,8 +955,8 @@ __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a) {
   float* dst = a.ring + ((size_t)s.bh * 2 + (s.seg & 1)) * a.N * P;
 #pragma unroll
   for (int q = 0; q < kMaxStTiles; ++q) {
-    const int i = wave + q * kW;
-    if (i < ntiles) {
+    const int i = state_tile(wr, wave, q, ntiles);
+    if (i >= 0) {
       const int nt = i % ntn, pt = i / ntn;
       const int kq = nt * 8 + 2 * g;
       const float2 r0 = s_srot[kq], r1 = s_srot[kq + 1];
@@ -894,14 +991,23 @@ __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a) {
   for (int c = s.c0; c < s.c1; ++c) {
     float* sc = s_scal + buf * (kScalBytes / 4);
     const bool more = c + 1 < s.c1;
+    const Ctx s = step_ctx(s0);
+    const Tiles t = step_tiles(tiles0, smem);
     step_partials<C>(a, lay, s, m, c, stg, sc, smem);
     __syncthreads();
     step_rotate<C, true, false>(a, lay, s, m, c, stg, sc, t, smem);
-    state_to_lds<C>(a, stt, t.G);
+    state_to_lds<C>(a, wr, stt, t.G);
     if (more) issue_loads<C, true>(a, s, m, c + 1, stg);
     __syncthreads();
-    chunk_output<C>(a, lay, s, chunk_res<C>(a, s, c), sc, t.C, t.B, t.X, t.G);
-    if (more) state_update<C>(a, lay, __expf(sc[4 * kLMax]), stt, t.W, t.X, smem);
+    chunk_output<C>(a, lay, wr, s, chunk_res<C>(a, s, c), sc, t.C, t.B, t.X, t.G);
+    if (more) {
+      float wd[3], wl[3];
+      if (scal_wave) scalar_loads(a, s, c + 1, wd, wl);
+      state_update<C>(a, lay, wr, __expf(sc[4 * kLMax]), stt, t.W, t.X, smem);
+      if (scal_wave)
+        chunk_scalars(a, (c + 1) * a.L, min(a.L, a.T - (c + 1) * a.L), s.Ah, wd, wl,
+                      s_scal + (buf ^ 1) * (kScalBytes / 4));
+    }
     buf ^= 1;
   }
 }
@@ -917,13 +1023,27 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// bfloat16 (the fast path) has instantiations with N fixed for the common
+// state sizes; float32 and other sizes take N at run time.
+template <typename T, int R, int P>
+hipError_t launch_trp(const PrefillArgs& a, hipStream_t stream) {
+  if constexpr (sizeof(T) == 2) {
+    switch (a.N) {
+      case 64: return launch_cfg<Cfg<T, R, P, 64>>(a, stream);
+      case 128: return launch_cfg<Cfg<T, R, P, 128>>(a, stream);
+      default: break;
+    }
+  }
+  return launch_cfg<Cfg<T, R, P, 0>>(a, stream);
+}
+
 template <typename T, int R>
 hipError_t launch_tr(const PrefillArgs& a, hipStream_t stream) {
   switch (a.P) {
-    case 16: return launch_cfg<Cfg<T, R, 16>>(a, stream);
-    case 32: return launch_cfg<Cfg<T, R, 32>>(a, stream);
-    case 64: return launch_cfg<Cfg<T, R, 64>>(a, stream);
-    case 128: return launch_cfg<Cfg<T, R, 128>>(a, stream);
+    case 16: return launch_trp<T, R, 16>(a, stream);
+    case 32: return launch_trp<T, R, 32>(a, stream);
+    case 64: return launch_trp<T, R, 64>(a, stream);
+    case 128: return launch_trp<T, R, 128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
