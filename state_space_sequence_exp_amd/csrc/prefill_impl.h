@@ -108,11 +108,12 @@ __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // A [rows][row_bytes] tile in LDS.  For 2-byte types its 16-byte columns are
-// XOR-swizzled by row within aligned groups of four columns (64 bytes), so
-// the 16 rows an MFMA fragment read touches spread over the banks, while a
-// byte offset that is a multiple of 64 still adds straight to the address of
-// the first group (fragment addresses are one per-lane base plus an
-// immediate).  4-byte tiles are not swizzled.
+// XOR-swizzled by row within aligned groups of up to eight columns (128
+// bytes), so the 16 rows an MFMA fragment read touches spread over all banks.
+// An offset that is a multiple of 128 bytes still adds straight to an
+// address, so fragment addresses are one of two per-lane bases (for the two
+// halves of a 128-byte group) plus an immediate.  4-byte tiles are not
+// swizzled.
 struct Tile {
   unsigned char* base;
   uint32_t rowb, mask;
@@ -123,18 +124,19 @@ struct Tile {
   __device__ __forceinline__ V& ref(uint32_t row, uint32_t byte) const {
     return *reinterpret_cast<V*>(base + at(row, byte));
   }
-  // element at byte `lane_byte` (< 64) of the first group plus `group_byte`
-  // (a multiple of 64)
+  // element at byte `byte` of the row, split as (byte mod 128) through the
+  // swizzle and (byte - byte mod 128) added afterwards
   template <typename V>
   __device__ __forceinline__ const V& ref2(uint32_t row, uint32_t lane_byte,
                                            uint32_t group_byte) const {
-    return *reinterpret_cast<const V*>(base + at(row, lane_byte) + group_byte);
+    const uint32_t b = lane_byte + group_byte;
+    return *reinterpret_cast<const V*>(base + at(row, b & 127u) + (b & ~127u));
   }
 };
 __device__ __forceinline__ Tile make_tile(unsigned char* base, uint32_t rowb, int esize) {
   const uint32_t ncol = rowb >> 4;
   const uint32_t low = ncol & (0u - ncol);
-  return Tile{base, rowb, esize == 2 ? (low < 4u ? low : 4u) - 1u : 0u};
+  return Tile{base, rowb, esize == 2 ? (low < 8u ? low : 8u) - 1u : 0u};
 }
 
 template <typename T_, int R_, int P_, int N_>
@@ -528,6 +530,16 @@ __device__ __forceinline__ void state_to_lds(const PrefillArgs& a, const WaveRol
   }
 }
 
+// Compile-time view of a wave's state tiles when N is fixed: with the tile
+// count a multiple of the wave count every wave holds exactly kTPW tiles and
+// no per-tile conditions are needed.
+template <class C>
+struct StateTiles {
+  static constexpr int kNT = C::NC ? (C::NC / 16) * C::NPT : 0;
+  static constexpr bool kFull = kNT != 0 && kNT % kW == 0 && kNT / kW <= kMaxStTiles;
+  static constexpr int kTPW = kFull ? kNT / kW : kMaxStTiles;
+};
+
 // Chunk state S_c = sum_u w_u B~_u x_u^T (MFMA, both operands read straight
 // from the K-major tiles) folded into this wave's state tiles: st <- R(Phi_c)
 // (d st + S_c).
@@ -538,34 +550,41 @@ __device__ __forceinline__ void state_update(const PrefillArgs& a, const Prefill
                                              const Tile& tX, const unsigned char* smem) {
   using T = typename C::T;
   using M = typename C::M;
+  using ST = StateTiles<C>;
+  constexpr int TPW = ST::kTPW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int ntn = a.N / 16, ntiles = ntn * C::NPT;
   if (state_tile(wr, wave, 0, ntiles) < 0) return;
   const float2* s_crot = reinterpret_cast<const float2*>(smem + lay.off_crot);
-  f32x4 acc[kMaxStTiles];
-  int tile[kMaxStTiles];
-  uint32_t nrow[kMaxStTiles], prow[kMaxStTiles];
+  f32x4 acc[TPW];
+  int tile[TPW];
+  uint32_t nrow[TPW], prow[TPW];
 #pragma unroll
-  for (int m = 0; m < kMaxStTiles; ++m) {
+  for (int m = 0; m < TPW; ++m) {
     acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    tile[m] = state_tile(wr, wave, m, ntiles);
+    tile[m] = ST::kFull ? wave + m * kW : state_tile(wr, wave, m, ntiles);
     const int i = tile[m] < 0 ? 0 : tile[m];
     nrow[m] = (uint32_t)((i % ntn) * 16 + li);
     prow[m] = (uint32_t)((i / ntn) * 16 + li);
   }
+  // a wave's tiles share their n-tile when N/16 divides the number of state
+  // waves: then one A fragment serves all
+  const bool share = (wr.nsw % ntn) == 0;
   for (int k0 = 0; k0 < lay.LRp; k0 += M::K) {
+    const typename M::frag fa0 = load_frag(tW, nrow[0], k0, (const T*)nullptr);
 #pragma unroll
-    for (int m = 0; m < kMaxStTiles; ++m)
-      if (tile[m] >= 0) {
-        const typename M::frag fa = load_frag(tW, nrow[m], k0, (const T*)nullptr);
+    for (int m = 0; m < TPW; ++m)
+      if (ST::kFull || tile[m] >= 0) {
+        const typename M::frag fa =
+            (m == 0 || share) ? fa0 : load_frag(tW, nrow[m], k0, (const T*)nullptr);
         const typename M::frag fb = load_frag(tX, prow[m], k0, (const T*)nullptr);
         acc[m] = M::mma(fa, fb, acc[m]);
       }
   }
 #pragma unroll
-  for (int m = 0; m < kMaxStTiles; ++m) {
-    if (tile[m] >= 0) {
+  for (int m = 0; m < TPW; ++m) {
+    if (ST::kFull || tile[m] >= 0) {
       const int kq = (tile[m] % ntn) * 8 + 2 * g;
       const float2 r0 = s_crot[kq], r1 = s_crot[kq + 1];
       const float v0 = d * stt[m][0] + acc[m][0], v1 = d * stt[m][1] + acc[m][1];
@@ -611,6 +630,117 @@ __device__ __forceinline__ void key_scalars4(const float* sc, int row0, float (&
   }
 }
 
+// One output unit: y rows of query block qb for the PPG p-tiles from p_lo.
+template <class C, int PPG>
+__device__ __forceinline__ void output_unit(const PrefillArgs& a, const Ctx& s, const rsrc& ry,
+                                            int qb, int p_lo, const float* sc, const Tile& tC,
+                                            const Tile& tB, const Tile& tX, const Tile& tG) {
+  using T = typename C::T;
+  using M = typename C::M;
+  constexpr int R = C::R, P = C::P;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int N = a.N;
+  const float* s_cs = sc;
+  f32x4 acc[PPG];
+#pragma unroll
+  for (int pp = 0; pp < PPG; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t qrow = (uint32_t)(qb * 16 + li);
+
+  // inter-chunk term: C~ G_c, rows scaled by exp(cs_t)
+  for (int n0 = 0; n0 < N; n0 += M::K) {
+    const typename M::frag fa = load_frag(tC, qrow, n0, (const T*)nullptr);
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp) {
+      const typename M::frag fb =
+          load_frag(tG, (uint32_t)((p_lo + pp) * 16 + li), n0, (const T*)nullptr);
+      acc[pp] = M::mma(fa, fb, acc[pp]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float scl = __expf(s_cs[(qb * 16 + 4 * g + j) / R]);
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp) acc[pp][j] *= scl;
+  }
+
+  // intra-chunk term over key blocks up to the diagonal
+  const int tq = (qb * 16 + li) / R;
+  const float csq = s_cs[tq];
+  constexpr int KB = (sizeof(T) == 2) ? 2 : 1;  // 16-row key blocks per step
+  for (int kb = 0; kb * 16 <= qb * 16 + 15; kb += KB) {
+    f32x4 sct[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) sct[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n0 = 0; n0 < N; n0 += M::K) {
+      const typename M::frag fq = load_frag(tC, qrow, n0, (const T*)nullptr);
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const typename M::frag fk =
+            load_frag(tB, (uint32_t)((kb + i) * 16 + li), n0, (const T*)nullptr);
+        sct[i] = M::mma(fk, fq, sct[i]);  // rows = keys, cols = queries
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      float kcs[4], kga[4], kgom[4];
+      key_scalars4<R>(sc, (kb + i) * 16 + 4 * g, kcs, kga, kgom);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tk = ((kb + i) * 16 + 4 * g + j) / R;
+        const float wl = __expf(csq - kcs[j]) * kgom[j];
+        sct[i][j] *= tk < tq ? wl : (tk == tq ? kga[j] : 0.f);
+      }
+    }
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 fa;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        fa[j] = from_f32<bf16>(sct[0][j]);
+        fa[4 + j] = from_f32<bf16>(sct[1][j]);
+      }
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) {
+        const uint32_t xr = (uint32_t)((p_lo + pp) * 16 + li);
+        // key rows kb*16 + 4g.. and (kb+1)*16 + 4g..
+        const bf16x4 lo = tX.ref2<bf16x4>(xr, 8u * g, (uint32_t)kb * 32u);
+        const bf16x4 hi = tX.ref2<bf16x4>(xr, 32u + 8u * g, (uint32_t)kb * 32u);
+        bf16x8 fb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          fb[j] = lo[j];
+          fb[4 + j] = hi[j];
+        }
+        acc[pp] = Mfma<bf16>::mma(fa, fb, acc[pp]);
+      }
+    } else {
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) {
+        const f32x4 xv =
+            tX.ref2<f32x4>((uint32_t)((p_lo + pp) * 16 + li), 16u * g, (uint32_t)kb * 64u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[pp] = Mfma<float>::mma(sct[0][j], xv[j], acc[pp]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = qb * 16 + 4 * g + j;
+    const uint32_t u = (uint32_t)(row / R), q = (uint32_t)(row % R);
+    const uint32_t off = u * s.rowX + (q * P + (uint32_t)li) * C::es;
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp) {
+      const uint32_t o = off + (uint32_t)((p_lo + pp) * 16 * C::es);
+      if constexpr (C::es == 2)
+        __builtin_amdgcn_raw_buffer_store_b16(
+            __builtin_bit_cast(unsigned short, from_f32<bf16>(acc[pp][j])), ry, (int)o, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[pp][j]), ry, (int)o, 0, 0);
+    }
+  }
+}
+
 // y of one chunk: units (query block qb, group of p-tiles) over the output
 // waves.  The scores of a query block are computed once per unit, so with one
 // p-group per query block nothing is recomputed.
@@ -619,131 +749,24 @@ __device__ __forceinline__ void chunk_output(const PrefillArgs& a, const Prefill
                                              const WaveRoles& wr, const Ctx& s,
                                              const ChunkRes& cr, const float* sc, const Tile& tC,
                                              const Tile& tB, const Tile& tX, const Tile& tG) {
-  using T = typename C::T;
-  using M = typename C::M;
-  constexpr int R = C::R, P = C::P, NPT = C::NPT;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, li = lane & 15;
-  const int N = a.N;
-  const float* s_cs = sc;
+  constexpr int NPT = C::NPT;
+  constexpr int PPG_A = NPT < 4 ? NPT : 4;  // the two p-group widths in use
+  constexpr int PPG_B = NPT < 2 ? NPT : 2;
+  const int wave = threadIdx.x >> 6;
   const size_t hrow = ((size_t)s.b * a.T + cr.t0) * a.H + s.h;
-  const uint32_t yb = (uint32_t)(R * P * C::es);
+  const uint32_t yb = (uint32_t)(C::R * C::P * C::es);
   const rsrc ry = make_rsrc(static_cast<unsigned char*>(a.y) + hrow * yb,
                             (uint32_t)(cr.len - 1) * s.rowX + yb);
-  constexpr int PPGM = NPT < 4 ? NPT : 4;  // largest p-group
-  const int ppg = wr.ppg;
-
   // wave w takes units w, 2kW-1-w, 2kW+w, ... so the causal (growing) cost
   // per query block balances when the units outnumber the waves
   for (int k = 0;; ++k) {
     const int unit = (k & 1) ? (k + 1) * kW - 1 - wave : k * kW + wave;
     if (unit >= wr.nout) break;
-    const int qb = unit / wr.npg, p_lo = (unit % wr.npg) * ppg;
-    f32x4 acc[PPGM];
-#pragma unroll
-    for (int pp = 0; pp < PPGM; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint32_t qrow = (uint32_t)(qb * 16 + li);
-
-    // inter-chunk term: C~ G_c, rows scaled by exp(cs_t)
-    for (int n0 = 0; n0 < N; n0 += M::K) {
-      const typename M::frag fa = load_frag(tC, qrow, n0, (const T*)nullptr);
-#pragma unroll
-      for (int pp = 0; pp < PPGM; ++pp)
-        if (pp < ppg) {
-          const typename M::frag fb =
-              load_frag(tG, (uint32_t)((p_lo + pp) * 16 + li), n0, (const T*)nullptr);
-          acc[pp] = M::mma(fa, fb, acc[pp]);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float scl = __expf(s_cs[(qb * 16 + 4 * g + j) / R]);
-#pragma unroll
-      for (int pp = 0; pp < PPGM; ++pp) acc[pp][j] *= scl;
-    }
-
-    // intra-chunk term over key blocks up to the diagonal
-    const int tq = (qb * 16 + li) / R;
-    const float csq = s_cs[tq];
-    constexpr int KB = (sizeof(T) == 2) ? 2 : 1;  // 16-row key blocks per step
-    for (int kb = 0; kb * 16 <= qb * 16 + 15; kb += KB) {
-      f32x4 sct[KB];
-#pragma unroll
-      for (int i = 0; i < KB; ++i) sct[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int n0 = 0; n0 < N; n0 += M::K) {
-        const typename M::frag fq = load_frag(tC, qrow, n0, (const T*)nullptr);
-#pragma unroll
-        for (int i = 0; i < KB; ++i) {
-          const typename M::frag fk =
-              load_frag(tB, (uint32_t)((kb + i) * 16 + li), n0, (const T*)nullptr);
-          sct[i] = M::mma(fk, fq, sct[i]);  // rows = keys, cols = queries
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        float kcs[4], kga[4], kgom[4];
-        key_scalars4<R>(sc, (kb + i) * 16 + 4 * g, kcs, kga, kgom);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int tk = ((kb + i) * 16 + 4 * g + j) / R;
-          float w = 0.f;
-          if (tk < tq)
-            w = __expf(csq - kcs[j]) * kgom[j];
-          else if (tk == tq)
-            w = kga[j];
-          sct[i][j] *= w;
-        }
-      }
-      if constexpr (sizeof(T) == 2) {
-        bf16x8 fa;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          fa[j] = from_f32<bf16>(sct[0][j]);
-          fa[4 + j] = from_f32<bf16>(sct[1][j]);
-        }
-#pragma unroll
-        for (int pp = 0; pp < PPGM; ++pp)
-          if (pp < ppg) {
-            const uint32_t xr = (uint32_t)((p_lo + pp) * 16 + li);
-            // key rows kb*16 + 4g.. and (kb+1)*16 + 4g.. (kb even: 64-byte groups)
-            const bf16x4 lo = tX.ref2<bf16x4>(xr, 8u * g, (uint32_t)kb * 32u);
-            const bf16x4 hi = tX.ref2<bf16x4>(xr, 32u + 8u * g, (uint32_t)kb * 32u);
-            bf16x8 fb;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              fb[j] = lo[j];
-              fb[4 + j] = hi[j];
-            }
-            acc[pp] = Mfma<bf16>::mma(fa, fb, acc[pp]);
-          }
-      } else {
-#pragma unroll
-        for (int pp = 0; pp < PPGM; ++pp)
-          if (pp < ppg) {
-            const f32x4 xv =
-                tX.ref2<f32x4>((uint32_t)((p_lo + pp) * 16 + li), 16u * g, (uint32_t)kb * 64u);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[pp] = Mfma<float>::mma(sct[0][j], xv[j], acc[pp]);
-          }
-      }
-    }
-
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = qb * 16 + 4 * g + j;
-      const uint32_t u = (uint32_t)(row / R), q = (uint32_t)(row % R);
-      const uint32_t off = u * s.rowX + (q * P + (uint32_t)li) * C::es;
-#pragma unroll
-      for (int pp = 0; pp < PPGM; ++pp)
-        if (pp < ppg) {
-          const uint32_t o = off + (uint32_t)((p_lo + pp) * 16 * C::es);
-          if constexpr (C::es == 2)
-            __builtin_amdgcn_raw_buffer_store_b16(
-                __builtin_bit_cast(unsigned short, from_f32<bf16>(acc[pp][j])), ry, (int)o, 0, 0);
-          else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[pp][j]), ry, (int)o, 0, 0);
-        }
-    }
+    const int qb = unit / wr.npg, p_lo = (unit % wr.npg) * wr.ppg;
+    if (wr.ppg == PPG_A)
+      output_unit<C, PPG_A>(a, s, ry, qb, p_lo, sc, tC, tB, tX, tG);
+    else
+      output_unit<C, PPG_B>(a, s, ry, qb, p_lo, sc, tC, tB, tX, tG);
   }
 }
 
