@@ -120,7 +120,7 @@ def time_prefill(cfg, g, steps, warmup, flush=True):
     dev = torch.device("cuda:0")
     ws_bytes = m3.prefill_workspace_size(cfg.batch, cfg.seqlen, cfg.nheads, cfg.P, cfg.N, cfg.R,
                                          cfg.chunk, g["x"].dtype)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     y = torch.empty_like(g["x"])
     hf = torch.empty((cfg.batch, cfg.nheads, cfg.N, cfg.P), dtype=torch.float32, device=dev)
     scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) if flush else None
@@ -308,7 +308,7 @@ def main():
         "config": {"workload": "SISO prefill: batch 4, T=2048, 16 heads, N=64, P=64, R=1, "
                                "bf16 x/B/C, fp32 state, chunk 64",
                    "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "none"},
-        "roofline": {"kernel": "m3_prefill (chunk_state + state_scan + chunk_out)",
+        "roofline": {"kernel": "prefill_kernel (fused chained prefill, one launch per m3_prefill call)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": nbytes,

@@ -108,10 +108,22 @@ size_t m3_prefill_workspace_size(const m3_dims* dims, int chunk, m3_dtype dtype)
  * element.
  *
  * workspace: device scratch of at least m3_prefill_workspace_size() bytes,
- * 256-byte aligned, owned by the caller, not read before being written.
- * Concurrent calls need distinct workspaces.
+ * 256-byte aligned, owned by the caller.  It starts with the chain's int32
+ * counters -- word 0 the work ticket, word 1 the error word, word 2 the
+ * finished-workgroup count, word 3 unused, then one word per (batch, head)
+ * unit: 16 + 4 * batch * nheads bytes -- and holds, from byte 4096 or from
+ * the first 256-byte boundary past the counters (whichever is later), the
+ * exit states that chain the segments of a sequence.  A call needs its
+ * counters zero on entry and leaves them zero (its last workgroup resets
+ * them), so a buffer zero-filled once serves every later call as long as
+ * batch * nheads <= 1020, or as long as no call has more units than the call
+ * before it on this buffer; otherwise zero the counter bytes before the call.
+ * The error word is left nonzero, and stays so, if a segment ever waited
+ * beyond its bounded spin for its predecessor (1), or if a call found the
+ * counters not zero on entry (2; that call computes nothing).  Concurrent
+ * calls need distinct workspaces.
  *
- * Returns M3_SUCCESS once all kernels are enqueued.  y and h_final must not
+ * Returns M3_SUCCESS once the kernel is enqueued (one launch per call).  y and h_final must not
  * overlap the inputs.  batch == 0 or seqlen == 0 enqueues nothing (h_final,
  * if given, is then zero-filled when seqlen == 0 and batch > 0).
  */

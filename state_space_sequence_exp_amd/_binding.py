@@ -161,7 +161,7 @@ def prefill(x, dt, A, lam, theta, B, C, chunk: int, *, y=None, h_final=None,
     d = _dims(nb, nt, nh, npd, nn, nr)
     need = int(lib.m3_prefill_workspace_size(ctypes.byref(d), int(chunk), code))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.m3_prefill(ctypes.byref(d), code, int(chunk), _ptr(x5), _ptr(dt), _ptr(A), _ptr(lam),
                         _ptr(theta), _ptr(B5), _ptr(C5), _ptr(y), _ptr(h_final),

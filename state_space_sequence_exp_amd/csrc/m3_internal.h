@@ -37,7 +37,8 @@ struct PrefillArgs {
   float* ring;   // [B*H][2][N][P] exit states of the two most recent segments
   int* flags;    // [B*H] segments of each sequence whose exit state is published
   int* ticket;   // [1]   next segment ticket (work order)
-  int* err;      // [1]   nonzero if a wait for a predecessor timed out
+  int* err;      // [1]   1: a wait for a predecessor timed out; 2: counters not zero at entry
+  int* done;     // [1]   finished workgroups; the last one zeroes flags, ticket, done
 };
 
 struct DecodeArgs {

@@ -47,21 +47,21 @@ m3_status check_prefill_shape(const m3_dims* d, int chunk, m3_dtype dtype) {
 }
 
 struct WsCarve {
-  size_t off_ring, off_flags, total;
+  size_t off_ring, total;
 };
 
-// ring: exit states of the two latest segments of every sequence;
-// flags: per-sequence published-segment counters, then the ticket counter
-// and the error word.
+// The counters come first, at offsets that do not depend on the shape:
+// int32 words ticket, error, finished workgroups, (unused), then one
+// published-segment counter per (batch, head) unit.  The exit-state ring
+// (the two latest segments of every unit) starts at 4 KiB or past the
+// counters, whichever is later, so calls with at most 1020 units never store
+// states where any call keeps counters.
 WsCarve carve(const m3_dims* d, int /*chunk*/, m3_dtype /*dtype*/) {
   WsCarve w;
   const size_t units = (size_t)d->batch * d->nheads;
-  size_t o = 0;
-  w.off_ring = o;
-  o = round256(o + units * 2 * (size_t)d->dstate_n * d->headdim_p * sizeof(float));
-  w.off_flags = o;
-  o = round256(o + (units + 2) * sizeof(int));
-  w.total = o;
+  const size_t counters = round256((4 + units) * sizeof(int));
+  w.off_ring = counters > 4096 ? counters : 4096;
+  w.total = round256(w.off_ring + units * 2 * (size_t)d->dstate_n * d->headdim_p * sizeof(float));
   return w;
 }
 
@@ -138,9 +138,10 @@ m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void*
   if (work) {
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     a.ring = reinterpret_cast<float*>(ws + w.off_ring);
-    a.flags = reinterpret_cast<int*>(ws + w.off_flags);
-    a.ticket = a.flags + a.nb * a.H;
+    a.ticket = reinterpret_cast<int*>(ws);
     a.err = a.ticket + 1;
+    a.done = a.ticket + 2;
+    a.flags = a.ticket + 4;
   }
   const hipError_t e = m3::launch_prefill(a, dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;

@@ -1,17 +1,9 @@
-// prefill.hip -- host side of the chunked prefill: chain-counter reset,
-// segment sizing and dispatch to the per-type kernels (prefill_bf16_r*.hip,
+// prefill.hip -- host side of the chunked prefill: segment sizing and dispatch to the per-type kernels (prefill_bf16_r*.hip,
 // prefill_f32.hip; the kernel itself is in prefill_impl.h).
 #include "m3_internal.h"
 
 namespace m3 {
 namespace {
-
-// flags[n] (published segments per sequence), then the ticket counter and
-// the error word, all zero before every launch (a fill kernel, not a memset,
-// so the launch can be captured in a graph).
-__global__ void reset_kernel(int* flags, int n) {
-  for (int i = threadIdx.x; i < n + 2; i += blockDim.x) flags[i] = 0;
-}
 
 __global__ void fill_zero_kernel(float* p, size_t n) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -41,9 +33,6 @@ hipError_t launch_prefill(const PrefillArgs& a, m3_dtype dtype, hipStream_t stre
                        a.h_final, n);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(256), 0, stream, a.flags, a.nb * a.H);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if (dtype != M3_BF16) return launch_prefill_f32(a, stream);
   switch (a.R) {
     case 1: return launch_prefill_bf16_r1(a, stream);

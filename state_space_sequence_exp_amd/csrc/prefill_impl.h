@@ -61,7 +61,8 @@
 // drains.  Exit states travel through a two-slot ring per sequence with
 // device-coherent (sc1) stores and loads, and a per-sequence counter that is
 // raised only after the stores have completed; the wait is bounded and
-// raises an error word instead of hanging.
+// raises an error word (1) instead of hanging.  A ticket outside the grid
+// (counters not zero at entry) raises the error word (2) and does no work.
 #pragma once
 
 #include "m3_device.h"
@@ -828,23 +829,15 @@ __device__ __forceinline__ void step_rotate(const PrefillArgs& a, const PrefillL
                                       t.W, smem);
 }
 
+// One workgroup's segment: local exit state, chain, outputs.  `ticket` is
+// known to lie inside the grid.
 template <class C>
-__global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a_in) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  // with N fixed at compile time every contraction loop over N unrolls and
-  // the pair / block index arithmetic folds
-  PrefillArgs a = a_in;
-  if constexpr (C::NC != 0) a.N = C::NC;
+__device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const PrefillLayout& lay,
+                                                int ticket, unsigned char* smem) {
   constexpr int P = C::P;
-  const PrefillLayout lay = prefill_layout(a.L, C::R, a.N, P, C::es);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
-
-  int* s_ticket = reinterpret_cast<int*>(smem + lay.off_misc);
-  if (tid == 0) *s_ticket = atomicAdd(a.ticket, 1);
-  __syncthreads();
-  const int ticket = *s_ticket;
   const int BH = a.nb * a.H;
   Ctx s0;
   Ctx& s = s0;
@@ -1032,6 +1025,46 @@ __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a_in) {
                       s_scal + (buf ^ 1) * (kScalBytes / 4));
     }
     buf ^= 1;
+  }
+}
+
+template <class C>
+__global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a_in) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  // with N fixed at compile time every contraction loop over N unrolls and
+  // the pair / block index arithmetic folds
+  PrefillArgs a = a_in;
+  if constexpr (C::NC != 0) a.N = C::NC;
+  const PrefillLayout lay = prefill_layout(a.L, C::R, a.N, C::P, C::es);
+  const int tid = threadIdx.x;
+  int* s_misc = reinterpret_cast<int*>(smem + lay.off_misc);
+  if (tid == 0) s_misc[0] = atomicAdd(a.ticket, 1);
+  __syncthreads();
+  const int ticket = s_misc[0];
+  // a ticket outside the grid means the counters were not zero at entry:
+  // report it and touch nothing else
+  if (ticket >= 0 && ticket < (int)gridDim.x)
+    prefill_segment<C>(a, lay, ticket, smem);
+  else if (tid == 0)
+    __hip_atomic_store(a.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // ---- the last workgroup to finish zeroes the chain counters -------------
+  // (so the next call on this workspace starts from zeros without a reset
+  // launch; every other workgroup has published its flag before counting
+  // itself done)
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    s_misc[1] = atomicAdd(a.done, 1) == (int)gridDim.x - 1;
+  }
+  __syncthreads();
+  if (s_misc[1]) {
+    __threadfence();
+    for (int i = tid; i < a.nb * a.H; i += kT) a.flags[i] = 0;
+    if (tid == 0) {
+      *a.ticket = 0;
+      *a.done = 0;
+    }
   }
 }
 

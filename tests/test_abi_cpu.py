@@ -56,13 +56,17 @@ def ws(d, chunk=32, dtype=m3.M3_F32):
 
 
 def test_workspace_size(lib):
-    """Two exit-state slots per (batch, head) unit plus the chain counters."""
+    """The chain counters (four words, then one per (batch, head) unit) and,
+    from 4 KiB or past the counters, two exit-state slots per unit."""
+    r256 = lambda v: (v + 255) // 256 * 256
     d = dims(2, 100, 3, 16, 32, 2)
     units = 2 * 3
-    r256 = lambda v: (v + 255) // 256 * 256
-    expect = r256(units * 2 * 32 * 16 * 4) + r256((units + 2) * 4)
+    expect = 4096 + r256(units * 2 * 32 * 16 * 4)
     assert ws(d, 32, m3.M3_F32) == expect
     assert ws(d, 32, m3.M3_BF16) == expect
+    units = 64 * 20                      # counters longer than 4 KiB
+    d = dims(64, 100, 20, 16, 32, 1)
+    assert ws(d, 32, m3.M3_BF16) == r256((units + 4) * 4) + r256(units * 2 * 32 * 16 * 4)
     assert ws(dims(0, 100), 32) == 0
     assert ws(dims(1, 0), 32) == 0
 

@@ -129,9 +129,58 @@ def test_repeatable_bitwise():
     inp = I.prefill_inputs(2, 640, 4, 64, 64, 4, "bf16", seed=51)
     g = upload_prefill(inp)
     y1, h1 = gpu_prefill(inp, 64, g)
-    y2, h2 = gpu_prefill(inp, 64, g)
+    y2, h2 = gpu_prefill(inp, 64, g, calls=3)   # one workspace, three calls
     assert np.array_equal(from_gpu(y1), from_gpu(y2))
     assert np.array_equal(from_gpu(h1), from_gpu(h2))
+
+
+def test_workspace_reused_across_shapes():
+    """The kernel returns the workspace's chain counters to zero, so one
+    zero-filled buffer serves successive calls of different shapes."""
+    import torch
+    import state_space_sequence_exp_amd as m3
+    big = I.prefill_inputs(2, 900, 3, 64, 64, 1, "bf16", seed=61)
+    small = I.prefill_inputs(1, 300, 2, 64, 32, 2, "bf16", seed=62)
+    gb, gs = upload_prefill(big), upload_prefill(small)
+    need = max(m3.prefill_workspace_size(2, 900, 3, 64, 64, 1, 64, gb["x"].dtype),
+               m3.prefill_workspace_size(1, 300, 2, 32, 64, 2, 32, gs["x"].dtype))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    outs = []
+    for g, chunk in ((gb, 64), (gs, 32), (gb, 64), (gs, 32)):
+        outs.append(m3.prefill(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"],
+                               chunk, workspace=ws))
+    torch.cuda.synchronize()
+    for (y, h), inp in ((outs[2], big), (outs[3], small)):
+        y_ref, h_ref = oracle_prefill(inp)
+        assert rel_l2(from_gpu(y), y_ref) <= TOL["bf16"]
+        assert rel_l2(from_gpu(h), h_ref) <= TOL["bf16"]
+    assert np.array_equal(from_gpu(outs[0][0]), from_gpu(outs[2][0]))
+    assert np.array_equal(from_gpu(outs[1][0]), from_gpu(outs[3][0]))
+    assert not ws[:4 * (2 * 3 + 4)].view(torch.int32).cpu().numpy().any()
+
+
+def test_dirty_counters_reported():
+    """A workspace whose ticket word is not zero on entry makes every
+    workgroup skip its segment and raise the error word (2); the counters are
+    still returned to zero, so the next call (error word cleared) is correct."""
+    import torch
+    import state_space_sequence_exp_amd as m3
+    inp = I.prefill_inputs(1, 200, 2, 32, 64, 1, "bf16", seed=63)
+    g = upload_prefill(inp)
+    need = m3.prefill_workspace_size(1, 200, 2, 64, 32, 1, 64, g["x"].dtype)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    words = ws[:4 * (2 + 4)].view(torch.int32)
+    words[0] = 1 << 20                   # a ticket far past the grid
+    m3.prefill(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"], 64, workspace=ws)
+    w = words.cpu().numpy()
+    assert w[1] == 2 and w[0] == 0 and w[2] == 0 and not w[4:].any(), w
+    words[1] = 0
+    y, h = m3.prefill(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"], 64,
+                      workspace=ws)
+    assert not words.cpu().numpy().any()
+    y_ref, h_ref = oracle_prefill(inp)
+    assert rel_l2(from_gpu(y), y_ref) <= TOL["bf16"]
+    assert rel_l2(from_gpu(h), h_ref) <= TOL["bf16"]
 
 
 def test_empty_and_optional_outputs():
