@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define M3SSM_VERSION 100 /* 1.0.0 */
+#define M3SSM_VERSION 110 /* 1.1.0 */
 
 typedef enum {
   M3_SUCCESS = 0,
@@ -131,6 +131,45 @@ m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void*
                      const float* dt, const float* A, const float* lam, const float* theta,
                      const void* B, const void* C, void* y, float* h_final, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * Prefill that continues a sequence: the same computation as m3_prefill, but
+ * the recurrence starts from a given state and previous token instead of
+ * zero, so a long prompt can be processed in pieces (or resumed from a cached
+ * prefix) with the result of one call over the whole sequence, up to rounding.
+ * The first token's update is then
+ *
+ *   h_0 = alpha_0 R_0 (h0 + (1-lam_0) dt_0 B_prev x_prev^T) + lam_0 dt_0 B_0 x_0^T
+ *
+ * -- the trapezoid rule's previous-input term (Mamba-3 paper summary,
+ * Proposition 1; explainer, first improvement) with the previous token's
+ * input, and the state and that term rotated together (explainer, second
+ * improvement).  After a call over tokens 0..T1-1 the next piece passes
+ * h0 = that call's h_final, x_prev = x[:, T1-1] and B_prev = B[:, T1-1]
+ * (raw, unrotated), exactly as m3_decode_step does for one token.  The
+ * chunked form chains chunks by the same recurrence on the state (explainer:
+ * parallel inside a chunk, recurrent across chunks), so a piece boundary is
+ * one more chunk boundary.
+ *
+ * h0:      [batch, nheads, N, P] fp32, unrotated frame, or NULL (zero state).
+ * x_prev:  [batch, nheads, R, P] in x's dtype, or NULL (no previous token).
+ * B_prev:  [batch, nheads, R, N] in x's dtype; NULL exactly when x_prev is.
+ *
+ * h_final may be h0 itself (the state is then updated in place) but must
+ * not partially overlap it.  With seqlen == 0, h_final (if given) receives
+ * h0, or zeros when h0 is NULL.  Everything else -- layouts, alignment,
+ * workspace, errors -- is as for m3_prefill; the extra pointers need element
+ * alignment.  With h0 or x_prev given the call enqueues two kernels: one
+ * that writes each sequence's entry state into the workspace, then the
+ * prefill kernel.  M3_ERR_INVALID_VALUE if exactly one of x_prev and B_prev
+ * is NULL or h_final partially overlaps h0.
+ */
+m3_status m3_prefill_from_state(const m3_dims* dims, m3_dtype dtype, int chunk, const float* h0,
+                                const void* x_prev, const void* B_prev, const void* x,
+                                const float* dt, const float* A, const float* lam,
+                                const float* theta, const void* B, const void* C, void* y,
+                                float* h_final, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /*
  * One decode step for `batch` independent sequences (dims->seqlen ignored):

@@ -6,7 +6,7 @@ hand-written HIP kernels for AMD Instinct MI355X (gfx950), behind a C ABI
 Python entry points (ctypes; PyTorch tensors supply device memory and the
 current stream):
 
-    prefill(x, dt, A, lam, theta, B, C, chunk) -> (y, h_final)
+    prefill(x, dt, A, lam, theta, B, C, chunk[, h0, x_prev, B_prev]) -> (y, h_final)
     decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta) -> (y_t, h)
     prefill_workspace_size(...), version(), status_string(code)
 

@@ -24,7 +24,7 @@ M3_BF16 = 1
 
 # every function declared in include/m3ssm.h
 ABI_SYMBOLS = ("m3_version", "m3_status_string", "m3_prefill_workspace_size", "m3_prefill",
-               "m3_decode_step")
+               "m3_prefill_from_state", "m3_decode_step")
 
 
 class M3Error(RuntimeError):
@@ -63,6 +63,9 @@ def load_library(path: Optional[str] = None):
     lib.m3_prefill.restype = ctypes.c_int
     lib.m3_prefill.argtypes = [dp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp,
                                vp, vp, ctypes.c_size_t, vp]
+    lib.m3_prefill_from_state.restype = ctypes.c_int
+    lib.m3_prefill_from_state.argtypes = [dp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.m3_decode_step.restype = ctypes.c_int
     lib.m3_decode_step.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    vp, vp]
@@ -124,13 +127,18 @@ def prefill_workspace_size(batch, seqlen, nheads, P, N, R, chunk, dtype) -> int:
     return int(load_library().m3_prefill_workspace_size(ctypes.byref(d), int(chunk), code))
 
 
-def prefill(x, dt, A, lam, theta, B, C, chunk: int, *, y=None, h_final=None,
-            want_h_final: bool = True, workspace=None, stream=None) -> Tuple:
+def prefill(x, dt, A, lam, theta, B, C, chunk: int, *, h0=None, x_prev=None, B_prev=None,
+            y=None, h_final=None, want_h_final: bool = True, workspace=None,
+            stream=None) -> Tuple:
     """Chunked prefill on the GPU.
 
     x [Bt,T,H,R,P] (or [Bt,T,H,P] for R=1); B, C [Bt,T,H,R,N] (or [Bt,T,H,N]);
     dt, lam [Bt,T,H]; theta [Bt,T,H,N/2]; A [H].  x, B, C float32 or
     bfloat16 (same dtype), the rest float32, all contiguous on one GPU.
+    To continue a sequence pass h0 [Bt,H,N,P] float32 (the state before the
+    first token) and/or x_prev [Bt,H,R,P] with B_prev [Bt,H,R,N] (the
+    previous token's x and B, x's dtype; R axis optional for R=1); this calls
+    m3_prefill_from_state.  h_final may be h0 (in-place update).
     Returns (y with x's shape and dtype, h_final [Bt,H,N,P] float32 or None).
     """
     import torch
@@ -158,16 +166,32 @@ def prefill(x, dt, A, lam, theta, B, C, chunk: int, *, y=None, h_final=None,
         h_final = torch.empty((nb, nh, nn, npd), dtype=torch.float32, device=dev)
     elif h_final is not None:
         _check(h_final, "h_final", torch.float32, (nb, nh, nn, npd), dev)
+    cont = h0 is not None or x_prev is not None or B_prev is not None
+    if h0 is not None:
+        _check(h0, "h0", torch.float32, (nb, nh, nn, npd), dev)
+    if (x_prev is None) != (B_prev is None):
+        raise ValueError("x_prev and B_prev go together")
+    if x_prev is not None:
+        x_prev = x_prev.unsqueeze(2) if x_prev.dim() == 3 else x_prev
+        B_prev = B_prev.unsqueeze(2) if B_prev.dim() == 3 else B_prev
+        _check(x_prev, "x_prev", x.dtype, (nb, nh, nr, npd), dev)
+        _check(B_prev, "B_prev", x.dtype, (nb, nh, nr, nn), dev)
     d = _dims(nb, nt, nh, npd, nn, nr)
     need = int(lib.m3_prefill_workspace_size(ctypes.byref(d), int(chunk), code))
     if workspace is None and need > 0:
         workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.m3_prefill(ctypes.byref(d), code, int(chunk), _ptr(x5), _ptr(dt), _ptr(A), _ptr(lam),
-                        _ptr(theta), _ptr(B5), _ptr(C5), _ptr(y), _ptr(h_final),
-                        _ptr(workspace), ws_bytes, _stream(stream))
+    if cont:
+        st = lib.m3_prefill_from_state(ctypes.byref(d), code, int(chunk), _ptr(h0), _ptr(x_prev),
+                                       _ptr(B_prev), _ptr(x5), _ptr(dt), _ptr(A), _ptr(lam),
+                                       _ptr(theta), _ptr(B5), _ptr(C5), _ptr(y), _ptr(h_final),
+                                       _ptr(workspace), ws_bytes, _stream(stream))
+    else:
+        st = lib.m3_prefill(ctypes.byref(d), code, int(chunk), _ptr(x5), _ptr(dt), _ptr(A),
+                            _ptr(lam), _ptr(theta), _ptr(B5), _ptr(C5), _ptr(y), _ptr(h_final),
+                            _ptr(workspace), ws_bytes, _stream(stream))
     if st != M3_SUCCESS:
-        raise M3Error(st, "m3_prefill")
+        raise M3Error(st, "m3_prefill_from_state" if cont else "m3_prefill")
     return y, h_final
 
 

@@ -31,6 +31,10 @@ struct PrefillArgs {
   const float* theta;
   const void* B;
   const void* C;
+  const float* h0;      // [B*H][N][P] state before the first token, or null (zero)
+  const void* x_prev;   // [B*H][R][P] input of the token before the first, or null (zero)
+  const void* B_prev;   // [B*H][R][N] its B (null exactly when x_prev is)
+  int cont;             // 1: the entry kernel staged each sequence's entry state in ring slot 1
   void* y;
   float* h_final;
   // workspace carve

@@ -89,10 +89,15 @@ size_t m3_prefill_workspace_size(const m3_dims* dims, int chunk, m3_dtype dtype)
   return carve(dims, chunk, dtype).total;
 }
 
-m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void* x,
-                     const float* dt, const float* A, const float* lam, const float* theta,
-                     const void* B, const void* C, void* y, float* h_final, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+m3_status prefill_impl(const m3_dims* dims, m3_dtype dtype, int chunk, const float* h0,
+                       const void* x_prev, const void* B_prev, const void* x, const float* dt,
+                       const float* A, const float* lam, const float* theta, const void* B,
+                       const void* C, void* y, float* h_final, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   const m3_status st = check_prefill_shape(dims, chunk, dtype);
   if (st != M3_SUCCESS) return st;
   const bool work = dims->batch > 0 && dims->seqlen > 0;
@@ -105,6 +110,18 @@ m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void*
       return M3_ERR_INVALID_VALUE;
   }
   if (h_final && !aligned(h_final, 4)) return M3_ERR_INVALID_VALUE;
+  // the continuation inputs: the previous token's x and B come together
+  if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_INVALID_VALUE;
+  if ((h0 && !aligned(h0, 4)) || (x_prev && !aligned(x_prev, es)) ||
+      (B_prev && !aligned(B_prev, es)))
+    return M3_ERR_INVALID_VALUE;
+  // h_final may be h0 itself but must not partially overlap it
+  if (h0 && h_final && h0 != h_final) {
+    const size_t hbytes =
+        (size_t)dims->batch * dims->nheads * dims->dstate_n * dims->headdim_p * sizeof(float);
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(h0), a1 = reinterpret_cast<uintptr_t>(h_final);
+    if (a0 < a1 + hbytes && a1 < a0 + hbytes) return M3_ERR_INVALID_VALUE;
+  }
   size_t need = 0;
   WsCarve w = {};
   if (work) {
@@ -133,6 +150,10 @@ m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void*
   a.theta = theta;
   a.B = B;
   a.C = C;
+  a.h0 = h0;
+  a.x_prev = x_prev;
+  a.B_prev = B_prev;
+  a.cont = (h0 != nullptr || x_prev != nullptr) ? 1 : 0;
   a.y = y;
   a.h_final = h_final;
   if (work) {
@@ -145,6 +166,28 @@ m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void*
   }
   const hipError_t e = m3::launch_prefill(a, dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void* x,
+                     const float* dt, const float* A, const float* lam, const float* theta,
+                     const void* B, const void* C, void* y, float* h_final, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return prefill_impl(dims, dtype, chunk, nullptr, nullptr, nullptr, x, dt, A, lam, theta, B, C,
+                      y, h_final, workspace, workspace_bytes, stream);
+}
+
+m3_status m3_prefill_from_state(const m3_dims* dims, m3_dtype dtype, int chunk, const float* h0,
+                                const void* x_prev, const void* B_prev, const void* x,
+                                const float* dt, const float* A, const float* lam,
+                                const float* theta, const void* B, const void* C, void* y,
+                                float* h_final, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return prefill_impl(dims, dtype, chunk, h0, x_prev, B_prev, x, dt, A, lam, theta, B, C, y,
+                      h_final, workspace, workspace_bytes, stream);
 }
 
 m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in, float* h_out,

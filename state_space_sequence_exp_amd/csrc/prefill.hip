@@ -1,13 +1,48 @@
-// prefill.hip -- host side of the chunked prefill: segment sizing and dispatch to the per-type kernels (prefill_bf16_r*.hip,
-// prefill_f32.hip; the kernel itself is in prefill_impl.h).
+// prefill.hip -- host side of the chunked prefill (segment sizing, dispatch to the per-type
+// kernels of prefill_bf16_r*.hip and prefill_f32.hip, whose body is prefill_impl.h) and two
+// small kernels: the empty-sequence final state and the continuation entry state.
+#include "m3_device.h"
 #include "m3_internal.h"
 
 namespace m3 {
 namespace {
 
-__global__ void fill_zero_kernel(float* p, size_t n) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.f;
+// h_final of an empty sequence: the given initial state, or zero.  dst may
+// equal src.
+__global__ void copy_or_zero_kernel(float* dst, const float* src, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src ? src[i] : 0.f;
+}
+
+// Entry state of each sequence's first chunk when the sequence continues
+// from a given state h0 and previous token (x_prev, B_prev):
+// G = h0 + (1 - lam_0) dt_0 B_prev x_prev^T, the state plus the trapezoid's
+// previous-input term, which the first token's update decays and rotates
+// together.  Written to ring slot 1 of each sequence, where the prefill
+// kernel's first segment reads its entry.  One thread per state element.
+template <typename T>
+__global__ void entry_kernel(PrefillArgs a) {
+  const size_t np = (size_t)a.N * a.P;
+  const size_t total = (size_t)a.nb * a.H * np;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t bh = i / np, e = i % np;
+    const int n = (int)(e / a.P), p = (int)(e % a.P);
+    float v = a.h0 ? a.h0[i] : 0.f;
+    if (a.x_prev) {
+      const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+      const size_t tok0 = (size_t)b * a.T * a.H + h;  // the sequence's first token
+      const float w0 = (1.f - a.lam[tok0]) * a.dt[tok0];
+      const T* xp = static_cast<const T*>(a.x_prev) + bh * a.R * a.P;
+      const T* bp = static_cast<const T*>(a.B_prev) + bh * a.R * a.N;
+      float acc = 0.f;
+      for (int r = 0; r < a.R; ++r)
+        acc = __builtin_fmaf(to_f32(bp[r * a.N + n]), to_f32(xp[r * a.P + p]), acc);
+      v = __builtin_fmaf(w0, acc, v);
+    }
+    a.ring[(bh * 2 + 1) * np + e] = v;
+  }
 }
 
 }  // namespace
@@ -29,9 +64,21 @@ hipError_t launch_prefill(const PrefillArgs& a, m3_dtype dtype, hipStream_t stre
   if (a.T == 0) {
     if (!a.h_final) return hipSuccess;
     const size_t n = (size_t)a.nb * a.H * a.N * a.P;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                       a.h_final, n);
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
+                       dim3(256), 0, stream, a.h_final, a.h0, n);
     return hipGetLastError();
+  }
+  if (a.h0 || a.x_prev) {
+    const size_t n = (size_t)a.nb * a.H * a.N * a.P;
+    const size_t blocks = (n + 255) / 256;
+    const dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
+    if (dtype == M3_BF16)
+      hipLaunchKernelGGL(entry_kernel<bf16>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(entry_kernel<float>, grid, dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   if (dtype != M3_BF16) return launch_prefill_f32(a, stream);
   switch (a.R) {

@@ -938,8 +938,11 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
   f32x4 ent[kMaxStTiles];
 #pragma unroll
   for (int q = 0; q < kMaxStTiles; ++q) ent[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (s.seg > 0) {
-    if (tid == 0) {
+  // the entry of a sequence's first segment is zero, or (a.cont) the state
+  // staged in the ring slot a predecessor would have used by the entry kernel
+  // that ran before this one
+  if (s.seg > 0 || a.cont) {
+    if (tid == 0 && s.seg > 0) {
       int spins = 0;
       while (__hip_atomic_load(a.flags + s.bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
              s.seg) {

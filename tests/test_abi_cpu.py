@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.m3_version() == 100
+    assert lib.m3_version() == 110
     for code in range(5):
         s = m3.status_string(code)
         assert s.startswith("M3_")
@@ -132,6 +132,47 @@ def test_prefill_pointer_and_workspace_validation(lib):
     assert lib.m3_prefill(ctypes.byref(d0), m3.M3_F32, 32, None, None, None, None, None, None,
                           None, None, None, None, 0, None) == m3.M3_SUCCESS
     assert lib.m3_prefill(None, m3.M3_F32, 32, *args, None, ok, need, None) == m3.M3_ERR_INVALID_VALUE
+
+
+def test_prefill_from_state_validation(lib):
+    """The continuation entry point validates like m3_prefill, plus its own
+    pointers: x_prev and B_prev together, element alignment, and h_final equal
+    to h0 or disjoint from it."""
+    d = dims(b=2, h=3, p=16, n=32, r=2)
+    ok = ctypes.c_void_p(0x100000)
+    mis = ctypes.c_void_p(0x100001)
+    need = ws(d)
+    hbytes = 2 * 3 * 32 * 16 * 4
+    args = [ok] * 8          # x, dt, A, lam, theta, B, C, y
+
+    def call(h0=None, xp=None, bp=None, hf=None, dd=d, a=args, w=ok, wb=need):
+        return lib.m3_prefill_from_state(ctypes.byref(dd), m3.M3_F32, 32, h0, xp, bp, *a, hf, w,
+                                         wb, None)
+    assert call(xp=ok) == m3.M3_ERR_INVALID_VALUE            # x_prev without B_prev
+    assert call(bp=ok) == m3.M3_ERR_INVALID_VALUE            # B_prev without x_prev
+    assert call(h0=mis) == m3.M3_ERR_INVALID_VALUE
+    assert call(xp=mis, bp=ok) == m3.M3_ERR_INVALID_VALUE
+    assert call(xp=ok, bp=mis) == m3.M3_ERR_INVALID_VALUE
+    h0 = 0x200000
+    # h_final partially overlapping h0
+    assert call(h0=ctypes.c_void_p(h0), hf=ctypes.c_void_p(h0 + 256)) == m3.M3_ERR_INVALID_VALUE
+    assert call(h0=ctypes.c_void_p(h0 + 256), hf=ctypes.c_void_p(h0)) == m3.M3_ERR_INVALID_VALUE
+    # the shared checks still apply
+    assert call(dd=dims(n=15)) == m3.M3_ERR_INVALID_VALUE
+    assert call(h0=ok, w=None) == m3.M3_ERR_WORKSPACE
+    bad = list(args)
+    bad[0] = None
+    assert call(h0=ok, a=bad) == m3.M3_ERR_INVALID_VALUE
+    # nothing to do: succeeds without touching the device
+    d0 = dims(b=0)
+    assert lib.m3_prefill_from_state(ctypes.byref(d0), m3.M3_F32, 32, ok, ok, ok, None, None,
+                                     None, None, None, None, None, None, None, None, 0,
+                                     None) == m3.M3_SUCCESS
+    # disjoint h_final, and h_final == h0, pass validation (checked here with a
+    # null workspace, which is reported after the pointer checks)
+    assert call(h0=ctypes.c_void_p(h0), hf=ctypes.c_void_p(h0 + hbytes),
+                w=None) == m3.M3_ERR_WORKSPACE
+    assert call(h0=ctypes.c_void_p(h0), hf=ctypes.c_void_p(h0), w=None) == m3.M3_ERR_WORKSPACE
 
 
 def test_decode_validation(lib):
