@@ -89,16 +89,27 @@ struct PrefillLayout {
   uint32_t off_misc;   // 16 bytes: the workgroup's ticket
   uint32_t off_Cr;     // [LR][N]   C~ (rotated C)
   uint32_t off_Br;     // [LR][N]   B~ (rotated B)
-  uint32_t off_BwT;    // [N][LRp]  B~ weighted by each token's state weight, transposed
-  uint32_t off_XT;     // [P][LRp]  x transposed
+  int KM;      // row length (elements) of the two contraction-major tiles
+  uint32_t off_BwT;    // [N][KM]   B~ weighted by each token's state weight, transposed
+  uint32_t off_XT;     // [P][KM]   x transposed
   uint32_t off_GT;     // [P][N]    chunk entry state, transposed
   uint32_t total;
 };
 
-__host__ __device__ inline PrefillLayout prefill_layout(int L, int R, int N, int P, int esize) {
+// Whether the kernel instantiated with N fixed at compile time takes the
+// shape: bfloat16, N of 64 or 128 and a chunk of at most 64 tokens, whose
+// contraction-major tiles then have a fixed row of 64 R elements, so every
+// tile's geometry is a compile-time constant.
+__host__ __device__ constexpr bool prefill_fixed_shape(int L, int N, int esize) {
+  return esize == 2 && (N == 64 || N == 128) && L <= 64;
+}
+
+__host__ __device__ inline PrefillLayout prefill_layout(int L, int R, int N, int P, int esize,
+                                                        bool fixed = false) {
   PrefillLayout c;
   c.LR = L * R;
   c.LRp = esize == 2 ? (c.LR + 31) / 32 * 32 : c.LR;
+  c.KM = fixed ? 64 * R : c.LRp;
   c.S = prefill_item_tokens(esize, R);
   c.npair = N / 2;
   c.nblk = L / c.S;
@@ -114,8 +125,8 @@ __host__ __device__ inline PrefillLayout prefill_layout(int L, int R, int N, int
   o = align_up_u32(o, 16);
   c.off_Cr = o; o += (uint32_t)c.LR * N * esize;
   c.off_Br = o; o += (uint32_t)c.LR * N * esize;
-  c.off_BwT = o; o += (uint32_t)N * c.LRp * esize;
-  c.off_XT = o; o += (uint32_t)P * c.LRp * esize;
+  c.off_BwT = o; o += (uint32_t)N * c.KM * esize;
+  c.off_XT = o; o += (uint32_t)P * c.KM * esize;
   c.off_GT = o; o += (uint32_t)P * N * esize;
   c.total = o;
   return c;

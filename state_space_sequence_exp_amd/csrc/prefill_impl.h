@@ -373,20 +373,22 @@ __device__ __forceinline__ double item_angle_sum(const float (&th)[S], const flo
 // Rotation item (pair kp, token block blk): angles from the preceding blocks'
 // sums, rotated B~ (and C~) pairs, the weighted transposed B~ rows, and for
 // the last block the chunk's total rotation (and the segment angle sum).
+// s_part holds the items' angle sums (block-major), s_crot receives the
+// chunk's total rotation per pair and s_sang the segment's angle sums.
 template <class C, bool kWithC, bool kAccumSeg>
-__device__ __forceinline__ void rotate_item(const PrefillLayout& lay, int kp, int blk,
+__device__ __forceinline__ void rotate_item(int npair, int nblk, int kp, int blk,
                                             const float (&th)[C::S], const float (&dt)[C::S],
                                             const uint32_t (&bv)[C::KR * C::PW],
                                             const uint32_t (&cv)[C::KR * C::PW],
                                             const float* s_w, const Tile& tB, const Tile& tC,
-                                            const Tile& tW, unsigned char* smem) {
+                                            const Tile& tW, const double* s_part, float2* s_crot,
+                                            double* s_sang) {
   using T = typename C::T;
   constexpr int R = C::R;
-  const double* s_part = reinterpret_cast<const double*>(smem + lay.off_part);
   // sum of the preceding blocks' angles; unrolled so the LDS reads overlap
   double pre = 0.0;
 #pragma unroll 8
-  for (int q = 0; q < blk; ++q) pre += s_part[q * lay.npair + kp];
+  for (int q = 0; q < blk; ++q) pre += s_part[q * npair + kp];
   double rv = pre * kInv2PiD;
   rv -= __builtin_rint(rv);
   float r = static_cast<float>(rv);  // revolutions
@@ -436,17 +438,14 @@ __device__ __forceinline__ void rotate_item(const PrefillLayout& lay, int kp, in
   const uint32_t kb = (uint32_t)(blk * C::KR * C::es);
   store_krow<T, C::KR>(tW, (uint32_t)(2 * kp), kb, wb0);
   store_krow<T, C::KR>(tW, (uint32_t)(2 * kp + 1), kb, wb1);
-  if (blk == lay.nblk - 1) {
+  if (blk == nblk - 1) {
     // the chunk's total angle; the chain multiplies its rotation over the
     // whole sequence, so it takes the accurate sine/cosine
     const double tot = pre + item_angle_sum<C::S>(th, dt);
     float sn, cn;
     sincosf(static_cast<float>(reduce_angle(tot)), &sn, &cn);
-    reinterpret_cast<float2*>(smem + lay.off_crot)[kp] = make_float2(cn, sn);
-    if constexpr (kAccumSeg) {
-      double* s_sang = reinterpret_cast<double*>(smem + lay.off_sang);
-      s_sang[kp] = reduce_angle(s_sang[kp] + tot);
-    }
+    s_crot[kp] = make_float2(cn, sn);
+    if constexpr (kAccumSeg) s_sang[kp] = reduce_angle(s_sang[kp] + tot);
   }
 }
 
@@ -779,7 +778,7 @@ struct Tiles {
 template <class C>
 __device__ __forceinline__ Tiles make_tiles(const PrefillArgs& a, const PrefillLayout& lay,
                                             unsigned char* smem) {
-  const uint32_t nb = (uint32_t)(a.N * C::es), kb = (uint32_t)(lay.LRp * C::es);
+  const uint32_t nb = (uint32_t)(a.N * C::es), kb = (uint32_t)(lay.KM * C::es);
   return Tiles{make_tile(smem + lay.off_Cr, nb, C::es), make_tile(smem + lay.off_Br, nb, C::es),
                make_tile(smem + lay.off_BwT, kb, C::es), make_tile(smem + lay.off_XT, kb, C::es),
                make_tile(smem + lay.off_GT, nb, C::es)};
@@ -794,6 +793,10 @@ __device__ __forceinline__ Ctx step_ctx(const Ctx& s) {
   r.rowX = opaque_u(s.rowX);
   return r;
 }
+// With N fixed the geometry is a compile-time constant (prefill_fixed_shape:
+// rows of N elements, contraction-major rows of 64 R) and only the bases are
+// made opaque.
+template <class C>
 __device__ __forceinline__ Tiles step_tiles(const Tiles& t, unsigned char* smem) {
   Tiles r;
   const Tile* src[5] = {&t.C, &t.B, &t.W, &t.X, &t.G};
@@ -801,7 +804,14 @@ __device__ __forceinline__ Tiles step_tiles(const Tiles& t, unsigned char* smem)
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
     const uint32_t off = opaque_u((uint32_t)(src[i]->base - smem));
-    *dst[i] = Tile{smem + off, opaque_u(src[i]->rowb), opaque_u(src[i]->mask)};
+    if constexpr (C::NC != 0) {
+      const bool km = i == 2 || i == 3;
+      const uint32_t rowb = (uint32_t)((km ? 64 * C::R : C::NC) * C::es);
+      const uint32_t ncol = rowb >> 4, low = ncol & (0u - ncol);
+      *dst[i] = Tile{smem + off, rowb, (low < 8u ? low : 8u) - 1u};
+    } else {
+      *dst[i] = Tile{smem + off, opaque_u(src[i]->rowb), opaque_u(src[i]->mask)};
+    }
   }
   return r;
 }
@@ -825,8 +835,10 @@ __device__ __forceinline__ void step_rotate(const PrefillArgs& a, const PrefillL
   const float* s_w = sc + 3 * kLMax;
   if (m.xact) write_x_item<C>(m.jp, m.xblk, st.x, t.X);
   if (m.act)
-    rotate_item<C, kWithC, kAccumSeg>(lay, m.kp, m.blk, st.th, st.dt, st.b, st.c, s_w, t.B, t.C,
-                                      t.W, smem);
+    rotate_item<C, kWithC, kAccumSeg>(
+        lay.npair, lay.nblk, m.kp, m.blk, st.th, st.dt, st.b, st.c, s_w, t.B, t.C, t.W,
+        reinterpret_cast<const double*>(smem + lay.off_part),
+        reinterpret_cast<float2*>(smem + lay.off_crot), reinterpret_cast<double*>(smem + lay.off_sang));
 }
 
 // One workgroup's segment: local exit state, chain, outputs.  `ticket` is
@@ -870,9 +882,12 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
   const int npair = lay.npair;
   const int ntn = a.N / 16, ntiles = ntn * (P / 16);
 
-  // zero the contraction padding of the K-major tiles (never written again)
-  if (lay.LRp > lay.LR) {
-    const int padb = (lay.LRp - lay.LR) * C::es;  // bytes per row, a multiple of 16
+  // zero the K-major tiles past the chunk's rows (never written again): the
+  // contraction padding, and the rest of a fixed-length row, which the key
+  // blocks of a chunk shorter than 32 rows read past the end of B~ and only
+  // mask out (so it must hold finite values)
+  if (lay.KM > lay.LR) {
+    const int padb = (lay.KM - lay.LR) * C::es;  // bytes per row, a multiple of 16
     const int per = padb / 16;
     for (int i = tid; i < (a.N + P) * per; i += kT) {
       const int row = i / per, col = i % per;
@@ -902,7 +917,7 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
   for (int c = s.c0; c < s.c1; ++c) {
     float* sc = s_scal + buf * (kScalBytes / 4);
     const Ctx s = step_ctx(s0);
-    const Tiles t = step_tiles(tiles0, smem);
+    const Tiles t = step_tiles<C>(tiles0, smem);
     step_partials<C>(a, lay, s, m, c, stg, sc, smem);
     __syncthreads();
     step_rotate<C, false, true>(a, lay, s, m, c, stg, sc, t, smem);
@@ -1011,7 +1026,7 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     float* sc = s_scal + buf * (kScalBytes / 4);
     const bool more = c + 1 < s.c1;
     const Ctx s = step_ctx(s0);
-    const Tiles t = step_tiles(tiles0, smem);
+    const Tiles t = step_tiles<C>(tiles0, smem);
     step_partials<C>(a, lay, s, m, c, stg, sc, smem);
     __syncthreads();
     step_rotate<C, true, false>(a, lay, s, m, c, stg, sc, t, smem);
@@ -1031,30 +1046,23 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
   }
 }
 
-template <class C>
-__global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a_in) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  // with N fixed at compile time every contraction loop over N unrolls and
-  // the pair / block index arithmetic folds
-  PrefillArgs a = a_in;
-  if constexpr (C::NC != 0) a.N = C::NC;
-  const PrefillLayout lay = prefill_layout(a.L, C::R, a.N, C::P, C::es);
-  const int tid = threadIdx.x;
-  int* s_misc = reinterpret_cast<int*>(smem + lay.off_misc);
-  if (tid == 0) s_misc[0] = atomicAdd(a.ticket, 1);
+// The workgroup's ticket (its segment).  A ticket outside the grid means the
+// counters were not zero at entry: the caller reports it (bad_ticket) and
+// touches nothing else.  s_misc: two ints of LDS.
+__device__ __forceinline__ int take_ticket(const PrefillArgs& a, int* s_misc) {
+  if (threadIdx.x == 0) s_misc[0] = atomicAdd(a.ticket, 1);
   __syncthreads();
-  const int ticket = s_misc[0];
-  // a ticket outside the grid means the counters were not zero at entry:
-  // report it and touch nothing else
-  if (ticket >= 0 && ticket < (int)gridDim.x)
-    prefill_segment<C>(a, lay, ticket, smem);
-  else if (tid == 0)
-    __hip_atomic_store(a.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return s_misc[0];
+}
+__device__ __forceinline__ void bad_ticket(const PrefillArgs& a) {
+  if (threadIdx.x == 0) __hip_atomic_store(a.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-  // ---- the last workgroup to finish zeroes the chain counters -------------
-  // (so the next call on this workspace starts from zeros without a reset
-  // launch; every other workgroup has published its flag before counting
-  // itself done)
+// The last workgroup to finish zeroes the chain counters, so the next call
+// on this workspace starts from zeros without a reset launch (every other
+// workgroup has published its flag before counting itself done).
+__device__ __forceinline__ void finish_workgroup(const PrefillArgs& a, int* s_misc) {
+  const int tid = threadIdx.x;
   __syncthreads();
   if (tid == 0) {
     __threadfence();
@@ -1072,8 +1080,27 @@ __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a_in) {
 }
 
 template <class C>
+__global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a_in) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  // with N fixed at compile time every contraction loop over N unrolls and
+  // the pair / block index arithmetic folds
+  PrefillArgs a = a_in;
+  if constexpr (C::NC != 0) a.N = C::NC;
+  const PrefillLayout lay = prefill_layout(a.L, C::R, a.N, C::P, C::es, C::NC != 0);
+  int* s_misc = reinterpret_cast<int*>(smem + lay.off_misc);
+  // (the range test stays at the call: the segment code is compiled knowing
+  // the ticket lies in the grid)
+  const int ticket = take_ticket(a, s_misc);
+  if (ticket >= 0 && ticket < (int)gridDim.x)
+    prefill_segment<C>(a, lay, ticket, smem);
+  else
+    bad_ticket(a);
+  finish_workgroup(a, s_misc);
+}
+
+template <class C>
 hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
-  const PrefillLayout lay = prefill_layout(a.L, C::R, a.N, C::P, C::es);
+  const PrefillLayout lay = prefill_layout(a.L, C::R, a.N, C::P, C::es, C::NC != 0);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<C>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.total);
   if (e != hipSuccess) return e;
@@ -1083,15 +1110,18 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
 }
 
 // bfloat16 (the fast path) has instantiations with N fixed for the common
-// state sizes; float32 and other sizes take N at run time.
+// state sizes and chunks of at most 64 tokens (every tile geometry a
+// compile-time constant); float32 and other shapes take N at run time.
 template <typename T, int R, int P>
 hipError_t launch_trp(const PrefillArgs& a, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
-    switch (a.N) {
-      case 64: return launch_cfg<Cfg<T, R, P, 64>>(a, stream);
-      case 128: return launch_cfg<Cfg<T, R, P, 128>>(a, stream);
-      default: break;
-    }
+    if (prefill_fixed_shape(a.L, a.N, 2) &&
+        prefill_layout(a.L, R, a.N, P, 2, true).total <= kLdsLimit)
+      switch (a.N) {
+        case 64: return launch_cfg<Cfg<T, R, P, 64>>(a, stream);
+        case 128: return launch_cfg<Cfg<T, R, P, 128>>(a, stream);
+        default: break;
+      }
   }
   return launch_cfg<Cfg<T, R, P, 0>>(a, stream);
 }
