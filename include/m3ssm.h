@@ -20,6 +20,14 @@
  * improvement"): x_t is P x R and B_t, C_t are N x R, so B x^T is a rank-R
  * product and y_t is R x P.  h_{-1} = 0 and B_{-1} x_{-1}^T = 0.
  *
+ * Reduced forms.  Every entry point takes lam and theta as optional: a NULL
+ * lam means lam = 1, the exponential-Euler rule -- the previous-input term
+ * vanishes and the update is Mamba-2's h = e^{dt A} h + dt B x^T (paper
+ * summary, Proposition 1 with lam = 1; paper translation, Remark 5) -- and a
+ * NULL theta means theta = 0, a real-valued state with no rotation (the
+ * complex transition of the explainer's "second improvement" switched off).
+ * Both NULL is the Mamba-2 recurrence on the same kernels.
+ *
  * Layouts (row-major, dense, no strides).  T is the storage type chosen by
  * m3_dtype (float or bfloat16) for x, B, C and y; everything else is float:
  *   x, y       [batch, T, H, R, P]   (x_t stored as its transpose, P contiguous)
@@ -192,6 +200,10 @@ m3_status m3_prefill_from_state(const m3_dims* dims, m3_dtype dtype, int chunk, 
  * First step of a fresh sequence: h_in = 0 and x_prev = B_prev = 0.  After a
  * prefill of T tokens: h_in = that call's h_final, x_prev = x_{T-1},
  * B_prev = B_{T-1} (the raw, unrotated inputs of the last prefilled token).
+ *
+ * lam and theta may be NULL (the reduced forms above).  Without lam the
+ * previous token's term vanishes: x_prev and B_prev are not read and may be
+ * NULL; with lam they are required.  Without theta, theta is not read.
  */
 m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in, float* h_out,
                          const void* x_t, const void* x_prev, const void* B_t,

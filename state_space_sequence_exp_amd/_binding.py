@@ -135,6 +135,8 @@ def prefill(x, dt, A, lam, theta, B, C, chunk: int, *, h0=None, x_prev=None, B_p
     x [Bt,T,H,R,P] (or [Bt,T,H,P] for R=1); B, C [Bt,T,H,R,N] (or [Bt,T,H,N]);
     dt, lam [Bt,T,H]; theta [Bt,T,H,N/2]; A [H].  x, B, C float32 or
     bfloat16 (same dtype), the rest float32, all contiguous on one GPU.
+    lam=None gives the exponential-Euler rule (lam = 1, Mamba-2's
+    discretisation) and theta=None a real state (no rotation).
     To continue a sequence pass h0 [Bt,H,N,P] float32 (the state before the
     first token) and/or x_prev [Bt,H,R,P] with B_prev [Bt,H,R,N] (the
     previous token's x and B, x's dtype; R axis optional for R=1); this calls
@@ -155,8 +157,10 @@ def prefill(x, dt, A, lam, theta, B, C, chunk: int, *, h0=None, x_prev=None, B_p
     _check(B5, "B", x.dtype, (nb, nt, nh, nr, nn), dev)
     _check(C5, "C", x.dtype, (nb, nt, nh, nr, nn), dev)
     _check(dt, "dt", torch.float32, (nb, nt, nh), dev)
-    _check(lam, "lam", torch.float32, (nb, nt, nh), dev)
-    _check(theta, "theta", torch.float32, (nb, nt, nh, nn // 2), dev)
+    if lam is not None:
+        _check(lam, "lam", torch.float32, (nb, nt, nh), dev)
+    if theta is not None:
+        _check(theta, "theta", torch.float32, (nb, nt, nh, nn // 2), dev)
     _check(A, "A", torch.float32, (nh,), dev)
     if y is None:
         y = torch.empty_like(x)
@@ -201,6 +205,8 @@ def decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta, *, h_out=No
 
     h [S,H,N,P] float32; x_t, x_prev [S,H,R,P]; B_t, B_prev, C_t [S,H,R,N]
     (float32 or bfloat16); dt, lam [S,H]; theta [S,H,N/2]; A [H].
+    lam=None gives the exponential-Euler rule (lam = 1; x_prev and B_prev
+    are then not read and may be None) and theta=None a real state.
     h_out defaults to h itself (in-place update).  Returns (y_t [S,H,R,P],
     h_out).
     """
@@ -211,13 +217,21 @@ def decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta, *, h_out=No
     dev = h.device
     code = _dtype_code(x_t)
     _check(h, "h", torch.float32, (ns, nh, nn, npd), dev)
+    if lam is None and x_prev is None and B_prev is None:
+        x_prev = B_prev = None
+    elif x_prev is None or B_prev is None:
+        raise ValueError("x_prev and B_prev are required with lam")
     for name, t in (("x_t", x_t), ("x_prev", x_prev)):
-        _check(t, name, x_t.dtype, (ns, nh, nr, npd), dev)
+        if t is not None:
+            _check(t, name, x_t.dtype, (ns, nh, nr, npd), dev)
     for name, t in (("B_t", B_t), ("B_prev", B_prev), ("C_t", C_t)):
-        _check(t, name, x_t.dtype, (ns, nh, nr, nn), dev)
+        if t is not None:
+            _check(t, name, x_t.dtype, (ns, nh, nr, nn), dev)
     _check(dt, "dt", torch.float32, (ns, nh), dev)
-    _check(lam, "lam", torch.float32, (ns, nh), dev)
-    _check(theta, "theta", torch.float32, (ns, nh, nn // 2), dev)
+    if lam is not None:
+        _check(lam, "lam", torch.float32, (ns, nh), dev)
+    if theta is not None:
+        _check(theta, "theta", torch.float32, (ns, nh, nn // 2), dev)
     _check(A, "A", torch.float32, (nh,), dev)
     if h_out is None:
         h_out = h

@@ -15,6 +15,11 @@
 //       c_r[n]   = C_t[r][n]
 //   * each element then needs one 2x2 rotation, 2R fused multiply-adds and R
 //     more for its share of y; y is reduced over N through LDS.
+//
+// Two reduced forms are compiled separately: without lam (lam = 1, the
+// exponential-Euler rule of Mamba-2) the previous token's term vanishes and
+// x_prev, B_prev are not read; without theta the state is real (no
+// rotation) and theta is not read.
 #include "m3_device.h"
 #include "m3_internal.h"
 
@@ -30,7 +35,7 @@ __device__ __forceinline__ float4 load4(const bf16* p) {
   return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
 }
 
-template <typename T, int R>
+template <typename T, int R, bool kTrap, bool kRot>
 __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) float dsm[];
   const int unit = blockIdx.x;  // s * H + h
@@ -53,12 +58,14 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
     }
   }
   const T* xt = static_cast<const T*>(a.x_t) + (size_t)unit * R * P;
-  const T* xp = static_cast<const T*>(a.x_prev) + (size_t)unit * R * P;
   float4 xc[R], xq[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     xc[r] = load4(xt + r * P + 4 * c4);
-    xq[r] = load4(xp + r * P + 4 * c4);
+    if constexpr (kTrap) {
+      const T* xp = static_cast<const T*>(a.x_prev) + (size_t)unit * R * P;
+      xq[r] = load4(xp + r * P + 4 * c4);
+    }
   }
 
   // 2. per-row coefficients in LDS
@@ -67,23 +74,25 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
   float* s_v = s_u + R * N;
   float* s_c = s_v + R * N;
   float* s_y = s_c + R * N;  // [rowgroups][R][P]
-  const float d = a.dt[unit], la = a.lam[unit];
+  const float d = a.dt[unit], la = kTrap ? a.lam[unit] : 1.f;
   const float alpha = expf(d * a.A[hh]);
   const float cu = alpha * (1.f - la) * d, cv = la * d;
   const T* Bp = static_cast<const T*>(a.B_prev) + (size_t)unit * R * N;
   const T* Bt = static_cast<const T*>(a.B_t) + (size_t)unit * R * N;
   const T* Ct = static_cast<const T*>(a.C_t) + (size_t)unit * R * N;
   for (int kp = tid; kp < npair; kp += kDecThreads) {
-    float sn, cn;
-    sincosf(d * a.theta[(size_t)unit * npair + kp], &sn, &cn);
+    float sn = 0.f, cn = 1.f;
+    if constexpr (kRot) sincosf(d * a.theta[(size_t)unit * npair + kp], &sn, &cn);
     s_rot[kp] = make_float2(cn, sn);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float2 bp = load_pair(Bp + r * N + 2 * kp);
       const float2 bt = load_pair(Bt + r * N + 2 * kp);
       const float2 ct = load_pair(Ct + r * N + 2 * kp);
-      s_u[r * N + 2 * kp] = cu * (cn * bp.x - sn * bp.y);
-      s_u[r * N + 2 * kp + 1] = cu * (sn * bp.x + cn * bp.y);
+      if constexpr (kTrap) {
+        const float2 bp = load_pair(Bp + r * N + 2 * kp);
+        s_u[r * N + 2 * kp] = cu * (cn * bp.x - sn * bp.y);
+        s_u[r * N + 2 * kp + 1] = cu * (sn * bp.x + cn * bp.y);
+      }
       s_v[r * N + 2 * kp] = cv * bt.x;
       s_v[r * N + 2 * kp + 1] = cv * bt.y;
       s_c[r * N + 2 * kp] = ct.x;
@@ -107,8 +116,10 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
       float u0[R], u1[R], v0[R], v1[R], q0[R], q1[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        u0[r] = s_u[r * N + 2 * kp];
-        u1[r] = s_u[r * N + 2 * kp + 1];
+        if constexpr (kTrap) {
+          u0[r] = s_u[r * N + 2 * kp];
+          u1[r] = s_u[r * N + 2 * kp + 1];
+        }
         v0[r] = s_v[r * N + 2 * kp];
         v1[r] = s_v[r * N + 2 * kp + 1];
         q0[r] = s_c[r * N + 2 * kp];
@@ -119,13 +130,25 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
       const float a1v[4] = {h1[i].x, h1[i].y, h1[i].z, h1[i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float n0 = alpha * (rc.x * a0v[e] - rc.y * a1v[e]);
-        float n1 = alpha * (rc.y * a0v[e] + rc.x * a1v[e]);
+        float n0, n1;
+        if constexpr (kRot) {
+          n0 = alpha * (rc.x * a0v[e] - rc.y * a1v[e]);
+          n1 = alpha * (rc.y * a0v[e] + rc.x * a1v[e]);
+        } else {
+          n0 = alpha * a0v[e];
+          n1 = alpha * a1v[e];
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const float xqe = (&xq[r].x)[e], xce = (&xc[r].x)[e];
-          n0 += u0[r] * xqe + v0[r] * xce;
-          n1 += u1[r] * xqe + v1[r] * xce;
+          const float xce = (&xc[r].x)[e];
+          if constexpr (kTrap) {
+            const float xqe = (&xq[r].x)[e];
+            n0 += u0[r] * xqe + v0[r] * xce;
+            n1 += u1[r] * xqe + v1[r] * xce;
+          } else {
+            n0 += v0[r] * xce;
+            n1 += v1[r] * xce;
+          }
         }
         o0[e] = n0;
         o1[e] = n1;
@@ -153,15 +176,27 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
   }
 }
 
-template <typename T, int R>
-hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
+template <typename T, int R, bool kTrap, bool kRot>
+hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   const int rowgroups = kDecThreads / (a.P / 4);
   const size_t lds = sizeof(float) * (2 * (a.N / 2) + 3 * R * a.N + (size_t)rowgroups * R * a.P);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, R>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const void* k = reinterpret_cast<const void*>(&decode_kernel<T, R, kTrap, kRot>);
+  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_kernel<T, R>), dim3(a.S * a.H), dim3(kDecThreads), lds, stream, a);
+  hipLaunchKernelGGL((decode_kernel<T, R, kTrap, kRot>), dim3(a.S * a.H), dim3(kDecThreads), lds,
+                     stream, a);
   return hipGetLastError();
+}
+
+// The mode follows the optional inputs: lam (trapezoid weight) and theta
+// (rotation) may each be absent.
+template <typename T, int R>
+hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
+  if (a.lam)
+    return a.theta ? launch_decode_mode<T, R, true, true>(a, stream)
+                   : launch_decode_mode<T, R, true, false>(a, stream);
+  return a.theta ? launch_decode_mode<T, R, false, true>(a, stream)
+                 : launch_decode_mode<T, R, false, false>(a, stream);
 }
 
 }  // namespace

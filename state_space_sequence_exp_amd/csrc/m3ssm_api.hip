@@ -103,7 +103,8 @@ m3_status prefill_impl(const m3_dims* dims, m3_dtype dtype, int chunk, const flo
   const bool work = dims->batch > 0 && dims->seqlen > 0;
   const uintptr_t es = esize_of(dtype);
   if (work) {
-    if (!x || !dt || !A || !lam || !theta || !B || !C || !y) return M3_ERR_INVALID_VALUE;
+    // lam and theta are optional (the exponential-Euler rule, a real state)
+    if (!x || !dt || !A || !B || !C || !y) return M3_ERR_INVALID_VALUE;
     // x, B, C and theta are read in 16-byte vectors
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(theta, 16) ||
         !aligned(y, es) || !aligned(dt, 4) || !aligned(A, 4) || !aligned(lam, 4))
@@ -205,9 +206,11 @@ m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in,
     return M3_ERR_NOT_SUPPORTED;
   if (d->batch * d->nheads > INT_MAX) return M3_ERR_NOT_SUPPORTED;
   if (d->batch == 0) return M3_SUCCESS;
-  const void* ptrs[] = {h_in, h_out, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta, y_t};
+  // lam and theta are optional; without lam x_prev and B_prev are not read
+  const void* ptrs[] = {h_in, h_out, x_t, B_t, C_t, dt, A, y_t};
   for (const void* p : ptrs)
     if (!p) return M3_ERR_INVALID_VALUE;
+  if (lam && (!x_prev || !B_prev)) return M3_ERR_INVALID_VALUE;
   // state rows in float4, x in 4-element vectors, B and C in rotation pairs
   const uintptr_t es = esize_of(dtype);
   if (!aligned(h_in, 16) || !aligned(h_out, 16) || !aligned(x_t, 4 * es) ||

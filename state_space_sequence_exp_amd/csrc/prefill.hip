@@ -33,7 +33,7 @@ __global__ void entry_kernel(PrefillArgs a) {
     if (a.x_prev) {
       const int b = (int)(bh / a.H), h = (int)(bh % a.H);
       const size_t tok0 = (size_t)b * a.T * a.H + h;  // the sequence's first token
-      const float w0 = (1.f - a.lam[tok0]) * a.dt[tok0];
+      const float w0 = a.lam ? (1.f - a.lam[tok0]) * a.dt[tok0] : 0.f;
       const T* xp = static_cast<const T*>(a.x_prev) + bh * a.R * a.P;
       const T* bp = static_cast<const T*>(a.B_prev) + bh * a.R * a.N;
       float acc = 0.f;

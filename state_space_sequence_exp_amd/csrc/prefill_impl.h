@@ -193,7 +193,9 @@ __device__ __forceinline__ ChunkRes chunk_res(const PrefillArgs& a, const Ctx& s
   const uint32_t bcb = (uint32_t)(C::R * a.N * C::es);
   r.B = make_rsrc(static_cast<const unsigned char*>(a.B) + hrow * bcb, last * s.rowB + bcb);
   r.C = make_rsrc(static_cast<const unsigned char*>(a.C) + hrow * bcb, last * s.rowB + bcb);
-  r.th = make_rsrc(a.theta + hrow * (a.N / 2), last * s.rowTh + (uint32_t)(a.N / 2) * 4);
+  // without theta (a real state) the range is empty and every angle reads 0
+  r.th = a.theta ? make_rsrc(a.theta + hrow * (a.N / 2), last * s.rowTh + (uint32_t)(a.N / 2) * 4)
+                 : make_rsrc(nullptr, 0);
   r.dt = make_rsrc(a.dt + hrow, last * s.rowDt + 4);
   const uint32_t xb = (uint32_t)(C::R * C::P * C::es);
   r.x = make_rsrc(static_cast<const unsigned char*>(a.x) + hrow * xb, last * s.rowX + xb);
@@ -277,12 +279,14 @@ __device__ __forceinline__ void scalar_loads(const PrefillArgs& a, const Ctx& s,
   const int t0 = c * a.L;
   const size_t hrow = ((size_t)s.b * a.T + t0) * a.H + s.h;
   const uint32_t bytes = (uint32_t)(a.T - t0 - 1) * s.rowDt + 4;
-  const rsrc rw = make_rsrc(a.dt + hrow, bytes), rl = make_rsrc(a.lam + hrow, bytes);
+  const rsrc rw = make_rsrc(a.dt + hrow, bytes);
+  const rsrc rl = a.lam ? make_rsrc(a.lam + hrow, bytes) : make_rsrc(nullptr, 0);
 #pragma unroll
   for (int jj = 0; jj < 3; ++jj) {
     const uint32_t o = (uint32_t)((threadIdx.x & 63) + jj * 64) * s.rowDt;
     wd[jj] = __uint_as_float(ld32(rw, o));
-    wl[jj] = __uint_as_float(ld32(rl, o));
+    // without lam the weight is 1 (the exponential-Euler rule)
+    wl[jj] = a.lam ? __uint_as_float(ld32(rl, o)) : 1.f;
   }
 }
 

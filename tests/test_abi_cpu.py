@@ -116,10 +116,16 @@ def test_prefill_pointer_and_workspace_validation(lib):
         ctypes.byref(d), m3.M3_F32, 32, *a, h, w, wb, None)
     for i in range(8):  # each input / output pointer null or misaligned
         a = list(args)
-        a[i] = None
-        assert base(a) == m3.M3_ERR_INVALID_VALUE
+        if i not in (3, 4):  # lam and theta are optional (the reduced forms)
+            a[i] = None
+            assert base(a) == m3.M3_ERR_INVALID_VALUE
         a[i] = mis
         assert base(a) == m3.M3_ERR_INVALID_VALUE
+    # without lam and theta the remaining checks still apply
+    a = list(args)
+    a[3] = a[4] = None
+    a[7] = mis
+    assert base(a) == m3.M3_ERR_INVALID_VALUE
     assert base(args, h=mis) == m3.M3_ERR_INVALID_VALUE
     a = list(args)
     a[0] = ctypes.c_void_p(0x10004)   # x must be 16-byte aligned
@@ -188,12 +194,19 @@ def test_decode_validation(lib):
     assert call(dims(b=2, p=128, n=256)) == m3.M3_ERR_NOT_SUPPORTED
     assert call(dims(b=2), dtype=5) == m3.M3_ERR_INVALID_VALUE
     assert call(dims(b=0)) == m3.M3_SUCCESS
+    # others: x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta, y_t
     for i in range(10):
         o = [fake] * 10
-        o[i] = None
-        assert call(dims(b=2), others=o) == m3.M3_ERR_INVALID_VALUE
+        if i not in (7, 8):  # lam and theta are optional
+            o[i] = None
+            assert call(dims(b=2), others=o) == m3.M3_ERR_INVALID_VALUE
         o[i] = mis
         assert call(dims(b=2), others=o) == m3.M3_ERR_INVALID_VALUE
+    # without lam, x_prev and B_prev may be null; the other checks still apply
+    o = [fake] * 10
+    o[1] = o[3] = o[7] = None
+    o[9] = mis
+    assert call(dims(b=2), others=o) == m3.M3_ERR_INVALID_VALUE
     # partial overlap of h_in and h_out is rejected
     d = dims(b=2, n=16, p=16)
     assert call(d, h_in=ctypes.c_void_p(0x10000), h_out=ctypes.c_void_p(0x10010)) == \
