@@ -94,6 +94,82 @@ def decode_bytes(cfg) -> int:
     return cfg.batch * cfg.nheads * per + cfg.nheads * 4
 
 
+def decode_mode_bytes(S, H, N, P, R, es, trap, rot) -> int:
+    """Algorithmic bytes of one decode step: the state read and written, the
+    token's inputs (the previous token's x and B and lam only for the
+    trapezoid rule, theta only with rotation) and y."""
+    per = (2 * N * P * 4 + R * P * es + 2 * R * N * es + 4 + R * P * es
+           + (R * P * es + R * N * es + 4 if trap else 0) + ((N // 2) * 4 if rot else 0))
+    return S * H * per + H * 4
+
+
+# decode-latency sweep: batch 128, 64 heads of P = 64 (a 1.5B model's layer,
+# d_inner 4096), state size 64 or 128, fp32 or bf16 inputs; Mamba-2 (the
+# exponential-Euler rule on a real state), Mamba-3 SISO and MIMO rank 4
+SWEEP = [("mamba2", 1, False, False), ("mamba3_siso", 1, True, True),
+         ("mamba3_mimo_r4", 4, True, True)]
+
+
+def decode_sweep(steps, log):
+    """Per-step decode latency for each sweep point: 'cold' steps each
+    preceded by a 512 MB scratch write (the state comes from HBM, as in a
+    model whose other layers evict it) and back-to-back steps."""
+    import numpy as np
+    import torch
+    import state_space_sequence_exp_amd as m3
+    from state_space_sequence_exp_amd import inputs as I
+    S, H, P = 128, 64, 64
+    scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+    rows = []
+    for N in (64, 128):
+        for dtype in ("f32", "bf16"):
+            for name, R, trap, rot in SWEEP:
+                log("decode sweep %s N=%d %s" % (name, N, dtype))
+                inp = I.decode_inputs(S, H, N, P, R, dtype, ring=2, seed=97 + N + R)
+                g = upload(inp)
+                del inp
+                h, y = g["h0"], None
+
+                def step(t):
+                    cur, prev = t % 2, (t - 1) % 2
+                    return m3.decode_step(h, g["x"][cur], g["x"][prev] if trap else None,
+                                          g["B"][cur], g["B"][prev] if trap else None,
+                                          g["C"][cur], g["dt"][cur], g["A"],
+                                          g["lam"][cur] if trap else None,
+                                          g["theta"][cur] if rot else None, y=y)
+                y, _ = step(0)
+                for t in range(3):
+                    step(t)
+                torch.cuda.synchronize()
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(steps)]
+                for t, (s0, e0) in enumerate(evs):
+                    scratch.fill_(1.0)
+                    s0.record()
+                    step(t)
+                    e0.record()
+                torch.cuda.synchronize()
+                cold = float(np.median([s0.elapsed_time(e0) for s0, e0 in evs])) * 1e3
+                s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s0.record()
+                for t in range(steps):
+                    step(t)
+                e0.record()
+                torch.cuda.synchronize()
+                b2b = s0.elapsed_time(e0) / steps * 1e3
+                es = 2 if dtype == "bf16" else 4
+                nb = decode_mode_bytes(S, H, N, P, R, es, trap, rot)
+                rows.append({"variant": name, "N": N, "dtype": dtype, "R": R,
+                             "us_cold": cold, "us_back_to_back": b2b,
+                             "hbm_gbs_cold": nb / (cold * 1e-6) / 1e9,
+                             "hbm_frac_cold": nb / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                             "algorithmic_bytes": nb})
+                del g, h, y
+                torch.cuda.empty_cache()
+    del scratch
+    return rows
+
+
 def upload(inp):
     import numpy as np
     import torch
@@ -254,6 +330,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the MALL between steps")
+    ap.add_argument("--no-decode-sweep", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="short untimed sequence for rocprofv3 counter runs: SISO prefill x3, "
                          "long SISO prefill x1, 10 decode steps, and a 512 MiB device copy x3 "
@@ -357,6 +434,8 @@ def main():
                                     "frac": gbs / HBM_PEAK_GBS,
                                     "traffic": measured_traffic("decode_config4"),
                                     "algorithmic_bytes": nb}}
+        if not args.no_decode_sweep:
+            sec["decode_sweep_b128_h64_p64"] = decode_sweep(20, log)
         line["secondary"] = sec
     print(json.dumps(line))
 
