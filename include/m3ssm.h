@@ -210,6 +210,48 @@ m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in,
                          const void* B_prev, const void* C_t, const float* dt, const float* A,
                          const float* lam, const float* theta, void* y_t, void* stream);
 
+/*
+ * Block-side steps on either side of the SSM (Mamba-3 paper translation,
+ * section 3.4 "Mamba-3 architecture"; paper summary, "Steps & Procedures"):
+ * BCNorm -- an RMS normalisation after the B and C projections, in the
+ * manner of QK normalisation -- then a learnable head-specific channel-wise
+ * bias on B and C, and the MIMO projections of section 3.3, which take the
+ * input from P to P x R channels and the output back, with additive
+ * parameter growth.  The pages leave the projections' exact form to an
+ * appendix they do not include; read here as per-head, per-rank
+ * channel-wise scalings (2 R P parameters per head):
+ *
+ *   m3_block_prepass:   B~[r] = B[r] / sqrt(mean_n B[r]^2 + eps) * norm_B[h] + bias_B[h][r]
+ *                       C~[r] likewise with norm_C, bias_C
+ *                       X[r]  = x * up[h][r]
+ *   m3_block_postpass:  y_out = sum_r down[h][r] * y[r]
+ *
+ * per token and head (mean over the N channels of the row).  The pre-pass's
+ * outputs are the x, B, C of m3_prefill / m3_decode_step; the post-pass
+ * takes their y.
+ *
+ * Layouts (row-major, dense; T the storage type of dtype; dims->seqlen may
+ * be 1 for a decode token):
+ *   x, y_out              [batch, T, H, P]
+ *   B, C, B~, C~          [batch, T, H, R, N]
+ *   X, y                  [batch, T, H, R, P]
+ *   norm_B, norm_C        [H, N]      float
+ *   bias_B, bias_C        [H, R, N]   float
+ *   up, down              [H, R, P]   float
+ * N must be 16, 32, 64, 128 or 256; P and R as for m3_prefill.  x, B, C,
+ * X, B~, C~, y and y_out need 16-byte alignment, the weights 4 bytes.
+ * B~ may be B and C~ may be C (in place), X may be x when R = 1; other
+ * overlaps between inputs and outputs are not allowed.  eps >= 0 (finite).
+ * One kernel launch each; batch * seqlen == 0 enqueues nothing.
+ */
+m3_status m3_block_prepass(const m3_dims* dims, m3_dtype dtype, const void* x, const void* B,
+                           const void* C, const float* norm_B, const float* norm_C,
+                           const float* bias_B, const float* bias_C, const float* up, float eps,
+                           void* x_out, void* B_out, void* C_out, void* stream);
+
+m3_status m3_block_postpass(const m3_dims* dims, m3_dtype dtype, const void* y,
+                            const float* down, void* y_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

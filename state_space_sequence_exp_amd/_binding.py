@@ -24,7 +24,7 @@ M3_BF16 = 1
 
 # every function declared in include/m3ssm.h
 ABI_SYMBOLS = ("m3_version", "m3_status_string", "m3_prefill_workspace_size", "m3_prefill",
-               "m3_prefill_from_state", "m3_decode_step")
+               "m3_prefill_from_state", "m3_decode_step", "m3_block_prepass", "m3_block_postpass")
 
 
 class M3Error(RuntimeError):
@@ -69,6 +69,11 @@ def load_library(path: Optional[str] = None):
     lib.m3_decode_step.restype = ctypes.c_int
     lib.m3_decode_step.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    vp, vp]
+    lib.m3_block_prepass.restype = ctypes.c_int
+    lib.m3_block_prepass.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     ctypes.c_float, vp, vp, vp, vp]
+    lib.m3_block_postpass.restype = ctypes.c_int
+    lib.m3_block_postpass.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp]
     if path is None:
         _lib = lib
     return lib
@@ -248,3 +253,69 @@ def decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta, *, h_out=No
     if st != M3_SUCCESS:
         raise M3Error(st, "m3_decode_step")
     return y, h_out
+
+
+def block_prepass(x, B, C, norm_B, norm_C, bias_B, bias_C, up, eps: float = 1e-6, *,
+                  x_out=None, B_out=None, C_out=None, stream=None) -> Tuple:
+    """BCNorm + bias on B and C, MIMO up-projection of x (m3_block_prepass).
+
+    x [Bt,T,H,P]; B, C [Bt,T,H,R,N] (float32 or bfloat16, same dtype);
+    norm_B, norm_C [H,N]; bias_B, bias_C [H,R,N]; up [H,R,P] float32.
+    Returns (X [Bt,T,H,R,P], B~, C~ [Bt,T,H,R,N]) in x's dtype.
+    """
+    import torch
+    lib = load_library()
+    nb, nt, nh, npd = x.shape
+    nr, nn = B.shape[3], B.shape[4]
+    dev = x.device
+    code = _dtype_code(x)
+    _check(x, "x", x.dtype, (nb, nt, nh, npd), dev)
+    _check(B, "B", x.dtype, (nb, nt, nh, nr, nn), dev)
+    _check(C, "C", x.dtype, (nb, nt, nh, nr, nn), dev)
+    _check(norm_B, "norm_B", torch.float32, (nh, nn), dev)
+    _check(norm_C, "norm_C", torch.float32, (nh, nn), dev)
+    _check(bias_B, "bias_B", torch.float32, (nh, nr, nn), dev)
+    _check(bias_C, "bias_C", torch.float32, (nh, nr, nn), dev)
+    _check(up, "up", torch.float32, (nh, nr, npd), dev)
+    if x_out is None:
+        x_out = torch.empty((nb, nt, nh, nr, npd), dtype=x.dtype, device=dev)
+    if B_out is None:
+        B_out = torch.empty_like(B)
+    if C_out is None:
+        C_out = torch.empty_like(C)
+    _check(x_out, "x_out", x.dtype, (nb, nt, nh, nr, npd), dev)
+    _check(B_out, "B_out", x.dtype, tuple(B.shape), dev)
+    _check(C_out, "C_out", x.dtype, tuple(C.shape), dev)
+    d = _dims(nb, nt, nh, npd, nn, nr)
+    st = lib.m3_block_prepass(ctypes.byref(d), code, _ptr(x), _ptr(B), _ptr(C), _ptr(norm_B),
+                              _ptr(norm_C), _ptr(bias_B), _ptr(bias_C), _ptr(up),
+                              ctypes.c_float(eps), _ptr(x_out), _ptr(B_out), _ptr(C_out),
+                              _stream(stream))
+    if st != M3_SUCCESS:
+        raise M3Error(st, "m3_block_prepass")
+    return x_out, B_out, C_out
+
+
+def block_postpass(y, down, *, y_out=None, stream=None):
+    """MIMO down-projection y_out = sum_r down[h,r] * y[r] (m3_block_postpass).
+
+    y [Bt,T,H,R,P] float32 or bfloat16; down [H,R,P] float32.
+    Returns y_out [Bt,T,H,P] in y's dtype.
+    """
+    import torch
+    lib = load_library()
+    nb, nt, nh, nr, npd = y.shape
+    dev = y.device
+    code = _dtype_code(y)
+    _check(y, "y", y.dtype, (nb, nt, nh, nr, npd), dev)
+    _check(down, "down", torch.float32, (nh, nr, npd), dev)
+    if y_out is None:
+        y_out = torch.empty((nb, nt, nh, npd), dtype=y.dtype, device=dev)
+    _check(y_out, "y_out", y.dtype, (nb, nt, nh, npd), dev)
+    # the state size does not enter the post-pass; any supported value
+    d = _dims(nb, nt, nh, npd, 64, nr)
+    st = lib.m3_block_postpass(ctypes.byref(d), code, _ptr(y), _ptr(down), _ptr(y_out),
+                               _stream(stream))
+    if st != M3_SUCCESS:
+        raise M3Error(st, "m3_block_postpass")
+    return y_out

@@ -54,6 +54,19 @@ struct DecodeArgs {
   void* y;
 };
 
+// Block-side passes (BCNorm + bias, MIMO projections).
+struct BlockArgs {
+  size_t rows;  // batch * seqlen * H token-head rows
+  int H, P, N, R;
+  float eps;
+  const void *x, *B, *C;                                     // pre-pass inputs
+  const float *norm_B, *norm_C, *bias_B, *bias_C, *up;      // pre-pass weights
+  void *x_out, *B_out, *C_out;                               // pre-pass outputs
+  const void* y;                                             // post-pass input
+  const float* down;                                         // post-pass weights
+  void* y_out;                                               // post-pass output
+};
+
 __host__ __device__ inline uint32_t align_up_u32(uint32_t v, uint32_t a) {
   return (v + a - 1) / a * a;
 }
@@ -171,6 +184,8 @@ __host__ __device__ inline bool prefill_shape_fits(int L, int R, int N, int P, i
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, m3_dtype dtype, hipStream_t stream);
+hipError_t launch_block_prepass(const BlockArgs& a, m3_dtype dtype, hipStream_t stream);
+hipError_t launch_block_postpass(const BlockArgs& a, m3_dtype dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, m3_dtype dtype, hipStream_t stream);
 
 // Per-type (and, for bfloat16, per-rank) prefill launchers, one translation

@@ -246,3 +246,86 @@ m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in,
 }
 
 }  // extern "C"
+
+// ---- block-side passes ------------------------------------------------------
+
+namespace {
+
+m3_status check_block_dims(const m3_dims* d, m3_dtype dtype) {
+  if (!d) return M3_ERR_INVALID_VALUE;
+  if (dtype != M3_F32 && dtype != M3_BF16) return M3_ERR_INVALID_VALUE;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->headdim_p < 1 || d->dstate_n < 1 ||
+      d->rank_r < 1)
+    return M3_ERR_INVALID_VALUE;
+  if (!valid_p(d->headdim_p) || !valid_r(d->rank_r)) return M3_ERR_NOT_SUPPORTED;
+  // a B / C row must be a power-of-two number of 16-byte vectors
+  const int64_t n = d->dstate_n;
+  if (n != 16 && n != 32 && n != 64 && n != 128 && n != 256) return M3_ERR_NOT_SUPPORTED;
+  if (d->batch > INT32_MAX || d->seqlen > INT32_MAX || d->nheads > INT32_MAX ||
+      (double)d->batch * (double)d->seqlen * (double)d->nheads * (double)d->rank_r * 256.0 >
+          9.0e15)
+    return M3_ERR_NOT_SUPPORTED;
+  return M3_SUCCESS;
+}
+
+m3::BlockArgs block_args(const m3_dims* d) {
+  m3::BlockArgs a = {};
+  a.rows = (size_t)d->batch * (size_t)d->seqlen * (size_t)d->nheads;
+  a.H = (int)d->nheads;
+  a.P = (int)d->headdim_p;
+  a.N = (int)d->dstate_n;
+  a.R = (int)d->rank_r;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_block_prepass(const m3_dims* dims, m3_dtype dtype, const void* x, const void* B,
+                           const void* C, const float* norm_B, const float* norm_C,
+                           const float* bias_B, const float* bias_C, const float* up, float eps,
+                           void* x_out, void* B_out, void* C_out, void* stream) {
+  const m3_status st = check_block_dims(dims, dtype);
+  if (st != M3_SUCCESS) return st;
+  if (!(eps >= 0.f) || !(eps < 3.0e38f)) return M3_ERR_INVALID_VALUE;  // also rejects NaN
+  m3::BlockArgs a = block_args(dims);
+  if (a.rows == 0) return M3_SUCCESS;
+  const void* vec[] = {x, B, C, x_out, B_out, C_out};
+  for (const void* p : vec)
+    if (!p || !aligned(p, 16)) return M3_ERR_INVALID_VALUE;
+  const float* wts[] = {norm_B, norm_C, bias_B, bias_C, up};
+  for (const float* p : wts)
+    if (!p || !aligned(p, 4)) return M3_ERR_INVALID_VALUE;
+  a.eps = eps;
+  a.x = x;
+  a.B = B;
+  a.C = C;
+  a.norm_B = norm_B;
+  a.norm_C = norm_C;
+  a.bias_B = bias_B;
+  a.bias_C = bias_C;
+  a.up = up;
+  a.x_out = x_out;
+  a.B_out = B_out;
+  a.C_out = C_out;
+  const hipError_t e = m3::launch_block_prepass(a, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;
+}
+
+m3_status m3_block_postpass(const m3_dims* dims, m3_dtype dtype, const void* y,
+                            const float* down, void* y_out, void* stream) {
+  const m3_status st = check_block_dims(dims, dtype);
+  if (st != M3_SUCCESS) return st;
+  m3::BlockArgs a = block_args(dims);
+  if (a.rows == 0) return M3_SUCCESS;
+  if (!y || !y_out || !aligned(y, 16) || !aligned(y_out, 16)) return M3_ERR_INVALID_VALUE;
+  if (!down || !aligned(down, 4)) return M3_ERR_INVALID_VALUE;
+  a.y = y;
+  a.down = down;
+  a.y_out = y_out;
+  const hipError_t e = m3::launch_block_postpass(a, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;
+}
+
+}  // extern "C"

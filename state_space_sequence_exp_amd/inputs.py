@@ -175,3 +175,31 @@ def decode_config_inputs(seed: Optional[int] = None, batch: Optional[int] = None
                          N=cfg.N, P=cfg.P, R=cfg.R, dtype=cfg.dtype,
                          ring=cfg.ring if ring is None else ring,
                          seed=4 if seed is None else seed)
+
+
+def block_inputs(batch: int, seqlen: int, nheads: int, N: int, P: int, R: int, dtype: str,
+                 seed: int) -> Dict[str, np.ndarray]:
+    """Synthetic inputs and random weights of the block-side passes.
+
+    Projection outputs before BCNorm: x ~ N(0,1) [B,T,H,P]; B, C ~ N(0,1)
+    [B,T,H,R,N] (the raw projections, whose scale BCNorm removes).  Weights
+    (float32, random -- no trained weights exist here): norm_B, norm_C ~
+    U(0.5, 1.5) [H,N]; bias_B, bias_C ~ N(0, 0.1^2) [H,R,N]; up, down ~
+    N(0, 1/R) [H,R,P].  Drawn in that order; x, B, C rounded to the storage
+    dtype (returned as stored float32 values plus *_raw storage arrays).
+    """
+    rng = np.random.default_rng(seed)
+    x32 = rng.standard_normal((batch, seqlen, nheads, P), dtype=np.float32)
+    B32 = rng.standard_normal((batch, seqlen, nheads, R, N), dtype=np.float32)
+    C32 = rng.standard_normal((batch, seqlen, nheads, R, N), dtype=np.float32)
+    norm_B = rng.uniform(0.5, 1.5, size=(nheads, N)).astype(np.float32)
+    norm_C = rng.uniform(0.5, 1.5, size=(nheads, N)).astype(np.float32)
+    bias_B = (0.1 * rng.standard_normal((nheads, R, N))).astype(np.float32)
+    bias_C = (0.1 * rng.standard_normal((nheads, R, N))).astype(np.float32)
+    up = (rng.standard_normal((nheads, R, P)) / np.sqrt(R)).astype(np.float32)
+    down = (rng.standard_normal((nheads, R, P)) / np.sqrt(R)).astype(np.float32)
+    x, x_raw = _store(x32, dtype)
+    Bv, B_raw = _store(B32, dtype)
+    Cv, C_raw = _store(C32, dtype)
+    return dict(x=x, B=Bv, C=Cv, x_raw=x_raw, B_raw=B_raw, C_raw=C_raw, norm_B=norm_B,
+                norm_C=norm_C, bias_B=bias_B, bias_C=bias_C, up=up, down=down, dtype=dtype)

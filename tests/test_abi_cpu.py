@@ -226,3 +226,41 @@ def test_prefill_lds_limit(lib):
                           fake, fake, None, fake, 1 << 40, None) == m3.M3_ERR_NOT_SUPPORTED
     assert ws(d, 128, m3.M3_F32) == 0
     assert ws(d, 64, m3.M3_F32) > 0
+
+
+def test_block_pass_validation(lib):
+    """Host-side checks of the block-side passes (nothing is launched)."""
+    ok = ctypes.c_void_p(0x100000)
+    mis16 = ctypes.c_void_p(0x100008)   # 8-byte aligned, not 16
+    mis4 = ctypes.c_void_p(0x100002)
+
+    def pre(d, ptrs=None, eps=1e-6, dtype=m3.M3_BF16):
+        p = ptrs or [ok] * 11   # x B C nB nC bB bC up x_out B_out C_out
+        return lib.m3_block_prepass(ctypes.byref(d), dtype, *p[:8], ctypes.c_float(eps), *p[8:],
+                                    None)
+
+    d = dims(b=2, t=8, h=2, p=64, n=64, r=2)
+    assert pre(dims(n=48)) == m3.M3_ERR_NOT_SUPPORTED      # rows must be 2^k vectors
+    assert pre(dims(n=512)) == m3.M3_ERR_NOT_SUPPORTED
+    assert pre(dims(p=24)) == m3.M3_ERR_NOT_SUPPORTED
+    assert pre(dims(r=3)) == m3.M3_ERR_NOT_SUPPORTED
+    assert pre(d, dtype=9) == m3.M3_ERR_INVALID_VALUE
+    assert pre(d, eps=-1.0) == m3.M3_ERR_INVALID_VALUE
+    assert pre(d, eps=float("nan")) == m3.M3_ERR_INVALID_VALUE
+    assert pre(dims(b=0)) == m3.M3_SUCCESS
+    assert pre(dims(t=0)) == m3.M3_SUCCESS
+    for i in range(11):
+        p = [ok] * 11
+        p[i] = None
+        assert pre(d, p) == m3.M3_ERR_INVALID_VALUE
+        p[i] = mis16 if i in (0, 1, 2, 8, 9, 10) else mis4
+        assert pre(d, p) == m3.M3_ERR_INVALID_VALUE
+
+    def post(d, y=ok, down=ok, out=ok):
+        return lib.m3_block_postpass(ctypes.byref(d), m3.M3_F32, y, down, out, None)
+    assert post(dims(b=0)) == m3.M3_SUCCESS
+    assert post(d, y=None) == m3.M3_ERR_INVALID_VALUE
+    assert post(d, y=mis16) == m3.M3_ERR_INVALID_VALUE
+    assert post(d, down=mis4) == m3.M3_ERR_INVALID_VALUE
+    assert post(d, out=None) == m3.M3_ERR_INVALID_VALUE
+    assert post(dims(r=3)) == m3.M3_ERR_NOT_SUPPORTED
