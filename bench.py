@@ -94,6 +94,15 @@ def decode_bytes(cfg) -> int:
     return cfg.batch * cfg.nheads * per + cfg.nheads * 4
 
 
+def flush_mall(scratch):
+    """Evict the last-level cache (MALL, 256 MB) before a cold timed call:
+    write a 512 MB scratch buffer, then read it back, so the cache holds only
+    clean scratch lines -- the dirty lines of the write are written back
+    here, not during the timed call."""
+    scratch.fill_(1.0)
+    scratch.sum()
+
+
 def decode_mode_bytes(S, H, N, P, R, es, trap, rot) -> int:
     """Algorithmic bytes of one decode step: the state read and written, the
     token's inputs (the previous token's x and B and lam only for the
@@ -112,7 +121,7 @@ SWEEP = [("mamba2", 1, False, False), ("mamba3_siso", 1, True, True),
 
 def decode_sweep(steps, log):
     """Per-step decode latency for each sweep point: 'cold' steps each
-    preceded by a 512 MB scratch write (the state comes from HBM, as in a
+    preceded by a MALL flush (the state comes from HBM, as in a
     model whose other layers evict it) and back-to-back steps."""
     import numpy as np
     import torch
@@ -144,7 +153,7 @@ def decode_sweep(steps, log):
                 evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                        for _ in range(steps)]
                 for t, (s0, e0) in enumerate(evs):
-                    scratch.fill_(1.0)
+                    flush_mall(scratch)
                     s0.record()
                     step(t)
                     e0.record()
@@ -170,6 +179,64 @@ def decode_sweep(steps, log):
     return rows
 
 
+def block_passes(steps, log):
+    """Block-side passes at the prefill bench shapes (batch 4, 16 heads,
+    N = P = 64, bf16; T 2048 with R = 1 and T 4096 with R = 4): per-call
+    time (last-level cache evicted before each call) and HBM bandwidth of
+    the algorithmic bytes -- every input read once, every output written once,
+    weights included."""
+    import numpy as np
+    import torch
+    import state_space_sequence_exp_amd as m3
+    from state_space_sequence_exp_amd import inputs as I
+    scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+    out = {}
+    for T, R in ((2048, 1), (4096, 4)):
+        nb, H, N, P, es = 4, 16, 64, 64, 2
+        inp = I.block_inputs(nb, T, H, N, P, R, "bf16", seed=140 + R)
+        g = upload(dict(x_raw=inp["x_raw"], B_raw=inp["B_raw"], C_raw=inp["C_raw"],
+                        dtype="bf16"))
+        w = {k: torch.from_numpy(inp[k]).to("cuda:0")
+             for k in ("norm_B", "norm_C", "bias_B", "bias_C", "up", "down")}
+        del inp
+        X = torch.empty((nb, T, H, R, P), dtype=torch.bfloat16, device="cuda:0")
+        Bo, Co = torch.empty_like(g["B"]), torch.empty_like(g["C"])
+        yo = torch.empty((nb, T, H, P), dtype=torch.bfloat16, device="cuda:0")
+
+        def pre():
+            m3.block_prepass(g["x"], g["B"], g["C"], w["norm_B"], w["norm_C"], w["bias_B"],
+                             w["bias_C"], w["up"], 1e-6, x_out=X, B_out=Bo, C_out=Co)
+
+        def post():
+            m3.block_postpass(X, w["down"], y_out=yo)
+
+        rows = nb * T * H
+        weights = (2 * H * N + 2 * H * R * N + H * R * P) * 4
+        nbytes = {"prepass": rows * (P + 4 * R * N + R * P) * es + weights,
+                  "postpass": rows * (R * P + P) * es + H * R * P * 4}
+        for name, fn in (("prepass", pre), ("postpass", post)):
+            fn()
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+            for s0, e0 in evs:
+                flush_mall(scratch)
+                s0.record()
+                fn()
+                e0.record()
+            torch.cuda.synchronize()
+            us = float(np.median([s0.elapsed_time(e0) for s0, e0 in evs])) * 1e3
+            gbs = nbytes[name] / (us * 1e-6) / 1e9
+            out["%s_b4_t%d_h16_n64_p64_r%d" % (name, T, R)] = {
+                "us": us, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                "algorithmic_bytes": nbytes[name]}
+            log("block %s T=%d R=%d: %.1f us, %.0f GB/s" % (name, T, R, us, gbs))
+        del g, w, X, Bo, Co, yo
+        torch.cuda.empty_cache()
+    del scratch
+    return out
+
+
 def upload(inp):
     import numpy as np
     import torch
@@ -182,7 +249,8 @@ def upload(inp):
 
     g = {k: st(inp[k + "_raw"]) for k in ("x", "B", "C")}
     for k in ("dt", "lam", "theta", "A"):
-        g[k] = torch.from_numpy(np.ascontiguousarray(inp[k], dtype=np.float32)).to(dev)
+        if k in inp:
+            g[k] = torch.from_numpy(np.ascontiguousarray(inp[k], dtype=np.float32)).to(dev)
     if "h0" in inp:
         g["h0"] = torch.from_numpy(np.ascontiguousarray(inp["h0"], dtype=np.float32)).to(dev)
     return g
@@ -190,7 +258,7 @@ def upload(inp):
 
 def time_prefill(cfg, g, steps, warmup, flush=True):
     """Per-call durations (ms) of m3_prefill with HIP events on the current
-    stream; a 512 MB scratch fill between calls evicts the MALL."""
+    stream; a MALL flush (flush_mall) before each call."""
     import torch
     import state_space_sequence_exp_amd as m3
     dev = torch.device("cuda:0")
@@ -213,7 +281,7 @@ def time_prefill(cfg, g, steps, warmup, flush=True):
            for _ in range(steps)]
     for s, e in evs:
         if flush:
-            scratch.fill_(1.0)
+            flush_mall(scratch)
         s.record()
         call()
         e.record()
@@ -331,6 +399,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not evict the MALL between steps")
     ap.add_argument("--no-decode-sweep", action="store_true")
+    ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="short untimed sequence for rocprofv3 counter runs: SISO prefill x3, "
                          "long SISO prefill x1, 10 decode steps, and a 512 MiB device copy x3 "
@@ -436,6 +505,8 @@ def main():
                                     "algorithmic_bytes": nb}}
         if not args.no_decode_sweep:
             sec["decode_sweep_b128_h64_p64"] = decode_sweep(20, log)
+        if not args.no_block:
+            sec["block_passes"] = block_passes(20, log)
         line["secondary"] = sec
     print(json.dumps(line))
 

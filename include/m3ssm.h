@@ -238,8 +238,9 @@ m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in,
  *   norm_B, norm_C        [H, N]      float
  *   bias_B, bias_C        [H, R, N]   float
  *   up, down              [H, R, P]   float
- * N must be 16, 32, 64, 128 or 256; P and R as for m3_prefill.  x, B, C,
- * X, B~, C~, y and y_out need 16-byte alignment, the weights 4 bytes.
+ * N must be 16, 32, 64, 128 or 256; P and R as for m3_prefill.  Every
+ * array (x, B, C, X, B~, C~, y, y_out and the weights) needs 16-byte
+ * alignment.
  * B~ may be B and C~ may be C (in place), X may be x when R = 1; other
  * overlaps between inputs and outputs are not allowed.  eps >= 0 (finite).
  * One kernel launch each; batch * seqlen == 0 enqueues nothing.

@@ -294,9 +294,10 @@ m3_status m3_block_prepass(const m3_dims* dims, m3_dtype dtype, const void* x, c
   const void* vec[] = {x, B, C, x_out, B_out, C_out};
   for (const void* p : vec)
     if (!p || !aligned(p, 16)) return M3_ERR_INVALID_VALUE;
+  // weights are read in 16-byte vectors too
   const float* wts[] = {norm_B, norm_C, bias_B, bias_C, up};
   for (const float* p : wts)
-    if (!p || !aligned(p, 4)) return M3_ERR_INVALID_VALUE;
+    if (!p || !aligned(p, 16)) return M3_ERR_INVALID_VALUE;
   a.eps = eps;
   a.x = x;
   a.B = B;
@@ -320,7 +321,7 @@ m3_status m3_block_postpass(const m3_dims* dims, m3_dtype dtype, const void* y,
   m3::BlockArgs a = block_args(dims);
   if (a.rows == 0) return M3_SUCCESS;
   if (!y || !y_out || !aligned(y, 16) || !aligned(y_out, 16)) return M3_ERR_INVALID_VALUE;
-  if (!down || !aligned(down, 4)) return M3_ERR_INVALID_VALUE;
+  if (!down || !aligned(down, 16)) return M3_ERR_INVALID_VALUE;
   a.y = y;
   a.down = down;
   a.y_out = y_out;
