@@ -211,6 +211,39 @@ m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in,
                          const float* lam, const float* theta, void* y_t, void* stream);
 
 /*
+ * Gradients of the recurrence (reverse mode) for training: given the
+ * forward inputs and the gradients dy of y (and optionally dh_final of the
+ * final state), computes the gradients of
+ *
+ *   L = sum_t <y_t, dy_t> + <h_{T-1}, dh_final>
+ *
+ * with respect to every input: dx, dB, dC in the inputs' layouts, ddt,
+ * dlam [batch, T, H], dtheta [batch, T, H, N/2], dA [H], all float32
+ * whatever the storage type.  The recurrence is the one m3_prefill computes
+ * (Mamba-3 paper summary, Proposition 1; explainer, "second improvement";
+ * paper summary, item 3 for the rank R); the pages release training kernels
+ * without describing them, so this is the plain adjoint of that recurrence:
+ * with G_t = dL/dh_t, G_t = C_t dy_t^T + alpha_{t+1} R_{t+1}^T G_{t+1}, and
+ * each token's gradients follow from h_t, h_{t-1} and G_t.
+ *
+ * The forward states h_t and the adjoint states G_t of every token are
+ * materialised in the workspace (m3_backward_workspace_size: 8 N P bytes per
+ * token-head plus 4), so the call moves about 5 x 4 N P bytes per
+ * token-head through HBM.  dy has x's layout and storage type; dh_final,
+ * if given, is [batch, H, N, P] float.  lam and theta are required.  N must
+ * be 16, 32, 64, 128 or 256 with N * P <= 8192; P and R as for m3_prefill.
+ * Pointers need element alignment and the workspace 256 bytes.  With
+ * batch * seqlen == 0 only dA is written (zeros).  Four kernel launches.
+ */
+size_t m3_backward_workspace_size(const m3_dims* dims, m3_dtype dtype);
+
+m3_status m3_backward(const m3_dims* dims, m3_dtype dtype, const void* x, const float* dt,
+                      const float* A, const float* lam, const float* theta, const void* B,
+                      const void* C, const void* dy, const float* dh_final, float* dx,
+                      float* ddt, float* dA, float* dlam, float* dtheta, float* dB, float* dC,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Block-side steps on either side of the SSM (Mamba-3 paper translation,
  * section 3.4 "Mamba-3 architecture"; paper summary, "Steps & Procedures"):
  * BCNorm -- an RMS normalisation after the B and C projections, in the

@@ -10,6 +10,7 @@ current stream):
     decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta) -> (y_t, h)
     block_prepass(x, B, C, norm_B, norm_C, bias_B, bias_C, up, eps) -> (X, B~, C~)
     block_postpass(y, down) -> y_out
+    backward(x, dt, A, lam, theta, B, C, dy[, dh_final]) -> dict of gradients
     prefill_workspace_size(...), version(), status_string(code)
 
 ``inputs`` draws the seeded synthetic workloads.  Build the library with
@@ -17,10 +18,12 @@ current stream):
 """
 from ._binding import (ABI_SYMBOLS, LIB_PATH, M3_BF16, M3_ERR_HIP, M3_ERR_INVALID_VALUE,
                        M3_ERR_NOT_SUPPORTED, M3_ERR_WORKSPACE, M3_F32, M3_SUCCESS, M3Dims,
-                       M3Error, block_postpass, block_prepass, decode_step, load_library,
+                       M3Error, backward, backward_workspace_size, block_postpass,
+                       block_prepass, decode_step, load_library,
                        prefill, prefill_workspace_size, status_string, version)
 
-__all__ = ["prefill", "decode_step", "block_prepass", "block_postpass", "prefill_workspace_size", "version", "status_string",
+__all__ = ["prefill", "decode_step", "block_prepass", "block_postpass", "backward",
+           "backward_workspace_size", "prefill_workspace_size", "version", "status_string",
            "load_library", "M3Error", "M3Dims", "ABI_SYMBOLS", "LIB_PATH", "M3_SUCCESS",
            "M3_ERR_INVALID_VALUE", "M3_ERR_NOT_SUPPORTED", "M3_ERR_WORKSPACE", "M3_ERR_HIP",
            "M3_F32", "M3_BF16"]

@@ -24,7 +24,8 @@ M3_BF16 = 1
 
 # every function declared in include/m3ssm.h
 ABI_SYMBOLS = ("m3_version", "m3_status_string", "m3_prefill_workspace_size", "m3_prefill",
-               "m3_prefill_from_state", "m3_decode_step", "m3_block_prepass", "m3_block_postpass")
+               "m3_prefill_from_state", "m3_decode_step", "m3_block_prepass", "m3_block_postpass",
+               "m3_backward_workspace_size", "m3_backward")
 
 
 class M3Error(RuntimeError):
@@ -69,6 +70,10 @@ def load_library(path: Optional[str] = None):
     lib.m3_decode_step.restype = ctypes.c_int
     lib.m3_decode_step.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    vp, vp]
+    lib.m3_backward_workspace_size.restype = ctypes.c_size_t
+    lib.m3_backward_workspace_size.argtypes = [dp, ctypes.c_int]
+    lib.m3_backward.restype = ctypes.c_int
+    lib.m3_backward.argtypes = [dp, ctypes.c_int] + [vp] * 17 + [ctypes.c_size_t, vp]
     lib.m3_block_prepass.restype = ctypes.c_int
     lib.m3_block_prepass.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp,
                                      ctypes.c_float, vp, vp, vp, vp]
@@ -319,3 +324,58 @@ def block_postpass(y, down, *, y_out=None, stream=None):
     if st != M3_SUCCESS:
         raise M3Error(st, "m3_block_postpass")
     return y_out
+
+
+def backward_workspace_size(batch, seqlen, nheads, P, N, R, dtype) -> int:
+    """Bytes of workspace m3_backward needs (0: nothing to do, or unsupported)."""
+    import torch
+    code = dtype if isinstance(dtype, int) else (M3_BF16 if dtype == torch.bfloat16 else M3_F32)
+    d = _dims(batch, seqlen, nheads, P, N, R)
+    return int(load_library().m3_backward_workspace_size(ctypes.byref(d), code))
+
+
+def backward(x, dt, A, lam, theta, B, C, dy, *, dh_final=None, workspace=None, stream=None):
+    """Gradients of sum(y * dy) (+ sum(h_final * dh_final)) for the prefill
+    inputs (m3_backward).  Shapes as for prefill; dy has x's shape and dtype.
+    Returns a dict of float32 gradients: x, dt, A, lam, theta, B, C."""
+    import torch
+    lib = load_library()
+    squeeze = x.dim() == 4
+    x5 = x.unsqueeze(3) if squeeze else x
+    B5 = B.unsqueeze(3) if B.dim() == 4 else B
+    C5 = C.unsqueeze(3) if C.dim() == 4 else C
+    dy5 = dy.unsqueeze(3) if dy.dim() == 4 else dy
+    nb, nt, nh, nr, npd = x5.shape
+    nn = B5.shape[-1]
+    dev = x.device
+    code = _dtype_code(x)
+    _check(x5, "x", x.dtype, (nb, nt, nh, nr, npd), dev)
+    _check(dy5, "dy", x.dtype, (nb, nt, nh, nr, npd), dev)
+    _check(B5, "B", x.dtype, (nb, nt, nh, nr, nn), dev)
+    _check(C5, "C", x.dtype, (nb, nt, nh, nr, nn), dev)
+    _check(dt, "dt", torch.float32, (nb, nt, nh), dev)
+    _check(lam, "lam", torch.float32, (nb, nt, nh), dev)
+    _check(theta, "theta", torch.float32, (nb, nt, nh, nn // 2), dev)
+    _check(A, "A", torch.float32, (nh,), dev)
+    if dh_final is not None:
+        _check(dh_final, "dh_final", torch.float32, (nb, nh, nn, npd), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"x": torch.empty((nb, nt, nh, nr, npd), **f32), "dt": torch.empty((nb, nt, nh), **f32),
+         "A": torch.empty((nh,), **f32), "lam": torch.empty((nb, nt, nh), **f32),
+         "theta": torch.empty((nb, nt, nh, nn // 2), **f32),
+         "B": torch.empty((nb, nt, nh, nr, nn), **f32), "C": torch.empty((nb, nt, nh, nr, nn), **f32)}
+    d = _dims(nb, nt, nh, npd, nn, nr)
+    need = int(lib.m3_backward_workspace_size(ctypes.byref(d), code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.m3_backward(ctypes.byref(d), code, _ptr(x5), _ptr(dt), _ptr(A), _ptr(lam),
+                         _ptr(theta), _ptr(B5), _ptr(C5), _ptr(dy5), _ptr(dh_final),
+                         _ptr(g["x"]), _ptr(g["dt"]), _ptr(g["A"]), _ptr(g["lam"]),
+                         _ptr(g["theta"]), _ptr(g["B"]), _ptr(g["C"]), _ptr(workspace),
+                         ws_bytes, _stream(stream))
+    if st != M3_SUCCESS:
+        raise M3Error(st, "m3_backward")
+    if squeeze:
+        g["x"] = g["x"].squeeze(3)
+    return g

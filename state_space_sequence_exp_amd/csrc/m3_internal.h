@@ -54,6 +54,15 @@ struct DecodeArgs {
   void* y;
 };
 
+// Gradients of the recurrence (backward.hip).
+struct BackwardArgs {
+  int nb, T, H, P, N, R;
+  const void *x, *B, *C, *dy;                       // storage type of the call
+  const float *dt, *A, *lam, *theta, *dh_final;     // dh_final may be null
+  float *dx, *ddt, *dA, *dlam, *dtheta, *dB, *dC;   // gradients, float
+  float *hs, *gs, *dAc;                             // workspace: h_t, G_t, dA terms
+};
+
 // Block-side passes (BCNorm + bias, MIMO projections).
 struct BlockArgs {
   size_t rows;  // batch * seqlen * H token-head rows
@@ -185,6 +194,7 @@ __host__ __device__ inline bool prefill_shape_fits(int L, int R, int N, int P, i
 
 hipError_t launch_prefill(const PrefillArgs& a, m3_dtype dtype, hipStream_t stream);
 hipError_t launch_block_prepass(const BlockArgs& a, m3_dtype dtype, hipStream_t stream);
+hipError_t launch_backward(const BackwardArgs& a, m3_dtype dtype, hipStream_t stream);
 hipError_t launch_block_postpass(const BlockArgs& a, m3_dtype dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, m3_dtype dtype, hipStream_t stream);
 

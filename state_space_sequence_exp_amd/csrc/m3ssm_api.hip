@@ -330,3 +330,109 @@ m3_status m3_block_postpass(const m3_dims* dims, m3_dtype dtype, const void* y,
 }
 
 }  // extern "C"
+
+// ---- gradients ----------------------------------------------------------------
+
+namespace {
+
+m3_status check_backward_dims(const m3_dims* d, m3_dtype dtype) {
+  if (!d) return M3_ERR_INVALID_VALUE;
+  if (dtype != M3_F32 && dtype != M3_BF16) return M3_ERR_INVALID_VALUE;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->headdim_p < 1 || d->dstate_n < 2 ||
+      d->rank_r < 1 || (d->dstate_n % 2) != 0)
+    return M3_ERR_INVALID_VALUE;
+  if (!valid_p(d->headdim_p) || !valid_r(d->rank_r)) return M3_ERR_NOT_SUPPORTED;
+  // a power-of-two state size with N * P <= 8192: one workgroup of
+  // (N/2) (P/8) <= 512 threads per token-head
+  const int64_t n = d->dstate_n;
+  if ((n != 16 && n != 32 && n != 64 && n != 128 && n != 256) || n * d->headdim_p > 8192)
+    return M3_ERR_NOT_SUPPORTED;
+  if (d->batch > INT32_MAX || d->seqlen > INT32_MAX || d->nheads > INT32_MAX ||
+      (double)d->batch * (double)d->seqlen * (double)d->nheads > 2.0e9)
+    return M3_ERR_NOT_SUPPORTED;
+  return M3_SUCCESS;
+}
+
+struct BwCarve {
+  size_t off_gs, off_dAc, total;
+};
+
+BwCarve bw_carve(const m3_dims* d) {
+  BwCarve w;
+  const size_t states = (size_t)d->batch * d->nheads * d->seqlen * d->dstate_n * d->headdim_p;
+  w.off_gs = round256(states * sizeof(float));
+  w.off_dAc = w.off_gs + round256(states * sizeof(float));
+  w.total = w.off_dAc + round256((size_t)d->batch * d->seqlen * d->nheads * sizeof(float));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t m3_backward_workspace_size(const m3_dims* dims, m3_dtype dtype) {
+  if (check_backward_dims(dims, dtype) != M3_SUCCESS) return 0;
+  if (dims->batch == 0 || dims->seqlen == 0) return 0;
+  return bw_carve(dims).total;
+}
+
+m3_status m3_backward(const m3_dims* dims, m3_dtype dtype, const void* x, const float* dt,
+                      const float* A, const float* lam, const float* theta, const void* B,
+                      const void* C, const void* dy, const float* dh_final, float* dx,
+                      float* ddt, float* dA, float* dlam, float* dtheta, float* dB, float* dC,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const m3_status st = check_backward_dims(dims, dtype);
+  if (st != M3_SUCCESS) return st;
+  const uintptr_t es = esize_of(dtype);
+  if (!dA || !aligned(dA, 4)) return M3_ERR_INVALID_VALUE;
+  // with no tokens only dA is written (the other arrays may be empty)
+  if (dims->batch > 0 && dims->seqlen > 0) {
+    const void* in_t[] = {x, B, C, dy};
+    const void* f32[] = {dt, A, lam, theta, dx, ddt, dlam, dtheta, dB, dC};
+    for (const void* p : in_t)
+      if (!p || !aligned(p, es)) return M3_ERR_INVALID_VALUE;
+    for (const void* p : f32)
+      if (!p || !aligned(p, 4)) return M3_ERR_INVALID_VALUE;
+    if (dh_final && !aligned(dh_final, 4)) return M3_ERR_INVALID_VALUE;
+  }
+  m3::BackwardArgs a = {};
+  a.nb = (int)dims->batch;
+  a.T = (int)dims->seqlen;
+  a.H = (int)dims->nheads;
+  a.P = (int)dims->headdim_p;
+  a.N = (int)dims->dstate_n;
+  a.R = (int)dims->rank_r;
+  a.dA = dA;
+  if (a.nb == 0 || a.T == 0) {
+    // no tokens: the per-token gradients are empty and dA sums nothing
+    const hipError_t e = m3::launch_backward(a, dtype, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;
+  }
+  const BwCarve w = bw_carve(dims);
+  if (!workspace || workspace_bytes < w.total) return M3_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return M3_ERR_INVALID_VALUE;
+  a.x = x;
+  a.B = B;
+  a.C = C;
+  a.dy = dy;
+  a.dt = dt;
+  a.A = A;
+  a.lam = lam;
+  a.theta = theta;
+  a.dh_final = dh_final;
+  a.dx = dx;
+  a.ddt = ddt;
+  a.dA = dA;
+  a.dlam = dlam;
+  a.dtheta = dtheta;
+  a.dB = dB;
+  a.dC = dC;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.hs = reinterpret_cast<float*>(ws);
+  a.gs = reinterpret_cast<float*>(ws + w.off_gs);
+  a.dAc = reinterpret_cast<float*>(ws + w.off_dAc);
+  const hipError_t e = m3::launch_backward(a, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;
+}
+
+}  // extern "C"

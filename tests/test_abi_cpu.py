@@ -264,3 +264,31 @@ def test_block_pass_validation(lib):
     assert post(d, down=mis4) == m3.M3_ERR_INVALID_VALUE
     assert post(d, out=None) == m3.M3_ERR_INVALID_VALUE
     assert post(dims(r=3)) == m3.M3_ERR_NOT_SUPPORTED
+
+
+def test_backward_validation(lib):
+    """Host-side checks of m3_backward (nothing is launched)."""
+    ok = ctypes.c_void_p(0x100000)
+    mis = ctypes.c_void_p(0x100001)
+
+    def call(d, ptrs=None, dtype=m3.M3_F32, ws=ok, wsb=1 << 40):
+        p = ptrs or [ok] * 16  # x dt A lam theta B C dy dh dx ddt dA dlam dtheta dB dC
+        return lib.m3_backward(ctypes.byref(d), dtype, *p, ws, wsb, None)
+
+    d = dims(b=2, t=16, h=2, p=64, n=64, r=2)
+    assert call(dims(n=48)) == m3.M3_ERR_NOT_SUPPORTED     # power-of-two state size
+    assert call(dims(n=256, p=64)) == m3.M3_ERR_NOT_SUPPORTED  # N * P > 8192
+    assert call(dims(r=3)) == m3.M3_ERR_NOT_SUPPORTED
+    assert call(d, dtype=7) == m3.M3_ERR_INVALID_VALUE
+    for i in range(16):
+        p = [ok] * 16
+        if i != 8:  # dh_final is optional
+            p[i] = None
+            assert call(d, p) == m3.M3_ERR_INVALID_VALUE
+        p[i] = mis
+        assert call(d, p) == m3.M3_ERR_INVALID_VALUE
+    assert call(d, ws=None) == m3.M3_ERR_WORKSPACE
+    need = lib.m3_backward_workspace_size(ctypes.byref(d), m3.M3_F32)
+    assert need == 2 * 2 * 2 * 16 * 64 * 64 * 4 + 256  # h_t and G_t of every token-head, dA terms
+    assert call(d, wsb=need - 1) == m3.M3_ERR_WORKSPACE
+    assert lib.m3_backward_workspace_size(ctypes.byref(dims(b=0)), m3.M3_F32) == 0

@@ -2,9 +2,9 @@
 
 The PyTorch forward is checked against the independent C oracle, and its
 reverse-mode gradients against central finite differences of the C oracle
-along random directions (second-order accurate: the error at step 1e-5 is
-far below the tolerance), so neither the forward written out here nor the
-differentiation is trusted on its own."""
+along random directions (central differences are second-order accurate:
+at the step used their error is far below the tolerance), so neither the
+forward written out here nor the differentiation is trusted on its own."""
 import numpy as np
 import pytest
 
