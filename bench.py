@@ -237,6 +237,56 @@ def block_passes(steps, log):
     return out
 
 
+def backward_bench(steps, log):
+    """m3_backward at the SISO prefill bench shape (batch 4, T 2048, 16 heads,
+    N = P = 64, bf16 inputs, float32 gradients): cold per-call time (MALL
+    flushed before each call).  Algorithmic bytes: every input and dy read
+    once, every gradient written once; the states the implementation writes
+    and reads back (h_t and G_t of every token) are reported separately."""
+    import numpy as np
+    import torch
+    import state_space_sequence_exp_amd as m3
+    from state_space_sequence_exp_amd import inputs as I
+    cfg = I.CONFIGS[1]
+    inp = I.config_inputs(1)
+    g = upload(inp)
+    del inp
+    dy = torch.randn(g["x"].shape, device="cuda:0").to(g["x"].dtype)
+    ws = torch.empty(m3.backward_workspace_size(cfg.batch, cfg.seqlen, cfg.nheads, cfg.P, cfg.N,
+                                                cfg.R, g["x"].dtype),
+                     dtype=torch.uint8, device="cuda:0")
+    scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+
+    def call():
+        return m3.backward(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"], dy,
+                           workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for s0, e0 in evs:
+        flush_mall(scratch)
+        s0.record()
+        call()
+        e0.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([s0.elapsed_time(e0) for s0, e0 in evs]))
+    th = cfg.batch * cfg.seqlen * cfg.nheads
+    es, R, N, P = 2, cfg.R, cfg.N, cfg.P
+    nbytes = (th * (2 * R * P * es + 2 * R * N * es + 8 + (N // 2) * 4)      # x, dy, B, C, dt, lam, theta
+              + th * (R * P * 4 + 2 * R * N * 4 + 8 + (N // 2) * 4)        # dx, dB, dC, ddt, dlam, dtheta
+              + cfg.nheads * 8)                                            # A, dA
+    state_bytes = th * N * P * 4 * 5   # h_t, G_t written once; h_t, h_{t-1}, G_t read once
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log("backward: %.3f ms, %.0f GB/s algorithmic" % (ms, gbs))
+    del g, dy, ws, scratch
+    torch.cuda.empty_cache()
+    return {"ms": ms, "tokens_per_s": cfg.batch * cfg.seqlen / (ms * 1e-3), "hbm_gbs": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+            "materialised_state_bytes": state_bytes,
+            "state_traffic_gbs": state_bytes / (ms * 1e-3) / 1e9}
+
+
 def upload(inp):
     import numpy as np
     import torch
@@ -400,6 +450,7 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="do not evict the MALL between steps")
     ap.add_argument("--no-decode-sweep", action="store_true")
     ap.add_argument("--no-block", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="short untimed sequence for rocprofv3 counter runs: SISO prefill x3, "
                          "long SISO prefill x1, 10 decode steps, and a 512 MiB device copy x3 "
@@ -507,6 +558,8 @@ def main():
             sec["decode_sweep_b128_h64_p64"] = decode_sweep(20, log)
         if not args.no_block:
             sec["block_passes"] = block_passes(20, log)
+        if not args.no_backward:
+            sec["backward_siso_b4_t2048_h16_n64_p64"] = backward_bench(10, log)
         line["secondary"] = sec
     print(json.dumps(line))
 

@@ -232,8 +232,9 @@ m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in,
  * token-head through HBM.  dy has x's layout and storage type; dh_final,
  * if given, is [batch, H, N, P] float.  lam and theta are required.  N must
  * be 16, 32, 64, 128 or 256 with N * P <= 8192; P and R as for m3_prefill.
- * Pointers need element alignment and the workspace 256 bytes.  With
- * batch * seqlen == 0 only dA is written (zeros).  Four kernel launches.
+ * x and dy need 16-byte alignment, the other pointers element alignment
+ * and the workspace 256 bytes.  With batch * seqlen == 0 only dA is written
+ * (zeros).  Four kernel launches.
  */
 size_t m3_backward_workspace_size(const m3_dims* dims, m3_dtype dtype);
 

@@ -350,6 +350,14 @@ m3_status check_backward_dims(const m3_dims* d, m3_dtype dtype) {
   if (d->batch > INT32_MAX || d->seqlen > INT32_MAX || d->nheads > INT32_MAX ||
       (double)d->batch * (double)d->seqlen * (double)d->nheads > 2.0e9)
     return M3_ERR_NOT_SUPPORTED;
+  // the time loops address one sequence's tokens with 32-bit buffer offsets
+  const double es = dtype == M3_BF16 ? 2.0 : 4.0;
+  const double row = (double)d->nheads * d->rank_r * (d->dstate_n > d->headdim_p ? d->dstate_n
+                                                                                 : d->headdim_p);
+  if ((double)d->seqlen * row * es >= 2147483648.0 ||
+      (double)d->seqlen * d->nheads * (d->dstate_n / 2) * 4.0 >= 2147483648.0 ||
+      (double)d->seqlen * d->dstate_n * d->headdim_p * 4.0 >= 2147483648.0)
+    return M3_ERR_NOT_SUPPORTED;
   return M3_SUCCESS;
 }
 
@@ -387,7 +395,9 @@ m3_status m3_backward(const m3_dims* dims, m3_dtype dtype, const void* x, const 
   if (!dA || !aligned(dA, 4)) return M3_ERR_INVALID_VALUE;
   // with no tokens only dA is written (the other arrays may be empty)
   if (dims->batch > 0 && dims->seqlen > 0) {
-    const void* in_t[] = {x, B, C, dy};
+    // x and dy are read in 16-byte vectors
+    if (!x || !dy || !aligned(x, 16) || !aligned(dy, 16)) return M3_ERR_INVALID_VALUE;
+    const void* in_t[] = {B, C};
     const void* f32[] = {dt, A, lam, theta, dx, ddt, dlam, dtheta, dB, dC};
     for (const void* p : in_t)
       if (!p || !aligned(p, es)) return M3_ERR_INVALID_VALUE;
