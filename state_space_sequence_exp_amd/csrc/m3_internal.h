@@ -82,8 +82,14 @@ __host__ __device__ inline uint32_t align_up_u32(uint32_t v, uint32_t a) {
 
 // Tokens per rotation item: one thread rotates one pair of B (and C) rows
 // over this many consecutive tokens (and all R ranks of each token).
-__host__ __device__ constexpr int prefill_item_tokens(int esize, int R) {
-  return (kPrefillThreads == 512 ? 2 : 1) * (esize == 2 ? (R == 1 ? 4 : 2) : (R == 4 ? 1 : 4 / R));
+__host__ __device__ constexpr int prefill_item_tokens(int esize, int R, int N = 0, int P = 0) {
+  // the instantiation with N = 64 (and P <= 64) fixed, R = 1 and bfloat16 takes
+  // chunks of at most 64 tokens: 32 pairs x 16 blocks of 4 tokens give every
+  // one of 512 threads a rotation item and an x item
+  return (kPrefillThreads == 512 && esize == 2 && R == 1 && N == 64 && P != 0 && P <= 64)
+             ? 4
+             : (kPrefillThreads == 512 ? 2 : 1) *
+                   (esize == 2 ? (R == 1 ? 4 : 2) : (R == 4 ? 1 : 4 / R));
 }
 
 // Per-token scalars of one chunk, one of two alternating buffers:
@@ -132,7 +138,7 @@ __host__ __device__ inline PrefillLayout prefill_layout(int L, int R, int N, int
   c.LR = L * R;
   c.LRp = esize == 2 ? (c.LR + 31) / 32 * 32 : c.LR;
   c.KM = fixed ? 64 * R : c.LRp;
-  c.S = prefill_item_tokens(esize, R);
+  c.S = fixed ? prefill_item_tokens(esize, R, N, P) : prefill_item_tokens(esize, R);
   c.npair = N / 2;
   c.nblk = L / c.S;
   c.items = c.npair * c.nblk;

@@ -3,7 +3,7 @@
 // dimension.  Included by one translation unit per storage type.
 //
 // The sequence of each (batch b, head h) is cut into chunks of L tokens and
-// the chunks into segments of K chunks.  One workgroup (1024 threads, one per
+// the chunks into segments of K chunks.  One workgroup (512 threads, one per
 // CU) owns one segment and runs three phases:
 //
 //  1. Local pass.  For each chunk: per-token log-decay prefix sums cs_u,
@@ -147,7 +147,7 @@ struct Cfg {
   static constexpr int R = R_, P = P_;
   static constexpr int NC = N_;  // state size if fixed at compile time, else 0
   static constexpr int es = (int)sizeof(T_);
-  static constexpr int S = prefill_item_tokens(es, R_);  // tokens per rotation item
+  static constexpr int S = prefill_item_tokens(es, R_, N_, P_);  // tokens per rotation item
   static constexpr int KR = S * R_;                      // chunk rows per item
   static constexpr int PW = es / 2;                      // 32-bit words per pair
   static constexpr int NPT = P_ / 16;                    // p-tiles
@@ -575,6 +575,32 @@ __device__ __forceinline__ void state_update(const PrefillArgs& a, const Prefill
   // a wave's tiles share their n-tile when N/16 divides the number of state
   // waves: then one A fragment serves all
   const bool share = (wr.nsw % ntn) == 0;
+  if constexpr (ST::kFull && sizeof(T) == 2) {
+    // N fixed: the contraction runs over the whole row of 64 R slots (the
+    // rows past the chunk are zero), unrolled, with the fragments of the
+    // next step requested before the MFMAs of this one
+    constexpr int KS = 64 * C::R / M::K;
+    typename M::frag fa[2], fb[2][TPW];
+    fa[0] = load_frag(tW, nrow[0], 0, (const T*)nullptr);
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) fb[0][m] = load_frag(tX, prow[m], 0, (const T*)nullptr);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const int cb = k & 1;
+      if (k + 1 < KS) {
+        fa[cb ^ 1] = load_frag(tW, nrow[0], (k + 1) * M::K, (const T*)nullptr);
+#pragma unroll
+        for (int m = 0; m < TPW; ++m)
+          fb[cb ^ 1][m] = load_frag(tX, prow[m], (k + 1) * M::K, (const T*)nullptr);
+      }
+#pragma unroll
+      for (int m = 0; m < TPW; ++m) {
+        const typename M::frag am =
+            share ? fa[cb] : load_frag(tW, nrow[m], k * M::K, (const T*)nullptr);
+        acc[m] = M::mma(am, fb[cb][m], acc[m]);
+      }
+    }
+  } else
   for (int k0 = 0; k0 < lay.LRp; k0 += M::K) {
     const typename M::frag fa0 = load_frag(tW, nrow[0], k0, (const T*)nullptr);
 #pragma unroll
@@ -634,100 +660,43 @@ __device__ __forceinline__ void key_scalars4(const float* sc, int row0, float (&
   }
 }
 
-// One output unit: y rows of query block qb for the PPG p-tiles from p_lo.
+// Scores of key blocks kb .. kb+KB-1 (rows) against the unit's queries
+// (columns) times the chunk's mask: exp(cs_t - cs_u)(gamma_u + omega_u) for
+// keys u before the query t, gamma_t on the diagonal, 0 after it.  Lane
+// (g, li) holds key rows 4g .. 4g+3 of each block and query column li.
+template <int R, int KB>
+__device__ __forceinline__ void mask_scores(f32x4 (&sct)[KB], const float (&kcs)[KB][4],
+                                            const float (&kga)[KB][4],
+                                            const float (&kgom)[KB][4], int kb, int g, int tq,
+                                            float csq) {
+#pragma unroll
+  for (int i = 0; i < KB; ++i) {
+    // branch-free: every lane takes the exponential of each of its key
+    // tokens (rows 4g .. 4g+3 hold 4 / R tokens; the argument is 0 for keys
+    // not before the query, so it stays finite), then selects
+    constexpr int TPG = R < 4 ? 4 / R : 1;
+    float e[TPG];
+#pragma unroll
+    for (int k = 0; k < TPG; ++k) {
+      const int tk = ((kb + i) * 16 + 4 * g + k * R) / R;
+      e[k] = __expf(tk < tq ? csq - kcs[i][k * R] : 0.f);
+      asm volatile("" : "+v"(e[k]));  // keep the exponential out of a branch
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tk = ((kb + i) * 16 + 4 * g + j) / R;
+      sct[i][j] *= tk < tq ? e[j / R] * kgom[i][j] : (tk == tq ? kga[i][j] : 0.f);
+    }
+  }
+}
+
+// y rows of the unit (query block qb, PPG p-tiles from p_lo) to global memory.
 template <class C, int PPG>
-__device__ __forceinline__ void output_unit(const PrefillArgs& a, const Ctx& s, const rsrc& ry,
-                                            int qb, int p_lo, const float* sc, const Tile& tC,
-                                            const Tile& tB, const Tile& tX, const Tile& tG) {
-  using T = typename C::T;
-  using M = typename C::M;
+__device__ __forceinline__ void store_unit(const Ctx& s, const rsrc& ry, int qb, int p_lo,
+                                           const f32x4 (&acc)[PPG]) {
   constexpr int R = C::R, P = C::P;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, li = lane & 15;
-  const int N = a.N;
-  const float* s_cs = sc;
-  f32x4 acc[PPG];
-#pragma unroll
-  for (int pp = 0; pp < PPG; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint32_t qrow = (uint32_t)(qb * 16 + li);
-
-  // inter-chunk term: C~ G_c, rows scaled by exp(cs_t)
-  for (int n0 = 0; n0 < N; n0 += M::K) {
-    const typename M::frag fa = load_frag(tC, qrow, n0, (const T*)nullptr);
-#pragma unroll
-    for (int pp = 0; pp < PPG; ++pp) {
-      const typename M::frag fb =
-          load_frag(tG, (uint32_t)((p_lo + pp) * 16 + li), n0, (const T*)nullptr);
-      acc[pp] = M::mma(fa, fb, acc[pp]);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float scl = __expf(s_cs[(qb * 16 + 4 * g + j) / R]);
-#pragma unroll
-    for (int pp = 0; pp < PPG; ++pp) acc[pp][j] *= scl;
-  }
-
-  // intra-chunk term over key blocks up to the diagonal
-  const int tq = (qb * 16 + li) / R;
-  const float csq = s_cs[tq];
-  constexpr int KB = (sizeof(T) == 2) ? 2 : 1;  // 16-row key blocks per step
-  for (int kb = 0; kb * 16 <= qb * 16 + 15; kb += KB) {
-    f32x4 sct[KB];
-#pragma unroll
-    for (int i = 0; i < KB; ++i) sct[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int n0 = 0; n0 < N; n0 += M::K) {
-      const typename M::frag fq = load_frag(tC, qrow, n0, (const T*)nullptr);
-#pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        const typename M::frag fk =
-            load_frag(tB, (uint32_t)((kb + i) * 16 + li), n0, (const T*)nullptr);
-        sct[i] = M::mma(fk, fq, sct[i]);  // rows = keys, cols = queries
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      float kcs[4], kga[4], kgom[4];
-      key_scalars4<R>(sc, (kb + i) * 16 + 4 * g, kcs, kga, kgom);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tk = ((kb + i) * 16 + 4 * g + j) / R;
-        const float wl = __expf(csq - kcs[j]) * kgom[j];
-        sct[i][j] *= tk < tq ? wl : (tk == tq ? kga[j] : 0.f);
-      }
-    }
-    if constexpr (sizeof(T) == 2) {
-      bf16x8 fa;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        fa[j] = from_f32<bf16>(sct[0][j]);
-        fa[4 + j] = from_f32<bf16>(sct[1][j]);
-      }
-#pragma unroll
-      for (int pp = 0; pp < PPG; ++pp) {
-        const uint32_t xr = (uint32_t)((p_lo + pp) * 16 + li);
-        // key rows kb*16 + 4g.. and (kb+1)*16 + 4g..
-        const bf16x4 lo = tX.ref2<bf16x4>(xr, 8u * g, (uint32_t)kb * 32u);
-        const bf16x4 hi = tX.ref2<bf16x4>(xr, 32u + 8u * g, (uint32_t)kb * 32u);
-        bf16x8 fb;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          fb[j] = lo[j];
-          fb[4 + j] = hi[j];
-        }
-        acc[pp] = Mfma<bf16>::mma(fa, fb, acc[pp]);
-      }
-    } else {
-#pragma unroll
-      for (int pp = 0; pp < PPG; ++pp) {
-        const f32x4 xv =
-            tX.ref2<f32x4>((uint32_t)((p_lo + pp) * 16 + li), 16u * g, (uint32_t)kb * 64u);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[pp] = Mfma<float>::mma(sct[0][j], xv[j], acc[pp]);
-      }
-    }
-  }
-
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = qb * 16 + 4 * g + j;
@@ -743,6 +712,171 @@ __device__ __forceinline__ void output_unit(const PrefillArgs& a, const Ctx& s, 
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[pp][j]), ry, (int)o, 0, 0);
     }
   }
+}
+
+// One output unit: y rows of query block qb for the PPG p-tiles from p_lo.
+template <class C, int PPG>
+__device__ __forceinline__ void output_unit(const PrefillArgs& a, const Ctx& s, const rsrc& ry,
+                                            int qb, int p_lo, const float* sc, const Tile& tC,
+                                            const Tile& tB, const Tile& tX, const Tile& tG) {
+  using T = typename C::T;
+  using M = typename C::M;
+  constexpr int R = C::R;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int N = a.N;
+  const float* s_cs = sc;
+  f32x4 acc[PPG];
+#pragma unroll
+  for (int pp = 0; pp < PPG; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t qrow = (uint32_t)(qb * 16 + li);
+  const int tq = (qb * 16 + li) / R;
+  const float csq = s_cs[tq];
+  constexpr int KB = (sizeof(T) == 2) ? 2 : 1;  // 16-row key blocks per step
+
+  if constexpr (C::NC == 64) {
+    // N = 64 fixed (bfloat16): the query fragments are loaded once for the
+    // inter-chunk term and every key block, and each step requests all of
+    // its LDS operands before its first MFMA, so their latencies overlap
+    // (with N = 128 the registers for this are not there)
+    constexpr int NK = C::NC / M::K;
+    typename M::frag fq[NK];
+#pragma unroll
+    for (int n = 0; n < NK; ++n) fq[n] = load_frag(tC, qrow, n * M::K, (const T*)nullptr);
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+      typename M::frag fg[PPG];
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp)
+        fg[pp] = load_frag(tG, (uint32_t)((p_lo + pp) * 16 + li), n * M::K, (const T*)nullptr);
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) acc[pp] = M::mma(fq[n], fg[pp], acc[pp]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float scl = __expf(s_cs[(qb * 16 + 4 * g + j) / R]);
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) acc[pp][j] *= scl;
+    }
+    for (int kb = 0; kb * 16 <= qb * 16 + 15; kb += KB) {
+      // key fragments two n-steps at a time (the next pair is requested
+      // before the current pair's MFMAs)
+      typename M::frag fk[KB][2];
+#pragma unroll
+      for (int i = 0; i < KB; ++i)
+        fk[i][0] = load_frag(tB, (uint32_t)((kb + i) * 16 + li), 0, (const T*)nullptr);
+      bf16x4 xlo[PPG], xhi[PPG];
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) {
+        const uint32_t xr = (uint32_t)((p_lo + pp) * 16 + li);
+        // key rows kb*16 + 4g.. and (kb+1)*16 + 4g..
+        xlo[pp] = tX.ref2<bf16x4>(xr, 8u * g, (uint32_t)kb * 32u);
+        xhi[pp] = tX.ref2<bf16x4>(xr, 32u + 8u * g, (uint32_t)kb * 32u);
+      }
+      float kcs[KB][4], kga[KB][4], kgom[KB][4];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) key_scalars4<R>(sc, (kb + i) * 16 + 4 * g, kcs[i], kga[i], kgom[i]);
+      f32x4 sct[KB];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) sct[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int n = 0; n < NK; ++n) {
+        if (n + 1 < NK) {
+#pragma unroll
+          for (int i = 0; i < KB; ++i)
+            fk[i][(n + 1) & 1] =
+                load_frag(tB, (uint32_t)((kb + i) * 16 + li), (n + 1) * M::K, (const T*)nullptr);
+        }
+#pragma unroll
+        for (int i = 0; i < KB; ++i) sct[i] = M::mma(fk[i][n & 1], fq[n], sct[i]);  // keys x queries
+      }
+      mask_scores<R, KB>(sct, kcs, kga, kgom, kb, g, tq, csq);
+      bf16x8 fa;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        fa[j] = from_f32<bf16>(sct[0][j]);
+        fa[4 + j] = from_f32<bf16>(sct[1][j]);
+      }
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) {
+        bf16x8 fb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          fb[j] = xlo[pp][j];
+          fb[4 + j] = xhi[pp][j];
+        }
+        acc[pp] = Mfma<bf16>::mma(fa, fb, acc[pp]);
+      }
+    }
+  } else {
+    // inter-chunk term: C~ G_c, rows scaled by exp(cs_t)
+    for (int n0 = 0; n0 < N; n0 += M::K) {
+      const typename M::frag fa = load_frag(tC, qrow, n0, (const T*)nullptr);
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) {
+        const typename M::frag fb =
+            load_frag(tG, (uint32_t)((p_lo + pp) * 16 + li), n0, (const T*)nullptr);
+        acc[pp] = M::mma(fa, fb, acc[pp]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float scl = __expf(s_cs[(qb * 16 + 4 * g + j) / R]);
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) acc[pp][j] *= scl;
+    }
+
+    // intra-chunk term over key blocks up to the diagonal
+    for (int kb = 0; kb * 16 <= qb * 16 + 15; kb += KB) {
+      f32x4 sct[KB];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) sct[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int n0 = 0; n0 < N; n0 += M::K) {
+        const typename M::frag fq = load_frag(tC, qrow, n0, (const T*)nullptr);
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+          const typename M::frag fk =
+              load_frag(tB, (uint32_t)((kb + i) * 16 + li), n0, (const T*)nullptr);
+          sct[i] = M::mma(fk, fq, sct[i]);  // rows = keys, cols = queries
+        }
+      }
+      float kcs[KB][4], kga[KB][4], kgom[KB][4];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) key_scalars4<R>(sc, (kb + i) * 16 + 4 * g, kcs[i], kga[i], kgom[i]);
+      mask_scores<R, KB>(sct, kcs, kga, kgom, kb, g, tq, csq);
+      if constexpr (sizeof(T) == 2) {
+        bf16x8 fa;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          fa[j] = from_f32<bf16>(sct[0][j]);
+          fa[4 + j] = from_f32<bf16>(sct[1][j]);
+        }
+#pragma unroll
+        for (int pp = 0; pp < PPG; ++pp) {
+          const uint32_t xr = (uint32_t)((p_lo + pp) * 16 + li);
+          // key rows kb*16 + 4g.. and (kb+1)*16 + 4g..
+          const bf16x4 lo = tX.ref2<bf16x4>(xr, 8u * g, (uint32_t)kb * 32u);
+          const bf16x4 hi = tX.ref2<bf16x4>(xr, 32u + 8u * g, (uint32_t)kb * 32u);
+          bf16x8 fb;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            fb[j] = lo[j];
+            fb[4 + j] = hi[j];
+          }
+          acc[pp] = Mfma<bf16>::mma(fa, fb, acc[pp]);
+        }
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < PPG; ++pp) {
+          const f32x4 xv =
+              tX.ref2<f32x4>((uint32_t)((p_lo + pp) * 16 + li), 16u * g, (uint32_t)kb * 64u);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[pp] = Mfma<float>::mma(sct[0][j], xv[j], acc[pp]);
+        }
+      }
+    }
+  }
+  store_unit<C, PPG>(s, ry, qb, p_lo, acc);
 }
 
 // y of one chunk: units (query block qb, group of p-tiles) over the output
@@ -1119,8 +1253,9 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
 template <typename T, int R, int P>
 hipError_t launch_trp(const PrefillArgs& a, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
-    if (prefill_fixed_shape(a.L, a.N, 2) &&
-        prefill_layout(a.L, R, a.N, P, 2, true).total <= kLdsLimit)
+    const PrefillLayout fl = prefill_layout(a.L, R, a.N, P, 2, true);
+    if (prefill_fixed_shape(a.L, a.N, 2) && fl.total <= kLdsLimit &&
+        fl.items <= kPrefillThreads && fl.xitems <= kPrefillThreads)
       switch (a.N) {
         case 64: return launch_cfg<Cfg<T, R, P, 64>>(a, stream);
         case 128: return launch_cfg<Cfg<T, R, P, 128>>(a, stream);
