@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define M3SSM_VERSION 110 /* 1.1.0 */
+#define M3SSM_VERSION 120 /* 1.2.0 */
 
 typedef enum {
   M3_SUCCESS = 0,
@@ -116,20 +116,25 @@ size_t m3_prefill_workspace_size(const m3_dims* dims, int chunk, m3_dtype dtype)
  * element.
  *
  * workspace: device scratch of at least m3_prefill_workspace_size() bytes,
- * 256-byte aligned, owned by the caller.  It starts with the chain's int32
- * counters -- word 0 the work ticket, word 1 the error word, word 2 the
- * finished-workgroup count, word 3 unused, then one word per (batch, head)
- * unit: 16 + 4 * batch * nheads bytes -- and holds, from byte 4096 or from
- * the first 256-byte boundary past the counters (whichever is later), the
- * exit states that chain the segments of a sequence.  A call needs its
- * counters zero on entry and leaves them zero (its last workgroup resets
- * them), so a buffer zero-filled once serves every later call as long as
- * batch * nheads <= 1020, or as long as no call has more units than the call
- * before it on this buffer; otherwise zero the counter bytes before the call.
- * The error word is left nonzero, and stays so, if a segment ever waited
- * beyond its bounded spin for its predecessor (1), or if a call found the
- * counters not zero on entry (2; that call computes nothing).  Concurrent
- * calls need distinct workspaces.
+ * 256-byte aligned, owned by the caller.  A call runs one workgroup per
+ * segment: with units = batch * nheads and nC = ceil(seqlen / chunk), a
+ * segment is K = min(nC, max(1, ceil(nC * units / 256))) chunks and there are
+ * G = units * ceil(nC / K) of them (G < 256 + units, and G = units when
+ * units >= 256).  The workspace starts with the chain's int32 counters --
+ * word 0 the work ticket, word 1 the error word, word 2 the
+ * finished-workgroup count, word 3 unused, then one status word per
+ * segment: 16 + 4 G bytes -- and holds, from byte 4096 or from the first
+ * 256-byte boundary past the counters (whichever is later), one slot per
+ * segment (the map from its entry to its exit state, then its exit state)
+ * and the entry state of each sequence.  A call needs its counters zero on
+ * entry and leaves them zero (its last workgroup resets them), so a buffer
+ * zero-filled once serves every later call as long as batch * nheads <=
+ * 1020 (then 4 + G <= 1024 words), or as long as no call has more segments
+ * than the call before it on this buffer; otherwise zero the counter bytes
+ * before the call.  The error word is left nonzero, and stays so, if a
+ * segment ever waited beyond its bounded spin for a predecessor (1), or if a
+ * call found the counters not zero on entry (2; that call computes
+ * nothing).  Concurrent calls need distinct workspaces.
  *
  * Returns M3_SUCCESS once the kernel is enqueued (one launch per call).  y and h_final must not
  * overlap the inputs.  batch == 0 or seqlen == 0 enqueues nothing (h_final,

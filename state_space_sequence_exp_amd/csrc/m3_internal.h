@@ -34,16 +34,34 @@ struct PrefillArgs {
   const float* h0;      // [B*H][N][P] state before the first token, or null (zero)
   const void* x_prev;   // [B*H][R][P] input of the token before the first, or null (zero)
   const void* B_prev;   // [B*H][R][N] its B (null exactly when x_prev is)
-  int cont;             // 1: the entry kernel staged each sequence's entry state in ring slot 1
+  int cont;             // 1: the entry kernel staged each sequence's entry state in cont_entry
   void* y;
   float* h_final;
   // workspace carve
-  float* ring;   // [B*H][2][N][P] exit states of the two most recent segments
-  int* flags;    // [B*H] segments of each sequence whose exit state is published
-  int* ticket;   // [1]   next segment ticket (work order)
-  int* err;      // [1]   1: a wait for a predecessor timed out; 2: counters not zero at entry
-  int* done;     // [1]   finished workgroups; the last one zeroes flags, ticket, done
+  float* slots;       // [grid] per segment (ticket): aggregate E [N][P], exit state [N][P],
+                      //        rotation (cos, sin) per pair [N/2][2], decay, 3 unused
+  float* cont_entry;  // [B*H][N][P] entry state of each sequence's first segment (cont)
+  int* status;        // [grid] per ticket: 0 nothing, 1 aggregate, 2 exit state published
+  int* ticket;        // [1]   next segment ticket (work order)
+  int* err;           // [1]   1: a wait for a predecessor timed out; 2: counters not zero at entry
+  int* done;          // [1]   finished workgroups; the last one zeroes status, ticket, done
 };
+
+// Floats of one segment's slot in the prefill workspace.
+__host__ __device__ constexpr size_t prefill_slot_floats(int N, int P) {
+  return 2 * (size_t)N * P + (size_t)N + 4;
+}
+
+// Position of state element (n, p) in the workspace's states (the slots and
+// the entry states), which are stored the way the prefill kernel's waves
+// hold them: 16 x 16 tile i = (p / 16) (N / 16) + n / 16, then lane
+// 16 ((n % 16) / 4) + p % 16, then n % 4, so a lane's four values are one
+// 16-byte vector.
+__host__ __device__ inline size_t prefill_state_index(int N, int n, int p) {
+  const int i = (p / 16) * (N / 16) + n / 16;
+  const int lane = 16 * ((n % 16) / 4) + p % 16;
+  return ((size_t)i * 64 + lane) * 4 + n % 4;
+}
 
 struct DecodeArgs {
   int S, H, P, N, R;
@@ -83,13 +101,13 @@ __host__ __device__ inline uint32_t align_up_u32(uint32_t v, uint32_t a) {
 // Tokens per rotation item: one thread rotates one pair of B (and C) rows
 // over this many consecutive tokens (and all R ranks of each token).
 __host__ __device__ constexpr int prefill_item_tokens(int esize, int R, int N = 0, int P = 0) {
-  // the instantiation with N = 64 (and P <= 64) fixed, R = 1 and bfloat16 takes
-  // chunks of at most 64 tokens: 32 pairs x 16 blocks of 4 tokens give every
-  // one of 512 threads a rotation item and an x item
-  return (kPrefillThreads == 512 && esize == 2 && R == 1 && N == 64 && P != 0 && P <= 64)
-             ? 4
-             : (kPrefillThreads == 512 ? 2 : 1) *
-                   (esize == 2 ? (R == 1 ? 4 : 2) : (R == 4 ? 1 : 4 / R));
+  // tokens per item at 1024 threads, times 1024 / threads; the instantiation
+  // with N = 64 (and P <= 64) fixed, R = 1 and bfloat16 takes chunks of at
+  // most 64 tokens and half that many (at 512 threads 32 pairs x 16 blocks of
+  // 4 tokens give every thread a rotation item and an x item)
+  return (esize == 2 ? (R == 1 ? 4 : 2) : (R == 4 ? 1 : 4 / R)) * (1024 / kPrefillThreads) /
+         ((esize == 2 && R == 1 && N == 64 && P != 0 && P <= 64 && kPrefillThreads < 1024) ? 2
+                                                                                         : 1);
 }
 
 // Per-token scalars of one chunk, one of two alternating buffers:
@@ -110,7 +128,7 @@ struct PrefillLayout {
   int items;   // rotation items (npair * nblk)
   int xitems;  // x items ((P / 2) * nblk)
   uint32_t off_scal;   // 2 x kScalBytes
-  uint32_t off_part;   // items doubles: per-item angle sums
+  uint32_t off_part;   // per-item (or per-wave) angle sums, doubles
   uint32_t off_crot;   // npair float2: (cos, sin) of the chunk's total angle
   uint32_t off_srot;   // npair float2: (cos, sin) of the segment's total angle
   uint32_t off_sang;   // npair doubles: segment angle sums
@@ -145,7 +163,10 @@ __host__ __device__ inline PrefillLayout prefill_layout(int L, int R, int N, int
   c.xitems = (P / 2) * c.nblk;
   uint32_t o = 0;
   c.off_scal = o; o += 2 * kScalBytes;
-  c.off_part = o; o += (uint32_t)c.items * 8;
+  // (with N fixed, at least one double per pair and wave: the waves' totals)
+  const int nsum = fixed && c.npair * (kPrefillThreads / 64) > c.items ? c.npair * (kPrefillThreads / 64)
+                                                                        : c.items;
+  c.off_part = o; o += (uint32_t)nsum * 8;
   c.off_crot = o; o += (uint32_t)c.npair * 8;
   c.off_srot = o; o += (uint32_t)c.npair * 8;
   c.off_sang = o; o += (uint32_t)c.npair * 8;
@@ -177,7 +198,7 @@ __host__ __device__ inline WaveRoles prefill_wave_roles(int LR, int P) {
   constexpr int kW = kPrefillThreads / 64;
   const int nqb = LR / 16, npt = P / 16;
   WaveRoles w;
-  const int cap = nqb * 2 <= kW ? 4 : 2;
+  const int cap = (nqb * 2 <= kW || (kW <= 4 && nqb <= kW)) ? 4 : 2;
   w.ppg = npt < cap ? npt : cap;
   w.npg = npt / w.ppg;
   w.nout = nqb * w.npg;

@@ -47,21 +47,30 @@ m3_status check_prefill_shape(const m3_dims* d, int chunk, m3_dtype dtype) {
 }
 
 struct WsCarve {
-  size_t off_ring, total;
+  size_t grid, off_slots, off_cont, total;
 };
 
 // The counters come first, at offsets that do not depend on the shape:
-// int32 words ticket, error, finished workgroups, (unused), then one
-// published-segment counter per (batch, head) unit.  The exit-state ring
-// (the two latest segments of every unit) starts at 4 KiB or past the
-// counters, whichever is later, so calls with at most 1020 units never store
-// states where any call keeps counters.
-WsCarve carve(const m3_dims* d, int /*chunk*/, m3_dtype /*dtype*/) {
+// int32 words ticket, error, finished workgroups, (unused), then one status
+// word per workgroup (segment).  The segments' slots (aggregate, exit state,
+// rotation and decay) start at 4 KiB or past the counters, whichever is
+// later, then the continuation entry states.  A call has at most 256 + units
+// workgroups when units < 256 and exactly units otherwise, so calls with at
+// most 1020 units keep their counters below 4 KiB and never store states
+// where any call keeps counters.
+WsCarve carve(const m3_dims* d, int chunk, m3_dtype /*dtype*/) {
   WsCarve w;
   const size_t units = (size_t)d->batch * d->nheads;
-  const size_t counters = round256((4 + units) * sizeof(int));
-  w.off_ring = counters > 4096 ? counters : 4096;
-  w.total = round256(w.off_ring + units * 2 * (size_t)d->dstate_n * d->headdim_p * sizeof(float));
+  const int nC = (int)((d->seqlen + chunk - 1) / chunk);
+  const int K = m3::prefill_segment_chunks((int)d->batch, (int)d->nheads, nC > 0 ? nC : 1);
+  w.grid = units * (size_t)((nC + K - 1) / K);
+  const size_t counters = round256((4 + w.grid) * sizeof(int));
+  w.off_slots = counters > 4096 ? counters : 4096;
+  const size_t np = (size_t)d->dstate_n * d->headdim_p;
+  w.off_cont = w.off_slots + round256(w.grid * m3::prefill_slot_floats((int)d->dstate_n,
+                                                                       (int)d->headdim_p) *
+                                      sizeof(float));
+  w.total = round256(w.off_cont + units * np * sizeof(float));
   return w;
 }
 
@@ -159,11 +168,12 @@ m3_status prefill_impl(const m3_dims* dims, m3_dtype dtype, int chunk, const flo
   a.h_final = h_final;
   if (work) {
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    a.ring = reinterpret_cast<float*>(ws + w.off_ring);
+    a.slots = reinterpret_cast<float*>(ws + w.off_slots);
+    a.cont_entry = reinterpret_cast<float*>(ws + w.off_cont);
     a.ticket = reinterpret_cast<int*>(ws);
     a.err = a.ticket + 1;
     a.done = a.ticket + 2;
-    a.flags = a.ticket + 4;
+    a.status = a.ticket + 4;
   }
   const hipError_t e = m3::launch_prefill(a, dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;

@@ -19,8 +19,9 @@ __global__ void copy_or_zero_kernel(float* dst, const float* src, size_t n) {
 // from a given state h0 and previous token (x_prev, B_prev):
 // G = h0 + (1 - lam_0) dt_0 B_prev x_prev^T, the state plus the trapezoid's
 // previous-input term, which the first token's update decays and rotates
-// together.  Written to ring slot 1 of each sequence, where the prefill
-// kernel's first segment reads its entry.  One thread per state element.
+// together.  Written to the workspace's entry states, where the prefill
+// kernel's first segment (and the look-back of later ones) reads it.  One
+// thread per state element.
 template <typename T>
 __global__ void entry_kernel(PrefillArgs a) {
   const size_t np = (size_t)a.N * a.P;
@@ -41,7 +42,7 @@ __global__ void entry_kernel(PrefillArgs a) {
         acc = __builtin_fmaf(to_f32(bp[r * a.N + n]), to_f32(xp[r * a.P + p]), acc);
       v = __builtin_fmaf(w0, acc, v);
     }
-    a.ring[(bh * 2 + 1) * np + e] = v;
+    a.cont_entry[bh * np + prefill_state_index(a.N, n, p)] = v;
   }
 }
 

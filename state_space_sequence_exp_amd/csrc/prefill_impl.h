@@ -58,10 +58,12 @@
 // Work order and the chain.  Workgroups take tickets from a counter; ticket
 // t is segment t / (B*H) of sequence t % (B*H).  A workgroup only waits for a
 // smaller ticket, which is held by a running workgroup, so the grid always
-// drains.  Exit states travel through a two-slot ring per sequence with
-// device-coherent (sc1) stores and loads, and a per-sequence counter that is
-// raised only after the stores have completed; the wait is bounded and
-// raises an error word (1) instead of hanging.  A ticket outside the grid
+// drains.  Segments publish their aggregate (the map from entry to exit
+// state) or their exit state in a per-ticket slot with device-coherent (sc1)
+// stores and loads, and a per-ticket status word that is raised only after
+// the stores have completed; a segment finds its entry by looking back over
+// its predecessors' slots (in groups, see phase 2).  Every wait is bounded
+// and raises an error word (1) instead of hanging.  A ticket outside the grid
 // (counters not zero at entry) raises the error word (2) and does no work.
 #pragma once
 
@@ -74,6 +76,8 @@ namespace pf {
 constexpr int kT = kPrefillThreads;
 constexpr int kW = kT / kWave;             // waves per workgroup
 constexpr int kSpinLimit = 1 << 18;        // bounded wait (a few hundred ms)
+constexpr int kGroup = 8;                  // segments per look-back group
+constexpr int kBatch = 4;                  // aggregates loaded at once in the look-back
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer descriptor, gfx9 family
 constexpr uint32_t kOOB = 0x7ff00000u;     // a buffer offset past every range
 constexpr double kInv2PiD = 0.15915494309189533577;
@@ -151,6 +155,11 @@ struct Cfg {
   static constexpr int KR = S * R_;                      // chunk rows per item
   static constexpr int PW = es / 2;                      // 32-bit words per pair
   static constexpr int NPT = P_ / 16;                    // p-tiles
+  // N fixed with N / 2 pairs dividing the wave: wave w holds token blocks
+  // w * 128 / N .. (w + 1) * 128 / N - 1 of every pair, and the angle sums
+  // before a block are the wave totals of the waves before it plus, with two
+  // blocks per wave, the lower half's sum (see step_partials)
+  static constexpr bool kWaveSums = N_ != 0 && 64 % (N_ / 2) == 0 && 64 / (N_ / 2) <= 2;
 };
 
 // Raw inputs of one chunk for this thread, staged in registers.
@@ -377,22 +386,34 @@ __device__ __forceinline__ double item_angle_sum(const float (&th)[S], const flo
 // Rotation item (pair kp, token block blk): angles from the preceding blocks'
 // sums, rotated B~ (and C~) pairs, the weighted transposed B~ rows, and for
 // the last block the chunk's total rotation (and the segment angle sum).
-// s_part holds the items' angle sums (block-major), s_crot receives the
-// chunk's total rotation per pair and s_sang the segment's angle sums.
+// s_part holds the items' angle sums (block-major), or with wave sums the
+// waves' totals (wave-major) and inw the sum of this wave's blocks before
+// this one; s_crot receives the chunk's total rotation per pair and s_sang
+// the segment's angle sums.
 template <class C, bool kWithC, bool kAccumSeg>
 __device__ __forceinline__ void rotate_item(int npair, int nblk, int kp, int blk,
                                             const float (&th)[C::S], const float (&dt)[C::S],
                                             const uint32_t (&bv)[C::KR * C::PW],
                                             const uint32_t (&cv)[C::KR * C::PW],
                                             const float* s_w, const Tile& tB, const Tile& tC,
-                                            const Tile& tW, const double* s_part, float2* s_crot,
-                                            double* s_sang) {
+                                            const Tile& tW, const double* s_part, double inw,
+                                            float2* s_crot, double* s_sang) {
   using T = typename C::T;
   constexpr int R = C::R;
-  // sum of the preceding blocks' angles; unrolled so the LDS reads overlap
-  double pre = 0.0;
+  // sum of the preceding blocks' angles
+  double pre = inw;
+  if constexpr (C::kWaveSums) {
+    // the totals of the waves before this one, all requested at once
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    double v[kW - 1];
+#pragma unroll
+    for (int q = 0; q < kW - 1; ++q) v[q] = s_part[q * npair + kp];
+#pragma unroll
+    for (int q = 0; q < kW - 1; ++q) pre += q < wave ? v[q] : 0.0;
+  } else {
 #pragma unroll 8
-  for (int q = 0; q < blk; ++q) pre += s_part[q * npair + kp];
+    for (int q = 0; q < blk; ++q) pre += s_part[q * npair + kp];
+  }
   double rv = pre * kInv2PiD;
   rv -= __builtin_rint(rv);
   float r = static_cast<float>(rv);  // revolutions
@@ -954,29 +975,201 @@ __device__ __forceinline__ Tiles step_tiles(const Tiles& t, unsigned char* smem)
   return r;
 }
 
-// [P]: this thread's item's angle sum.
+// [P]: this thread's item's angle sum into LDS.  With wave sums (N fixed) a
+// wave's total per pair goes to LDS instead, and the return value is the sum
+// of this wave's blocks before this thread's (the lower half's sum for lanes
+// 32..63 when a wave holds two blocks, else 0).  Items fill whole waves.
 template <class C>
-__device__ __forceinline__ void step_partials(const PrefillArgs& a, const PrefillLayout& lay,
-                                              const Ctx& s, const Map& m, int c,
-                                              const Stage<C>& st, float* sc,
-                                              unsigned char* smem) {
+__device__ __forceinline__ double step_partials(const PrefillArgs& a, const PrefillLayout& lay,
+                                                const Ctx& s, const Map& m, int c,
+                                                const Stage<C>& st, float* sc,
+                                                unsigned char* smem) {
   double* s_part = reinterpret_cast<double*>(smem + lay.off_part);
-  if (m.act) s_part[m.blk * lay.npair + m.kp] = item_angle_sum<C::S>(st.th, st.dt);
+  if constexpr (C::kWaveSums) {
+    if (!m.act) return 0.0;
+    const double own = item_angle_sum<C::S>(st.th, st.dt);
+    const int wave = threadIdx.x >> 6;
+    if constexpr (C::NC / 2 == 32) {
+      // lanes l and l + 32 hold blocks 2w and 2w + 1 of pair l % 32:
+      // v_permlane32_swap with both operands own gives (own of lanes 0..31)
+      // twice in the first result and (own of lanes 32..63) twice in the
+      // second, so each lane reads its partner's sum from the other half
+      const uint64_t b = __builtin_bit_cast(uint64_t, own);
+      const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+      const auto hi =
+          __builtin_amdgcn_permlane32_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+      const bool upper = (threadIdx.x & 32) != 0;
+      const double partner = __builtin_bit_cast(
+          double, (uint64_t)(upper ? lo[0] : lo[1]) | ((uint64_t)(upper ? hi[0] : hi[1]) << 32));
+      if (!upper) s_part[wave * 32 + m.kp] = own + partner;
+      return upper ? partner : 0.0;
+    } else {
+      s_part[wave * lay.npair + m.kp] = own;
+      return 0.0;
+    }
+  } else {
+    if (m.act) s_part[m.blk * lay.npair + m.kp] = item_angle_sum<C::S>(st.th, st.dt);
+    return 0.0;
+  }
 }
 
 // [R]: rotation items and x items into LDS (consumes the staged registers).
 template <class C, bool kWithC, bool kAccumSeg>
 __device__ __forceinline__ void step_rotate(const PrefillArgs& a, const PrefillLayout& lay,
                                             const Ctx& s, const Map& m, int c, Stage<C>& st,
-                                            const float* sc, const Tiles& t,
+                                            const float* sc, const Tiles& t, double inw,
                                             unsigned char* smem) {
   const float* s_w = sc + 3 * kLMax;
   if (m.xact) write_x_item<C>(m.jp, m.xblk, st.x, t.X);
   if (m.act)
     rotate_item<C, kWithC, kAccumSeg>(
         lay.npair, lay.nblk, m.kp, m.blk, st.th, st.dt, st.b, st.c, s_w, t.B, t.C, t.W,
-        reinterpret_cast<const double*>(smem + lay.off_part),
+        reinterpret_cast<const double*>(smem + lay.off_part), inw,
         reinterpret_cast<float2*>(smem + lay.off_crot), reinterpret_cast<double*>(smem + lay.off_sang));
+}
+
+// ---- chain helpers ---------------------------------------------------------
+// This wave's state tiles to / from a state in the workspace (stored tile by
+// tile as the waves hold them, prefill_state_index), one 16-byte vector per
+// lane and tile, with device-coherent (sc1) buffer stores and loads: the
+// other side of the exchange runs on another CU, possibly another XCD.
+constexpr int kSc1 = 16;  // cache-policy operand of the buffer intrinsics: sc1
+template <class C>
+__device__ __forceinline__ void store_state_tiles(const PrefillArgs& a, const WaveRoles& wr,
+                                                  const f32x4 (&v)[kMaxStTiles], float* dst) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ntiles = (a.N / 16) * C::NPT;
+  const rsrc r = make_rsrc(dst, (uint32_t)(a.N * C::P * 4));
+#pragma unroll
+  for (int q = 0; q < kMaxStTiles; ++q) {
+    const int i = state_tile(wr, wave, q, ntiles);
+    if (i >= 0)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[q]), r,
+                                             (i * 64 + lane) * 16, 0, kSc1);
+  }
+}
+template <class C>
+__device__ __forceinline__ void load_state_tiles(const PrefillArgs& a, const WaveRoles& wr,
+                                                 const float* src, f32x4 (&v)[kMaxStTiles]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ntiles = (a.N / 16) * C::NPT;
+  const rsrc r = make_rsrc(src, (uint32_t)(a.N * C::P * 4));
+#pragma unroll
+  for (int q = 0; q < kMaxStTiles; ++q) {
+    v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int i = state_tile(wr, wave, q, ntiles);
+    if (i >= 0)
+      v[q] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (i * 64 + lane) * 16, 0, kSc1));
+  }
+}
+
+// Publish this segment's status word (1 aggregate, 2 exit state) once every
+// thread's stores have completed: no writeback fence is needed, since the
+// stores and the readers' loads are device-coherent.
+__device__ __forceinline__ void publish_status(const PrefillArgs& a, int ticket, int st) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.status + ticket, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until the status words of tickets first - k * stride (k < n) are 1
+// and, if last_idx >= 0, the status word of ticket last_idx is 2: one lane
+// per word, each wait bounded.  Returns whether every wait succeeded (false:
+// a wait timed out and the error word is 1); the answer reaches the
+// workgroup through the LDS word s_word.
+__device__ __forceinline__ bool wait_statuses(const PrefillArgs& a, int first, int stride, int n,
+                                              int last_idx, int* s_word) {
+  const int tid = threadIdx.x;
+  if (tid == 0) *s_word = 1;
+  __syncthreads();
+  const int idx = tid < n ? first - tid * stride : (tid == n ? last_idx : -1);
+  if (idx >= 0) {
+    const int want = tid < n ? 1 : 2;
+    int spins = 0;
+    while (__hip_atomic_load(a.status + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) {
+        __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_word = 0;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  return *s_word != 0;
+}
+
+// ent += D R v: the accumulated map applied to a state v (an exit state, or
+// the continuation's entry), per state tile.
+template <class C>
+__device__ __forceinline__ void apply_map(const PrefillArgs& a, const WaveRoles& wr,
+                                          const float2 (&accr)[kMaxStTiles][2], float accD,
+                                          const f32x4 (&v)[kMaxStTiles],
+                                          f32x4 (&ent)[kMaxStTiles]) {
+#pragma unroll
+  for (int q = 0; q < kMaxStTiles; ++q) {
+    const float2 r0 = accr[q][0], r1 = accr[q][1];
+    const float v0 = accD * v[q][0], v1 = accD * v[q][1];
+    const float v2 = accD * v[q][2], v3 = accD * v[q][3];
+    ent[q][0] += r0.x * v0 - r0.y * v1;
+    ent[q][1] += r0.y * v0 + r0.x * v1;
+    ent[q][2] += r1.x * v2 - r1.y * v3;
+    ent[q][3] += r1.y * v2 + r1.x * v3;
+  }
+}
+
+// A predecessor's aggregate as this wave holds it: E per state tile, the
+// rotation of each tile's two pairs (lane rows 4g .. 4g+3), the decay.
+struct Agg {
+  f32x4 v[kMaxStTiles];
+  float2 r[kMaxStTiles][2];
+  float d;
+};
+
+// Request a slot's aggregate (E at slot, rotation and decay at slot + 2NP).
+template <class C>
+__device__ __forceinline__ void load_agg(const PrefillArgs& a, const WaveRoles& wr,
+                                         const float* slot, Agg& g_) {
+  load_state_tiles<C>(a, wr, slot, g_.v);
+  const float* rd = slot + 2 * (size_t)a.N * C::P;
+  const rsrc r = make_rsrc(rd, (uint32_t)(a.N * 4 + 4));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int ntn = a.N / 16, ntiles = ntn * C::NPT;
+#pragma unroll
+  for (int q = 0; q < kMaxStTiles; ++q) {
+    g_.r[q][0] = g_.r[q][1] = make_float2(1.f, 0.f);
+    const int i = state_tile(wr, wave, q, ntiles);
+    if (i >= 0) {
+      // (cos, sin) of pairs kq and kq + 1: one 16-byte vector
+      const int kq = (i % ntn) * 8 + 2 * g;
+      const f32x4 c = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, kq * 8, 0, kSc1));
+      g_.r[q][0] = make_float2(c[0], c[1]);
+      g_.r[q][1] = make_float2(c[2], c[3]);
+    }
+  }
+  g_.d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, a.N * 4, 0, kSc1));
+}
+
+// Compose a predecessor's aggregate into the accumulated map: the offset
+// gains D R E, then the rotation and decay take the predecessor's.
+template <class C>
+__device__ __forceinline__ void compose_map(const PrefillArgs& a, const WaveRoles& wr,
+                                            const Agg& g_, float2 (&accr)[kMaxStTiles][2],
+                                            float& accD, f32x4 (&ent)[kMaxStTiles]) {
+  apply_map<C>(a, wr, accr, accD, g_.v, ent);
+#pragma unroll
+  for (int q = 0; q < kMaxStTiles; ++q)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float2 r = accr[q][k], c = g_.r[q][k];
+      accr[q][k] = make_float2(r.x * c.x - r.y * c.y, r.y * c.x + r.x * c.y);
+    }
+  accD *= g_.d;
 }
 
 // One workgroup's segment: local exit state, chain, outputs.  `ticket` is
@@ -1056,9 +1249,9 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     float* sc = s_scal + buf * (kScalBytes / 4);
     const Ctx s = step_ctx(s0);
     const Tiles t = step_tiles<C>(tiles0, smem);
-    step_partials<C>(a, lay, s, m, c, stg, sc, smem);
+    const double inw = step_partials<C>(a, lay, s, m, c, stg, sc, smem);
     __syncthreads();
-    step_rotate<C, false, true>(a, lay, s, m, c, stg, sc, t, smem);
+    step_rotate<C, false, true>(a, lay, s, m, c, stg, sc, t, inw, smem);
     // prefetch the next chunk; the last step prefetches the first chunk
     // again, with C, for phase 3
     if (c + 1 < s.c1)
@@ -1080,7 +1273,16 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     buf ^= 1;
   }
 
-  // ---- phase 2: chain ------------------------------------------------------
+  // ---- phase 2: chain (look-back in groups) ---------------------------------
+  // Each segment's map from entry to exit state is x -> R(Phi) D x + E_local
+  // (linear recurrence).  Segments form groups of kGroup consecutive
+  // segments.  Inside a group a segment publishes its map (its aggregate) as
+  // soon as its local pass is done; the group's last segment publishes its
+  // exit state instead.  A segment's entry state is its group predecessors'
+  // maps, composed newest first, applied to the previous group's exit state
+  // (or to the sequence's start).  So only the groups chain one after
+  // another, and every entry is computed by the same operations on every
+  // call (the result does not depend on timing).
   __syncthreads();
   for (int kp = tid; kp < npair; kp += kT) {
     float sn, cn;
@@ -1088,73 +1290,102 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     s_srot[kp] = make_float2(cn, sn);
   }
   const float segD = __expf(seg_logdecay);
+  const bool last = s.seg == a.nSeg - 1;
+  const bool group_end = s.seg % kGroup == kGroup - 1;
+  const size_t np = (size_t)a.N * P;
+  const size_t slotf = prefill_slot_floats(a.N, P);
+  float* mine = a.slots + (size_t)ticket * slotf;
+  int* s_misc = reinterpret_cast<int*>(smem + lay.off_misc);
   f32x4 ent[kMaxStTiles];
 #pragma unroll
   for (int q = 0; q < kMaxStTiles; ++q) ent[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // the entry of a sequence's first segment is zero, or (a.cont) the state
-  // staged in the ring slot a predecessor would have used by the entry kernel
-  // that ran before this one
-  if (s.seg > 0 || a.cont) {
-    if (tid == 0 && s.seg > 0) {
-      int spins = 0;
-      while (__hip_atomic_load(a.flags + s.bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-             s.seg) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > kSpinLimit) {
-          __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
+  __syncthreads();  // s_srot
+  if (!last && !group_end) {
+    // aggregate: E_local, the segment's rotation per pair, its decay
+    store_state_tiles<C>(a, wr, stt, mine);
+    for (int kp = tid; kp < npair; kp += kT) {
+      __hip_atomic_store(mine + 2 * np + 2 * kp, s_srot[kp].x, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(mine + 2 * np + 2 * kp + 1, s_srot[kp].y, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0)
+      __hip_atomic_store(mine + 2 * np + a.N, segD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    publish_status(a, ticket, 1);
+  }
+  {
+    // the accumulated map: per state tile the rotation of its lane's two
+    // pairs, one decay, and the accumulated offset (in ent)
+    float2 accr[kMaxStTiles][2];
+#pragma unroll
+    for (int q = 0; q < kMaxStTiles; ++q) accr[q][0] = accr[q][1] = make_float2(1.f, 0.f);
+    float accD = 1.f;
+    const int BH = a.nb * a.H;
+    const int g0 = s.seg - s.seg % kGroup;  // first segment of the group
+    const int nprev = s.seg - g0;           // aggregates to compose
+    // every wait at once: the group predecessors' aggregates and the
+    // previous group's exit state
+    const bool ok = wait_statuses(a, (s.seg - 1) * BH + s.bh, BH, nprev,
+                                  g0 > 0 ? (g0 - 1) * BH + s.bh : -1, s_misc + 2);
+    if (ok) {
+      // newest first, several aggregates' loads in flight at a time (fewer
+      // with more state per wave: registers)
+      constexpr int NB = C::NC == 64 ? kBatch : (C::NC != 0 ? kBatch / 2 : 1);
+      for (int j0 = s.seg - 1; j0 >= g0; j0 -= NB) {
+        Agg ag[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+          if (j0 - k >= g0) load_agg<C>(a, wr, a.slots + (size_t)((j0 - k) * BH + s.bh) * slotf, ag[k]);
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+          if (j0 - k >= g0) compose_map<C>(a, wr, ag[k], accr, accD, ent);
+      }
+      // applied to the previous group's exit state, or the sequence's start
+      // (zero, or the continuation's entry state)
+      if (g0 > 0 || a.cont) {
+        const float* src = g0 > 0 ? a.slots + (size_t)((g0 - 1) * BH + s.bh) * slotf + np
+                                  : a.cont_entry + (size_t)s.bh * np;
+        f32x4 v[kMaxStTiles];
+        load_state_tiles<C>(a, wr, src, v);
+        apply_map<C>(a, wr, accr, accD, v, ent);
       }
     }
-    __syncthreads();
-    const float* src = a.ring + ((size_t)s.bh * 2 + ((s.seg - 1) & 1)) * a.N * P;
+  }
+  if (last || group_end) {
+    // exit state = R(Phi_seg) (D_seg * entry) + local
 #pragma unroll
     for (int q = 0; q < kMaxStTiles; ++q) {
       const int i = state_tile(wr, wave, q, ntiles);
       if (i >= 0) {
-        const int nt = i % ntn, pt = i / ntn;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          ent[q][j] = __hip_atomic_load(src + (size_t)(nt * 16 + 4 * g + j) * P + pt * 16 + li,
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int nt = i % ntn;
+        const int kq = nt * 8 + 2 * g;
+        const float2 r0 = s_srot[kq], r1 = s_srot[kq + 1];
+        f32x4 e;
+        const float v0 = segD * ent[q][0], v1 = segD * ent[q][1];
+        const float v2 = segD * ent[q][2], v3 = segD * ent[q][3];
+        e[0] = r0.x * v0 - r0.y * v1 + stt[q][0];
+        e[1] = r0.y * v0 + r0.x * v1 + stt[q][1];
+        e[2] = r1.x * v2 - r1.y * v3 + stt[q][2];
+        e[3] = r1.y * v2 + r1.x * v3 + stt[q][3];
+        stt[q] = e;
       }
     }
-  } else {
-    __syncthreads();
-  }
-  // exit state = R(Phi_seg) (D_seg * entry) + local
-  const bool last = s.seg == a.nSeg - 1;
-  float* dst = a.ring + ((size_t)s.bh * 2 + (s.seg & 1)) * a.N * P;
+    if (!last) {
+      store_state_tiles<C>(a, wr, stt, mine + np);
+      publish_status(a, ticket, 2);
+    } else if (a.h_final) {
 #pragma unroll
-  for (int q = 0; q < kMaxStTiles; ++q) {
-    const int i = state_tile(wr, wave, q, ntiles);
-    if (i >= 0) {
-      const int nt = i % ntn, pt = i / ntn;
-      const int kq = nt * 8 + 2 * g;
-      const float2 r0 = s_srot[kq], r1 = s_srot[kq + 1];
-      f32x4 e;
-      const float v0 = segD * ent[q][0], v1 = segD * ent[q][1];
-      const float v2 = segD * ent[q][2], v3 = segD * ent[q][3];
-      e[0] = r0.x * v0 - r0.y * v1 + stt[q][0];
-      e[1] = r0.y * v0 + r0.x * v1 + stt[q][1];
-      e[2] = r1.x * v2 - r1.y * v3 + stt[q][2];
-      e[3] = r1.y * v2 + r1.x * v3 + stt[q][3];
+      for (int q = 0; q < kMaxStTiles; ++q) {
+        const int i = state_tile(wr, wave, q, ntiles);
+        if (i >= 0) {
+          const int nt = i % ntn, pt = i / ntn;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const size_t off = (size_t)(nt * 16 + 4 * g + j) * P + pt * 16 + li;
-        if (!last)
-          __hip_atomic_store(dst + off, e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else if (a.h_final)
-          a.h_final[(size_t)s.bh * a.N * P + off] = e[j];
+          for (int j = 0; j < 4; ++j)
+            a.h_final[(size_t)s.bh * np + (size_t)(nt * 16 + 4 * g + j) * P + pt * 16 + li] =
+                stt[q][j];
+        }
       }
     }
-  }
-  if (!last) {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's ring stores have completed
-    __syncthreads();
-    if (tid == 0)
-      __hip_atomic_store(a.flags + s.bh, s.seg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 #pragma unroll
   for (int q = 0; q < kMaxStTiles; ++q) stt[q] = ent[q];
@@ -1165,9 +1396,9 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     const bool more = c + 1 < s.c1;
     const Ctx s = step_ctx(s0);
     const Tiles t = step_tiles<C>(tiles0, smem);
-    step_partials<C>(a, lay, s, m, c, stg, sc, smem);
+    const double inw = step_partials<C>(a, lay, s, m, c, stg, sc, smem);
     __syncthreads();
-    step_rotate<C, true, false>(a, lay, s, m, c, stg, sc, t, smem);
+    step_rotate<C, true, false>(a, lay, s, m, c, stg, sc, t, inw, smem);
     state_to_lds<C>(a, wr, stt, t.G);
     if (more) issue_loads<C, true>(a, s, m, c + 1, stg);
     __syncthreads();
@@ -1198,7 +1429,8 @@ __device__ __forceinline__ void bad_ticket(const PrefillArgs& a) {
 
 // The last workgroup to finish zeroes the chain counters, so the next call
 // on this workspace starts from zeros without a reset launch (every other
-// workgroup has published its flag before counting itself done).
+// workgroup has published and read every status word it touches before
+// counting itself done).
 __device__ __forceinline__ void finish_workgroup(const PrefillArgs& a, int* s_misc) {
   const int tid = threadIdx.x;
   __syncthreads();
@@ -1209,7 +1441,7 @@ __device__ __forceinline__ void finish_workgroup(const PrefillArgs& a, int* s_mi
   __syncthreads();
   if (s_misc[1]) {
     __threadfence();
-    for (int i = tid; i < a.nb * a.H; i += kT) a.flags[i] = 0;
+    for (int i = tid; i < (int)gridDim.x; i += kT) a.status[i] = 0;
     if (tid == 0) {
       *a.ticket = 0;
       *a.done = 0;

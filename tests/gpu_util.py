@@ -44,6 +44,22 @@ def upload_prefill(inp):
         theta=to_gpu_f32(inp["theta"]), A=to_gpu_f32(inp["A"]))
 
 
+def prefill_grid(nb, nt, nh, chunk):
+    """Workgroups (segments) of one prefill call, by the rule the workspace
+    layout documents: K = clamp(ceil(nC * units / 256), 1, nC) chunks per
+    segment, units * ceil(nC / K) segments."""
+    units = nb * nh
+    nc = max(1, -(-nt // chunk))
+    k = min(nc, max(1, -(-(nc * units) // 256)))
+    return units * (-(-nc // k))
+
+
+def counter_words(nb, nt, nh, chunk):
+    """int32 words of the workspace's chain counters: four, then one status
+    word per workgroup."""
+    return 4 + prefill_grid(nb, nt, nh, chunk)
+
+
 def gpu_prefill(inp, chunk, dev_inp=None, calls=1):
     """Prefill through the C ABI with an explicit zero-filled workspace (reused
     for `calls` calls), then check the workspace's chain counters: the kernel
@@ -59,7 +75,7 @@ def gpu_prefill(inp, chunk, dev_inp=None, calls=1):
         y, hf = m3.prefill(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"], chunk,
                            workspace=ws)
     if need > 0:
-        words = ws[:4 * (nb * nh + 4)].view(torch.int32).cpu().numpy()
+        words = ws[:4 * counter_words(nb, nt, nh, chunk)].view(torch.int32).cpu().numpy()
         assert words[1] == 0, "error word set: %d" % words[1]
         assert not words.any(), "chain counters not reset: %s" % words
     return y, hf

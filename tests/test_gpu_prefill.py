@@ -8,7 +8,7 @@ import pytest
 
 from state_space_sequence_exp_amd import inputs as I
 
-from gpu_util import (TOL, from_gpu, gpu_prefill, log, oracle_prefill, rel_l2, upload_prefill,
+from gpu_util import (TOL, counter_words, from_gpu, gpu_prefill, log, oracle_prefill, rel_l2, upload_prefill,
                       worst_unit_rel)
 
 pytestmark = pytest.mark.gpu
@@ -156,7 +156,8 @@ def test_workspace_reused_across_shapes():
         assert rel_l2(from_gpu(h), h_ref) <= TOL["bf16"]
     assert np.array_equal(from_gpu(outs[0][0]), from_gpu(outs[2][0]))
     assert np.array_equal(from_gpu(outs[1][0]), from_gpu(outs[3][0]))
-    assert not ws[:4 * (2 * 3 + 4)].view(torch.int32).cpu().numpy().any()
+    nw = max(counter_words(2, 900, 3, 64), counter_words(1, 300, 2, 32))
+    assert not ws[:4 * nw].view(torch.int32).cpu().numpy().any()
 
 
 def test_dirty_counters_reported():
@@ -169,7 +170,7 @@ def test_dirty_counters_reported():
     g = upload_prefill(inp)
     need = m3.prefill_workspace_size(1, 200, 2, 64, 32, 1, 64, g["x"].dtype)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
-    words = ws[:4 * (2 + 4)].view(torch.int32)
+    words = ws[:4 * counter_words(1, 200, 2, 64)].view(torch.int32)
     words[0] = 1 << 20                   # a ticket far past the grid
     m3.prefill(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"], 64, workspace=ws)
     w = words.cpu().numpy()
