@@ -14,6 +14,8 @@
 // (blockIdx.y: B rows, C rows, x rows); a B or C row of N channels is N / E
 // consecutive lanes (E elements per vector, N / E a power of two dividing the
 // wave), whose sum of squares is reduced by lane shuffles inside that group.
+#include <initializer_list>
+
 #include "m3_device.h"
 #include "m3_internal.h"
 
@@ -57,8 +59,20 @@ __device__ __forceinline__ uint4 pack16(const float (&v)[4], const float*) {
 
 // Vectors per thread: each thread handles kU vectors a grid-stride apart
 // (the stride is a multiple of the wave, so a row's lane group stays in one
-// wave), issuing all their loads before any arithmetic.
-constexpr int kU = 4;
+// wave), issuing all their loads before any arithmetic.  The stride is also a
+// multiple of every row space's period M (heads x ranks x 16-byte pieces per
+// row; launch_block_*), so all of a thread's vectors share one (head, rank,
+// piece) and the thread reads its weights once.
+constexpr int kU = 8;
+
+template <int E>
+__device__ __forceinline__ void load_w(const float* p, float (&w)[E]) {
+#pragma unroll
+  for (int q = 0; q < E / 4; ++q) {
+    const float4 v = reinterpret_cast<const float4*>(p)[q];
+    w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+  }
+}
 
 template <typename T>
 __global__ void __launch_bounds__(kBlkThreads) prepass_kernel(BlockArgs a) {
@@ -72,30 +86,19 @@ __global__ void __launch_bounds__(kBlkThreads) prepass_kernel(BlockArgs a) {
     const size_t nvec = a.rows * a.R * (size_t)cpr;
     const uint4* src = static_cast<const uint4*>(part == 0 ? a.B : a.C);
     uint4* dst = static_cast<uint4*>(part == 0 ? a.B_out : a.C_out);
-    const float* wbase = part == 0 ? a.norm_B : a.norm_C;
-    const float* bbase = part == 0 ? a.bias_B : a.bias_C;
     uint4 raw[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const size_t i = i0 + u * stride;
       raw[u] = i < nvec ? src[i] : make_uint4(0u, 0u, 0u, 0u);
     }
-    float w[kU][E], b[kU][E];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const size_t i = i0 + u * stride;
-      const size_t row = i < nvec ? i / cpr : 0;  // (token, head, rank) row
-      const int n0 = (int)(i % cpr) * E;
-      const int r = (int)(row % a.R), h = (int)((row / a.R) % a.H);
-      const float4* wp = reinterpret_cast<const float4*>(wbase + (size_t)h * a.N + n0);
-      const float4* bp = reinterpret_cast<const float4*>(bbase + ((size_t)h * a.R + r) * a.N + n0);
-#pragma unroll
-      for (int q = 0; q < E / 4; ++q) {
-        const float4 wv = wp[q], bv = bp[q];
-        w[u][4 * q] = wv.x; w[u][4 * q + 1] = wv.y; w[u][4 * q + 2] = wv.z; w[u][4 * q + 3] = wv.w;
-        b[u][4 * q] = bv.x; b[u][4 * q + 1] = bv.y; b[u][4 * q + 2] = bv.z; b[u][4 * q + 3] = bv.w;
-      }
-    }
+    // this thread's (head, rank, piece): vector i is piece i % cpr of rank
+    // (i / cpr) % R of head (i / (cpr R)) % H
+    const size_t m = i0 % ((size_t)a.H * a.R * cpr);
+    const int n0 = (int)(m % cpr) * E, r = (int)((m / cpr) % a.R), h = (int)(m / ((size_t)cpr * a.R));
+    float w[E], b[E];
+    load_w<E>((part == 0 ? a.norm_B : a.norm_C) + (size_t)h * a.N + n0, w);
+    load_w<E>((part == 0 ? a.bias_B : a.bias_C) + ((size_t)h * a.R + r) * a.N + n0, b);
     float v[kU][E], ss[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -115,12 +118,13 @@ __global__ void __launch_bounds__(kBlkThreads) prepass_kernel(BlockArgs a) {
       if (i < nvec) {
         const float scale = 1.f / sqrtf(ss[u] / (float)a.N + a.eps);
 #pragma unroll
-        for (int e = 0; e < E; ++e) v[u][e] = __builtin_fmaf(v[u][e] * scale, w[u][e], b[u][e]);
+        for (int e = 0; e < E; ++e) v[u][e] = __builtin_fmaf(v[u][e] * scale, w[e], b[e]);
         dst[i] = pack16(v[u], (const T*)nullptr);
       }
     }
   } else {
     // up-projection of 16-byte pieces of x into R pieces of X
+    constexpr int kRMax = 4;
     const int cpr = a.P / E;
     const size_t nvec = a.rows * (size_t)cpr;
     const uint4* src = static_cast<const uint4*>(a.x);
@@ -131,83 +135,100 @@ __global__ void __launch_bounds__(kBlkThreads) prepass_kernel(BlockArgs a) {
       const size_t i = i0 + u * stride;
       raw[u] = i < nvec ? src[i] : make_uint4(0u, 0u, 0u, 0u);
     }
+    const size_t m = i0 % ((size_t)a.H * cpr);
+    const int c = (int)(m % cpr), p0 = c * E, h = (int)(m / cpr);
+    float up[kRMax][E];
+#pragma unroll
+    for (int r = 0; r < kRMax; ++r)
+      if (r < a.R) load_w<E>(a.up + ((size_t)h * a.R + r) * a.P + p0, up[r]);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const size_t i = i0 + u * stride;
       if (i >= nvec) break;
       const size_t row = i / cpr;  // (token, head)
-      const int p0 = (int)(i % cpr) * E;
-      const int h = (int)(row % a.H);
       float v[E];
       unpack16(raw[u], v, (const T*)nullptr);
-      for (int r = 0; r < a.R; ++r) {
-        const float4* up = reinterpret_cast<const float4*>(a.up + ((size_t)h * a.R + r) * a.P + p0);
+#pragma unroll
+      for (int r = 0; r < kRMax; ++r) {
+        if (r >= a.R) break;
         float o[E];
 #pragma unroll
-        for (int q = 0; q < E / 4; ++q) {
-          const float4 uv = up[q];
-          o[4 * q] = v[4 * q] * uv.x;
-          o[4 * q + 1] = v[4 * q + 1] * uv.y;
-          o[4 * q + 2] = v[4 * q + 2] * uv.z;
-          o[4 * q + 3] = v[4 * q + 3] * uv.w;
-        }
-        dst[(row * a.R + r) * cpr + (i % cpr)] = pack16(o, (const T*)nullptr);
+        for (int e = 0; e < E; ++e) o[e] = v[e] * up[r][e];
+        dst[(row * a.R + r) * cpr + c] = pack16(o, (const T*)nullptr);
       }
     }
   }
 }
 
-template <typename T>
+// The post-pass reads R pieces per output piece: R is a template argument
+// (registers), and with R = 4 a thread takes half as many pieces.
+template <int R>
+constexpr int post_pieces() {
+  return R == 4 ? kU / 2 : kU;
+}
+
+template <typename T, int R>
 __global__ void __launch_bounds__(kBlkThreads) postpass_kernel(BlockArgs a) {
   constexpr int E = Vec16<T>::E;
-  constexpr int kRMax = 4;
+  constexpr int U = post_pieces<R>();
   const size_t stride = (size_t)gridDim.x * kBlkThreads;
   const size_t i0 = (size_t)blockIdx.x * kBlkThreads + threadIdx.x;
   const int cpr = a.P / E;
   const size_t nvec = a.rows * (size_t)cpr;
   const uint4* src = static_cast<const uint4*>(a.y);
-  uint4 raw[kU][kRMax];
+  uint4 raw[U][R];
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
+  for (int u = 0; u < U; ++u) {
     const size_t i = i0 + u * stride;
     const size_t row = i / cpr;
 #pragma unroll
-    for (int r = 0; r < kRMax; ++r)
-      raw[u][r] = (i < nvec && r < a.R) ? src[(row * a.R + r) * cpr + (i % cpr)]
-                                        : make_uint4(0u, 0u, 0u, 0u);
+    for (int r = 0; r < R; ++r)
+      raw[u][r] = i < nvec ? src[(row * R + r) * cpr + (i % cpr)] : make_uint4(0u, 0u, 0u, 0u);
   }
+  const size_t m = i0 % ((size_t)a.H * cpr);
+  const int p0 = (int)(m % cpr) * E, h = (int)(m / cpr);
+  float dw[R][E];
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
+  for (int r = 0; r < R; ++r) load_w<E>(a.down + ((size_t)h * R + r) * a.P + p0, dw[r]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
     const size_t i = i0 + u * stride;
     if (i >= nvec) break;
-    const size_t row = i / cpr;  // (token, head)
-    const int p0 = (int)(i % cpr) * E;
-    const int h = (int)(row % a.H);
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int r = 0; r < kRMax; ++r) {
-      if (r >= a.R) break;
+    for (int r = 0; r < R; ++r) {
       float v[E];
       unpack16(raw[u][r], v, (const T*)nullptr);
-      const float4* d = reinterpret_cast<const float4*>(a.down + ((size_t)h * a.R + r) * a.P + p0);
 #pragma unroll
-      for (int q = 0; q < E / 4; ++q) {
-        const float4 dv = d[q];
-        acc[4 * q] = __builtin_fmaf(v[4 * q], dv.x, acc[4 * q]);
-        acc[4 * q + 1] = __builtin_fmaf(v[4 * q + 1], dv.y, acc[4 * q + 1]);
-        acc[4 * q + 2] = __builtin_fmaf(v[4 * q + 2], dv.z, acc[4 * q + 2]);
-        acc[4 * q + 3] = __builtin_fmaf(v[4 * q + 3], dv.w, acc[4 * q + 3]);
-      }
+      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(v[e], dw[r][e], acc[e]);
     }
     static_cast<uint4*>(a.y_out)[i] = pack16(acc, (const T*)nullptr);
   }
 }
 
-dim3 grid_for(size_t nvec, unsigned parts) {
-  const size_t per_block = (size_t)kBlkThreads * kU;
-  return dim3((unsigned)((nvec + per_block - 1) / per_block), parts);
+size_t gcd_sz(size_t x, size_t y) {
+  while (y) {
+    const size_t t = x % y;
+    x = y;
+    y = t;
+  }
+  return x;
+}
+
+// Blocks for nvec vectors, u per thread, rounded up so that the grid's
+// thread count is a multiple of every period in `periods` (see kU).
+dim3 grid_for(size_t nvec, int u, unsigned parts, std::initializer_list<size_t> periods) {
+  size_t q = 1;  // blocks must be a multiple of q
+  for (size_t M : periods) {
+    const size_t need = M / gcd_sz(M, kBlkThreads);
+    q = q / gcd_sz(q, need) * need;
+  }
+  const size_t per_block = (size_t)kBlkThreads * u;
+  size_t blocks = (nvec + per_block - 1) / per_block;
+  blocks = (blocks + q - 1) / q * q;
+  return dim3((unsigned)blocks, parts);
 }
 
 }  // namespace
@@ -216,7 +237,9 @@ hipError_t launch_block_prepass(const BlockArgs& a, m3_dtype dtype, hipStream_t 
   if (a.rows == 0) return hipSuccess;
   const size_t es = dtype == M3_BF16 ? 2 : 4, E = 16 / es;
   const size_t nbc = a.rows * a.R * (a.N / E), nx = a.rows * (a.P / E);
-  const dim3 grid = grid_for(nbc > nx ? nbc : nx, 3);
+  const dim3 grid = grid_for(nbc > nx ? nbc : nx, kU, 3,
+                             {(size_t)a.H * a.R * (a.N / E), (size_t)a.H * (a.P / E)});
+  if (grid.x > 0x7fffffffu) return hipErrorInvalidValue;
   if (dtype == M3_BF16)
     hipLaunchKernelGGL(prepass_kernel<bf16>, grid, dim3(kBlkThreads), 0, stream, a);
   else
@@ -224,15 +247,28 @@ hipError_t launch_block_prepass(const BlockArgs& a, m3_dtype dtype, hipStream_t 
   return hipGetLastError();
 }
 
+template <typename T, int R>
+hipError_t launch_post(const BlockArgs& a, hipStream_t stream) {
+  constexpr size_t E = Vec16<T>::E;
+  const dim3 grid = grid_for(a.rows * (a.P / E), post_pieces<R>(), 1, {(size_t)a.H * (a.P / E)});
+  if (grid.x > 0x7fffffffu) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((postpass_kernel<T, R>), grid, dim3(kBlkThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_post_t(const BlockArgs& a, hipStream_t stream) {
+  switch (a.R) {
+    case 1: return launch_post<T, 1>(a, stream);
+    case 2: return launch_post<T, 2>(a, stream);
+    case 4: return launch_post<T, 4>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_block_postpass(const BlockArgs& a, m3_dtype dtype, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
-  const size_t es = dtype == M3_BF16 ? 2 : 4, E = 16 / es;
-  const dim3 grid = grid_for(a.rows * (a.P / E), 1);
-  if (dtype == M3_BF16)
-    hipLaunchKernelGGL(postpass_kernel<bf16>, grid, dim3(kBlkThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(postpass_kernel<float>, grid, dim3(kBlkThreads), 0, stream, a);
-  return hipGetLastError();
+  return dtype == M3_BF16 ? launch_post_t<bf16>(a, stream) : launch_post_t<float>(a, stream);
 }
 
 }  // namespace m3
