@@ -402,11 +402,21 @@ def cpu_baseline(cfg, inp, budget_s=20.0):
                        inp["C"], units=list(range(n2)), nthreads=cores)
         dt = time.perf_counter() - t0
         n = n2
+    # the whole workload fits the budget: repeat it so the time is not a
+    # single short measurement
+    reps = 1
+    if n == nunits and dt < budget_s / 2:
+        reps = max(1, min(100, int(budget_s / 2 / max(dt, 1e-6))))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.prefill(inp["x"], inp["dt"], inp["A"], inp["lam"], inp["theta"], inp["B"],
+                           inp["C"], units=list(range(n)), nthreads=cores)
+        dt = (time.perf_counter() - t0) / reps
     full_time = dt * nunits / n
     return {"value": cfg.batch * cfg.seqlen / full_time, "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
-            "sample": "%d of %d (batch, head) units over all %d tokens, fp64 C oracle, %.1f s"
-                      % (n, nunits, cfg.seqlen, dt)}
+            "sample": "%d of %d (batch, head) units over all %d tokens, fp64 C oracle, "
+                      "%d run(s) of %.2f s" % (n, nunits, cfg.seqlen, reps, dt)}
 
 
 def counter_sequence():
