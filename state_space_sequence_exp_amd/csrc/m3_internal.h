@@ -139,6 +139,8 @@ struct PrefillLayout {
   uint32_t off_BwT;    // [N][KM]   B~ weighted by each token's state weight, transposed
   uint32_t off_XT;     // [P][KM]   x transposed
   uint32_t off_GT;     // [P][N]    chunk entry state, transposed
+  uint32_t off_hand;   // N P floats: the entry state handed between wave layouts (N = 64
+                       // fixed, P <= 64, R = 1), else empty
   uint32_t total;
 };
 
@@ -177,6 +179,8 @@ __host__ __device__ inline PrefillLayout prefill_layout(int L, int R, int N, int
   c.off_BwT = o; o += (uint32_t)N * c.KM * esize;
   c.off_XT = o; o += (uint32_t)P * c.KM * esize;
   c.off_GT = o; o += (uint32_t)P * N * esize;
+  c.off_hand = o;
+  if (fixed && N == 64 && P <= 64 && R == 1) o += (uint32_t)N * P * 4;
   c.total = o;
   return c;
 }

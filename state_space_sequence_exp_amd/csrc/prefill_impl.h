@@ -155,6 +155,10 @@ struct Cfg {
   static constexpr int KR = S * R_;                      // chunk rows per item
   static constexpr int PW = es / 2;                      // 32-bit words per pair
   static constexpr int NPT = P_ / 16;                    // p-tiles
+  // N = 64 fixed, P <= 64, R = 1: at most four output units, so the output
+  // pass keeps the state tiles on the other four waves only, and the state
+  // update runs beside the outputs (the local pass spreads them over all)
+  static constexpr bool kSplit3 = N_ == 64 && P_ <= 64 && R_ == 1 && kPrefillThreads == 512;
   // N fixed with N / 2 pairs dividing the wave: wave w holds token blocks
   // w * 128 / N .. (w + 1) * 128 / N - 1 of every pair, and the angle sums
   // before a block are the wave totals of the waves before it plus, with two
@@ -555,27 +559,28 @@ __device__ __forceinline__ void state_to_lds(const PrefillArgs& a, const WaveRol
   }
 }
 
-// Compile-time view of a wave's state tiles when N is fixed: with the tile
-// count a multiple of the wave count every wave holds exactly kTPW tiles and
-// no per-tile conditions are needed.
-template <class C>
+// Compile-time view of a wave's state tiles when N is fixed and the tiles
+// sit on the last NSW waves: with the tile count a multiple of NSW every state
+// wave holds exactly kTPW tiles and no per-tile conditions are needed.
+template <class C, int NSW = kW>
 struct StateTiles {
   static constexpr int kNT = C::NC ? (C::NC / 16) * C::NPT : 0;
-  static constexpr bool kFull = kNT != 0 && kNT % kW == 0 && kNT / kW <= kMaxStTiles;
-  static constexpr int kTPW = kFull ? kNT / kW : kMaxStTiles;
+  static constexpr bool kFull = kNT != 0 && kNT % NSW == 0 && kNT / NSW <= kMaxStTiles;
+  static constexpr int kTPW = kFull ? kNT / NSW : kMaxStTiles;
+  static constexpr int kFirst = kW - NSW;  // first state wave
 };
 
 // Chunk state S_c = sum_u w_u B~_u x_u^T (MFMA, both operands read straight
 // from the K-major tiles) folded into this wave's state tiles: st <- R(Phi_c)
-// (d st + S_c).
-template <class C>
+// (d st + S_c).  The tiles sit on the last NSW waves (wr says the same).
+template <class C, int NSW = kW>
 __device__ __forceinline__ void state_update(const PrefillArgs& a, const PrefillLayout& lay,
                                              const WaveRoles& wr, float d,
                                              f32x4 (&stt)[kMaxStTiles], const Tile& tW,
                                              const Tile& tX, const unsigned char* smem) {
   using T = typename C::T;
   using M = typename C::M;
-  using ST = StateTiles<C>;
+  using ST = StateTiles<C, NSW>;
   constexpr int TPW = ST::kTPW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
@@ -588,7 +593,7 @@ __device__ __forceinline__ void state_update(const PrefillArgs& a, const Prefill
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
     acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    tile[m] = ST::kFull ? wave + m * kW : state_tile(wr, wave, m, ntiles);
+    tile[m] = ST::kFull ? wave - ST::kFirst + m * NSW : state_tile(wr, wave, m, ntiles);
     const int i = tile[m] < 0 ? 0 : tile[m];
     nrow[m] = (uint32_t)((i % ntn) * 16 + li);
     prow[m] = (uint32_t)((i / ntn) * 16 + li);
@@ -1387,8 +1392,30 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
       }
     }
   }
+  // the output pass's state distribution (see Cfg::kSplit3): the entry
+  // state moves to its waves through LDS
+  WaveRoles wr3 = wr;
+  if constexpr (C::kSplit3) {
+    wr3.sw0 = kW / 2;
+    wr3.nsw = kW / 2;
+    float* s_hand = reinterpret_cast<float*>(smem + lay.off_hand);
 #pragma unroll
-  for (int q = 0; q < kMaxStTiles; ++q) stt[q] = ent[q];
+    for (int q = 0; q < kMaxStTiles; ++q) {
+      const int i = state_tile(wr, wave, q, ntiles);
+      if (i >= 0) *reinterpret_cast<f32x4*>(s_hand + (i * 64 + lane) * 4) = ent[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kMaxStTiles; ++q) {
+      const int i = state_tile(wr3, wave, q, ntiles);
+      stt[q] = i >= 0 ? *reinterpret_cast<const f32x4*>(s_hand + (i * 64 + lane) * 4)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kMaxStTiles; ++q) stt[q] = ent[q];
+  }
+  constexpr int NSW3 = C::kSplit3 ? kW / 2 : kW;
 
   // ---- phase 3: outputs from the true entry state -------------------------
   for (int c = s.c0; c < s.c1; ++c) {
@@ -1399,14 +1426,14 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     const double inw = step_partials<C>(a, lay, s, m, c, stg, sc, smem);
     __syncthreads();
     step_rotate<C, true, false>(a, lay, s, m, c, stg, sc, t, inw, smem);
-    state_to_lds<C>(a, wr, stt, t.G);
+    state_to_lds<C>(a, wr3, stt, t.G);
     if (more) issue_loads<C, true>(a, s, m, c + 1, stg);
     __syncthreads();
     chunk_output<C>(a, lay, wr, s, chunk_res<C>(a, s, c), sc, t.C, t.B, t.X, t.G);
     if (more) {
       float wd[3], wl[3];
       if (scal_wave) scalar_loads(a, s, c + 1, wd, wl);
-      state_update<C>(a, lay, wr, __expf(sc[4 * kLMax]), stt, t.W, t.X, smem);
+      state_update<C, NSW3>(a, lay, wr3, __expf(sc[4 * kLMax]), stt, t.W, t.X, smem);
       if (scal_wave)
         chunk_scalars(a, (c + 1) * a.L, min(a.L, a.T - (c + 1) * a.L), s.Ah, wd, wl,
                       s_scal + (buf ^ 1) * (kScalBytes / 4));
