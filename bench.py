@@ -424,7 +424,7 @@ def counter_sequence():
     import torch
     import state_space_sequence_exp_amd as m3
     from state_space_sequence_exp_amd import inputs as I
-    for idx, reps in ((1, 3), (3, 1)):
+    for idx, reps in ((1, 3), (3, 1), (2, 1)):
         cfg = I.CONFIGS[idx]
         g = upload(I.config_inputs(idx))
         for _ in range(reps):
