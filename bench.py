@@ -247,7 +247,7 @@ def backward_bench(steps, log):
     import torch
     import state_space_sequence_exp_amd as m3
     from state_space_sequence_exp_amd import inputs as I
-    cfg = I.CONFIGS[1]
+    cfg = I.WORKLOADS[1]
     inp = I.config_inputs(1)
     g = upload(inp)
     del inp
@@ -425,13 +425,13 @@ def counter_sequence():
     import state_space_sequence_exp_amd as m3
     from state_space_sequence_exp_amd import inputs as I
     for idx, reps in ((1, 3), (3, 1), (2, 1)):
-        cfg = I.CONFIGS[idx]
+        cfg = I.WORKLOADS[idx]
         g = upload(I.config_inputs(idx))
         for _ in range(reps):
             m3.prefill(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"], cfg.chunk)
         torch.cuda.synchronize()
         del g
-    c = I.CONFIGS[4]
+    c = I.WORKLOADS[4]
     g = upload(I.decode_config_inputs(ring=2))
     h = g["h0"].clone()
     for t in range(10):
@@ -468,9 +468,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every (batch, head) unit is independent; sharding is described in DESIGN.md)",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (every "
+              "(batch, head) unit is independent, so a batch or its heads split across GPUs "
+              "with no communication)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -487,7 +487,7 @@ def main():
         return
 
     # ---- headline: SISO prefill (configuration 1) ----
-    cfg = I.CONFIGS[1]
+    cfg = I.WORKLOADS[1]
     log("generating %s" % cfg.name)
     inp = I.config_inputs(1)
     g = upload(inp)
@@ -532,7 +532,7 @@ def main():
     if not args.no_secondary:
         sec = {}
         for idx in (2, 3):
-            c = I.CONFIGS[idx]
+            c = I.WORKLOADS[idx]
             log("generating %s" % c.name)
             ii = I.config_inputs(idx)
             gg = upload(ii)
@@ -549,7 +549,7 @@ def main():
                            "algorithmic_bytes": nb, "chunk": c.chunk}
             del gg
             torch.cuda.empty_cache()
-        c = I.CONFIGS[4]
+        c = I.WORKLOADS[4]
         log("generating %s" % c.name)
         ii = I.decode_config_inputs()
         gg = upload(ii)

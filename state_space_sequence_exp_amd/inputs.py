@@ -60,7 +60,7 @@ class DecodeConfig:
     ring: int       # distinct per-step input sets cycled through
 
 
-CONFIGS = {
+WORKLOADS = {
     0: PrefillConfig("tiny_siso_fp32_b1_h1_t256_n16_p16", 1, 256, 1, 16, 16, 1, "f32", 32),
     1: PrefillConfig("siso_prefill_b4_t2048_h16_n64_p64", 4, 2048, 16, 64, 64, 1, "bf16", 64),
     2: PrefillConfig("mimo_r4_prefill_b4_t4096_h16_n64_p64", 4, 4096, 16, 64, 64, 4, "bf16", 64),
@@ -132,7 +132,7 @@ def prefill_inputs(batch: int, seqlen: int, nheads: int, N: int, P: int, R: int,
 
 def config_inputs(index: int, seed: Optional[int] = None, **overrides) -> Dict[str, np.ndarray]:
     """Inputs of prefill configuration ``index`` (0..3); seed defaults to the index."""
-    cfg = CONFIGS[index]
+    cfg = WORKLOADS[index]
     if not isinstance(cfg, PrefillConfig):
         raise ValueError("configuration %d is not a prefill configuration" % index)
     kw = dict(batch=cfg.batch, seqlen=cfg.seqlen, nheads=cfg.nheads, N=cfg.N, P=cfg.P,
@@ -170,7 +170,7 @@ def decode_inputs(batch: int, nheads: int, N: int, P: int, R: int, dtype: str, r
 
 def decode_config_inputs(seed: Optional[int] = None, batch: Optional[int] = None,
                          ring: Optional[int] = None) -> Dict[str, np.ndarray]:
-    cfg = CONFIGS[4]
+    cfg = WORKLOADS[4]
     return decode_inputs(batch=cfg.batch if batch is None else batch, nheads=cfg.nheads,
                          N=cfg.N, P=cfg.P, R=cfg.R, dtype=cfg.dtype,
                          ring=cfg.ring if ring is None else ring,

@@ -6,7 +6,7 @@ Tolerance: the GPU computes every gradient in float32 from the same stored
 inputs the oracle reads (bfloat16 inputs are upcast exactly), through two
 time recurrences of at most a few thousand float32 steps and per-token sums
 of at most N P terms; rel-L2 over each gradient tensor <= 1e-4, the
-spec float32 bound, for both storage types."""
+float32 parity bound, for both storage types."""
 import numpy as np
 import pytest
 

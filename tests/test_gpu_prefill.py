@@ -38,7 +38,7 @@ def check_prefill(inp, chunk, units=None, label=""):
 
 
 def test_config0_full():
-    cfg = I.CONFIGS[0]
+    cfg = I.WORKLOADS[0]
     check_prefill(I.config_inputs(0), cfg.chunk, label="config0")
 
 
@@ -118,7 +118,7 @@ def test_parity_construction_long():
 def test_full_config_sampled_units(index):
     """Full-size configuration in the launch configuration the benchmark times;
     the oracle checks three (b, h) units over the whole sequence."""
-    cfg = I.CONFIGS[index]
+    cfg = I.WORKLOADS[index]
     inp = I.config_inputs(index)
     nunits = cfg.batch * cfg.nheads
     units = sorted({0, nunits // 2 + 1, nunits - 1})
