@@ -231,15 +231,25 @@ m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in,
  * with G_t = dL/dh_t, G_t = C_t dy_t^T + alpha_{t+1} R_{t+1}^T G_{t+1}, and
  * each token's gradients follow from h_t, h_{t-1} and G_t.
  *
- * The forward states h_t and the adjoint states G_t of every token are
- * materialised in the workspace (m3_backward_workspace_size: 8 N P bytes per
- * token-head plus 4), so the call moves about 5 x 4 N P bytes per
- * token-head through HBM.  dy has x's layout and storage type; dh_final,
- * if given, is [batch, H, N, P] float.  lam and theta are required.  N must
- * be 16, 32, 64, 128 or 256 with N * P <= 8192; P and R as for m3_prefill.
- * x and dy need 16-byte alignment, the other pointers element alignment
- * and the workspace 256 bytes.  With batch * seqlen == 0 only dA is written
- * (zeros).  Four kernel launches.
+ * With N * P <= 4096 the sequence is cut into segments of S tokens (32,
+ * or 16 or 8 where the segment's staged inputs would not fit the LDS): a
+ * local pass walks every segment from a zero state both ways, a chain pass
+ * composes the segments into each one's entry state and exit adjoint, and
+ * a gradient pass recomputes each segment's states in blocks of 8 tokens
+ * on chip and walks them backward.  The workspace holds two N x P float
+ * states per segment-head, plus per segment a decay and N/2 angles, plus
+ * 4 bytes per token-head (each area rounded up to 256 bytes).  Four kernel
+ * launches.
+ * With N * P = 8192 the states h_t and G_t of every token are materialised
+ * in the workspace instead (8 N P bytes per token-head plus 4), so the call
+ * moves about 5 x 4 N P bytes per token-head through HBM.  Four kernel
+ * launches.
+ * m3_backward_workspace_size gives the bytes for either case.  dy has x's
+ * layout and storage type; dh_final, if given, is [batch, H, N, P] float.
+ * lam and theta are required.  N must be 16, 32, 64, 128 or 256 with
+ * N * P <= 8192; P and R as for m3_prefill.  x and dy need 16-byte
+ * alignment, the other pointers element alignment and the workspace 256
+ * bytes.  With batch * seqlen == 0 only dA is written (zeros).
  */
 size_t m3_backward_workspace_size(const m3_dims* dims, m3_dtype dtype);
 

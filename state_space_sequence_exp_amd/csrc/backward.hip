@@ -19,14 +19,16 @@
 //   d gamma_t = <G_t, P_t>,  d beta_t = <dU_t, P_{t-1}>
 // and the chain rule through alpha, beta, gamma, psi to dt, lam, theta, A.
 //
-// The kernels materialise the states: fwd_states_kernel stores every h_t
-// and adj_states_kernel every G_t (one lane per (row pair, column), a time
-// loop each way, inputs staged kAhead tokens ahead); token_grads_kernel
-// then forms every token's gradients in parallel from h_t, h_{t-1} and G_t,
-// a few consecutive tokens per workgroup
-// (dU_{t+1} = G_t - sum_r C dy^T, so G_{t+1} is not read); dA_kernel sums
-// dA over (batch, time) per head.  Every reduction has a fixed order, so the
-// results are bitwise repeatable.
+// Two paths, every reduction in a fixed order (results bitwise repeatable):
+// - N P <= 4096: checkpointed segments (seg_local_kernel, seg_chain_kernel,
+//   seg_grads_kernel below); no per-token state reaches memory.
+// - otherwise the states are materialised: fwd_states_kernel stores every
+//   h_t and adj_states_kernel every G_t (one lane per (row pair, column), a
+//   time loop each way, inputs staged kAhead tokens ahead); token_grads_kernel
+//   then forms every token's gradients in parallel from h_t, h_{t-1} and G_t,
+//   a few consecutive tokens per workgroup (dU_{t+1} = G_t - sum_r C dy^T, so
+//   G_{t+1} is not read).
+// dA_kernel sums dA over (batch, time) per head.
 #include "m3_device.h"
 #include "m3_internal.h"
 
@@ -463,6 +465,559 @@ __global__ void __launch_bounds__(512) token_grads_kernel(BackwardArgs a) {
   }
 }
 
+// ---- checkpointed segments -------------------------------------------------
+//
+// Shapes with N P <= 4096 take segments of S tokens and never store a
+// per-token state.  seg_local_kernel walks each segment from zero both ways
+// and seg_chain_kernel chains the segments, giving every segment's entry
+// state and exit adjoint.  seg_grads_kernel then takes one workgroup per
+// (batch, head, segment), thread (kp, q) holding rows 2kp, 2kp+1 and
+// columns 4q .. 4q+3 of h and G.  From the entry state it walks the segment
+// forward,
+// keeping each kBwSub-token block's entry state in its own LDS slots; then,
+// block by block from the last, it recomputes the block's states into
+// registers and walks it backward from the segment-exit adjoint, forming
+// every token's gradients as token_grads_kernel does.  Sums over columns
+// run in DPP steps within the row pair's lanes, sums over row pairs across
+// lanes and then waves through LDS, all in a fixed order.
+
+// Two consecutive elements (a B or C pair) and four (an x or dy quad) of a
+// staged row, as float.
+template <typename T>
+__device__ __forceinline__ void lds_pair(const unsigned char* p, float& a0, float& a1) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    a0 = __uint_as_float(w << 16);
+    a1 = __uint_as_float(w & 0xffff0000u);
+  } else {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    a0 = v.x;
+    a1 = v.y;
+  }
+}
+template <typename T>
+__device__ __forceinline__ void lds_quad(const unsigned char* p, float (&v)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(w.x << 16);
+    v[1] = __uint_as_float(w.x & 0xffff0000u);
+    v[2] = __uint_as_float(w.y << 16);
+    v[3] = __uint_as_float(w.y & 0xffff0000u);
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(p);
+    v[0] = f.x;
+    v[1] = f.y;
+    v[2] = f.z;
+    v[3] = f.w;
+  }
+}
+
+// Sum over each aligned group of gw consecutive lanes (gw = 4, 8, 16 or 32),
+// complete in the group's last lane: shifts within rows of 16, then row 0's
+// (row 2's) last lane added into row 1 (row 3).
+template <int gw>
+__device__ __forceinline__ float group_sum_last(float v) {
+  v += dpp_move<0x111>(v);  // row_shr:1
+  v += dpp_move<0x112>(v);  // row_shr:2
+  if constexpr (gw >= 8) v += dpp_move<0x114>(v);   // row_shr:4
+  if constexpr (gw >= 16) v += dpp_move<0x118>(v);  // row_shr:8
+  if constexpr (gw >= 32) v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  return v;
+}
+
+// Sum over the lanes of a wave that share l mod gw, in every lane: rotations
+// within rows, then the partner row and the partner half (v_permlane16_swap
+// and v_permlane32_swap with both operands the value give the lower and the
+// upper partner's value, so both add in the same order).  `full`: all 64
+// lanes active.
+template <int gw>
+__device__ __forceinline__ float cross_group_sum(float v, bool full) {
+  if constexpr (gw <= 8) v += dpp_move<0x128>(v);  // row_ror:8
+  if constexpr (gw <= 4) v += dpp_move<0x124>(v);  // row_ror:4
+  if constexpr (gw <= 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if (full) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return v;
+}
+
+// The inputs of tokens t0 - 1 .. t0 + S of one (batch, head) sequence into
+// LDS as stored (zeros outside the sequence).
+template <typename T>
+__device__ __forceinline__ void stage_segment(const BackwardArgs& a, const BwSegLayout& L,
+                                              unsigned char* sm, int t0, size_t tok_base, int hh,
+                                              int tid, int nt) {
+  {
+    const uint32_t* gB = static_cast<const uint32_t*>(a.B);
+    const uint32_t* gC = static_cast<const uint32_t*>(a.C);
+    uint32_t* dB = reinterpret_cast<uint32_t*>(sm + L.oB);
+    uint32_t* dC = reinterpret_cast<uint32_t*>(sm + L.oC);
+    for (int i = tid; i < L.nslot * (int)L.wB; i += nt) {
+      const int sl = i / (int)L.wB, w = i - sl * (int)L.wB, t = t0 - 1 + sl;
+      uint32_t vb = 0u, vc = 0u;
+      if (t >= 0 && t < a.T) {
+        const size_t o = ((tok_base + t) * a.H + hh) * L.wB + w;
+        vb = gB[o];
+        vc = gC[o];
+      }
+      dB[i] = vb;
+      dC[i] = vc;
+    }
+    const int qX = (int)L.wX / 4;  // 16-byte pieces per row
+    const uint4* gX = static_cast<const uint4*>(a.x);
+    const uint4* gD = static_cast<const uint4*>(a.dy);
+    uint4* dX = reinterpret_cast<uint4*>(sm + L.oX);
+    uint4* dD = reinterpret_cast<uint4*>(sm + L.oDY);
+    for (int i = tid; i < L.nslot * qX; i += nt) {
+      const int sl = i / qX, w = i - sl * qX, t = t0 - 1 + sl;
+      uint4 vx = {0u, 0u, 0u, 0u}, vd = {0u, 0u, 0u, 0u};
+      if (t >= 0 && t < a.T) {
+        const size_t o = ((tok_base + t) * a.H + hh) * qX + w;
+        vx = gX[o];
+        vd = gD[o];
+      }
+      dX[i] = vx;
+      dD[i] = vd;
+    }
+    const int nkp = a.N / 2;
+    float* dTh = reinterpret_cast<float*>(sm + L.oTh);
+    for (int i = tid; i < L.nslot * nkp; i += nt) {
+      const int sl = i / nkp, k = i - sl * nkp, t = t0 - 1 + sl;
+      dTh[i] = (t >= 0 && t < a.T) ? a.theta[((tok_base + t) * a.H + hh) * nkp + k] : 0.f;
+    }
+    float* dDt = reinterpret_cast<float*>(sm + L.oDt);
+    float* dLam = reinterpret_cast<float*>(sm + L.oLam);
+    for (int i = tid; i < L.nslot; i += nt) {
+      const int t = t0 - 1 + i;
+      const bool in = t >= 0 && t < a.T;
+      dDt[i] = in ? a.dt[(tok_base + t) * a.H + hh] : 0.f;
+      dLam[i] = in ? a.lam[(tok_base + t) * a.H + hh] : 0.f;
+    }
+  }
+}
+
+template <typename T, int R, int P>
+struct SegCtx {
+  const unsigned char *sB, *sC, *sX, *sDY;
+  const float *sTh, *sDt, *sLam;
+  uint32_t rowB, rowX;  // staged bytes per token slot
+  uint32_t offB, offX;  // this thread's pair / quad within a rank's row
+  int N, kp;
+  float Ah;
+
+  __device__ void pair(const unsigned char* base, int slot, int r, float& b0, float& b1) const {
+    lds_pair<T>(base + slot * rowB + (uint32_t)(r * N) * sizeof(T) + offB, b0, b1);
+  }
+  __device__ void quad(const unsigned char* base, int slot, int r, float (&v)[4]) const {
+    lds_quad<T>(base + slot * rowX + (uint32_t)(r * P) * sizeof(T) + offX, v);
+  }
+  // sum_r B_r x_r^T (or C dy^T) over this thread's rows and columns
+  __device__ void outer(const unsigned char* bb, const unsigned char* xb, int slot,
+                        float (&o)[2][4]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[0][j] = o[1][j] = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float b0, b1, xv[4];
+      pair(bb, slot, r, b0, b1);
+      quad(xb, slot, r, xv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[0][j] = __builtin_fmaf(b0, xv[j], o[0][j]);
+        o[1][j] = __builtin_fmaf(b1, xv[j], o[1][j]);
+      }
+    }
+  }
+  // h_t from h_{t-1} (in place); pq: P_{t-1} in, P_t out
+  __device__ void step(int slot, float (&h)[2][4], float (&pq)[2][4]) const {
+    const float d = sDt[slot], l = sLam[slot];
+    const float alpha = __expf(d * Ah), beta = (1.f - l) * d, gamma = l * d;
+    float sn, cn;
+    sincos_step(d * sTh[slot * (N / 2) + kp], sn, cn);
+    float pc[2][4];
+    outer(sB, sX, slot, pc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float u0 = __builtin_fmaf(beta, pq[0][j], h[0][j]);
+      const float u1 = __builtin_fmaf(beta, pq[1][j], h[1][j]);
+      h[0][j] = __builtin_fmaf(alpha, cn * u0 - sn * u1, gamma * pc[0][j]);
+      h[1][j] = __builtin_fmaf(alpha, sn * u0 + cn * u1, gamma * pc[1][j]);
+      pq[0][j] = pc[0][j];
+      pq[1][j] = pc[1][j];
+    }
+  }
+};
+
+template <typename T, int R, int P>
+__global__ void __launch_bounds__(kBwMaxThreads) seg_grads_kernel(BackwardArgs a, int nseg) {
+  extern __shared__ __align__(16) unsigned char sm[];
+  constexpr int es = sizeof(T);
+  constexpr int gw = P / 4;  // lanes per row pair
+  const int S = a.S, NSUB = S / kBwSub;
+  const int nt = blockDim.x, tid = threadIdx.x;
+  const int kp = tid / gw, q = tid - kp * gw;
+  const int unit = blockIdx.x / nseg, seg = blockIdx.x - unit * nseg;
+  const int bidx = unit / a.H, hh = unit - bidx * a.H;
+  const int t0 = seg * S;
+  const BwSegLayout L = bw_seg_layout(S, R, a.N, P, es);
+  const size_t NP = (size_t)a.N * a.P;
+  const size_t tok_base = (size_t)bidx * a.T;  // (batch, token) row of token 0
+
+  stage_segment<T>(a, L, sm, t0, tok_base, hh, tid, nt);
+  __syncthreads();
+
+  SegCtx<T, R, P> c;
+  c.sB = sm + L.oB;
+  c.sC = sm + L.oC;
+  c.sX = sm + L.oX;
+  c.sDY = sm + L.oDY;
+  c.sTh = reinterpret_cast<const float*>(sm + L.oTh);
+  c.sDt = reinterpret_cast<const float*>(sm + L.oDt);
+  c.sLam = reinterpret_cast<const float*>(sm + L.oLam);
+  c.rowB = L.wB * 4;
+  c.rowX = L.wX * 4;
+  c.offB = (uint32_t)(2 * kp) * es;
+  c.offX = (uint32_t)(4 * q) * es;
+  c.N = a.N;
+  c.kp = kp;
+  c.Ah = a.A[hh];
+  float* sDx = reinterpret_cast<float*>(sm + L.oDx);
+  float* sSc = reinterpret_cast<float*>(sm + L.oSc);
+  float* sHs = reinterpret_cast<float*>(sm + L.oHs);
+  float* sdB = reinterpret_cast<float*>(sm + L.odB);
+  float* sdC = reinterpret_cast<float*>(sm + L.odC);
+  float* sdTh = reinterpret_cast<float*>(sm + L.odTh);
+  float* sNull = reinterpret_cast<float*>(sm + L.oNull) + (tid & 63) * 4;
+  const size_t el0 = (size_t)(2 * kp) * P + 4 * q;  // this thread's first element
+
+  // ---- forward walk: block-entry states ----------------------------------------
+  float h[2][4], pq[2][4];
+  if (seg == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h[0][j] = h[1][j] = 0.f;
+  } else {
+    const float* hk = a.hs + ((size_t)unit * nseg + seg) * NP + el0;
+    const float4 r0 = *reinterpret_cast<const float4*>(hk);
+    const float4 r1 = *reinterpret_cast<const float4*>(hk + P);
+    h[0][0] = r0.x; h[0][1] = r0.y; h[0][2] = r0.z; h[0][3] = r0.w;
+    h[1][0] = r1.x; h[1][1] = r1.y; h[1][2] = r1.z; h[1][3] = r1.w;
+  }
+  c.outer(c.sB, c.sX, 0, pq);  // P of token t0 - 1
+#pragma nounroll
+  for (int sb = 0; sb < NSUB; ++sb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sHs[(sb * 8 + e) * nt + tid] = h[e >> 2][e & 3];
+#pragma unroll
+    for (int i = 0; i < kBwSub; ++i) c.step(sb * kBwSub + i + 1, h, pq);
+  }
+
+  // ---- backward, block by block --------------------------------------------------
+  float e[2][4];  // dU_{t+1} (dh_final, or zero, after the last token)
+  {
+    const float* ek = a.gs + ((size_t)unit * nseg + seg) * NP + el0;
+    const float4 r0 = *reinterpret_cast<const float4*>(ek);
+    const float4 r1 = *reinterpret_cast<const float4*>(ek + P);
+    e[0][0] = r0.x; e[0][1] = r0.y; e[0][2] = r0.z; e[0][3] = r0.w;
+    e[1][0] = r1.x; e[1][1] = r1.y; e[1][2] = r1.z; e[1][3] = r1.w;
+  }
+  const int nw = (nt + 63) >> 6, wave = tid >> 6;
+  const bool full = nt >= 64;
+  constexpr bool kFull = P >= 32;  // N >= 16: at least 64 threads
+  constexpr int RP = R * P;
+#pragma nounroll
+  for (int sb = NSUB - 1; sb >= 0; --sb) {
+    const int k0 = t0 + sb * kBwSub;
+    float hist[kBwSub + 1][2][4];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) hist[0][v >> 2][v & 3] = sHs[(sb * 8 + v) * nt + tid];
+    c.outer(c.sB, c.sX, sb * kBwSub, pq);
+#pragma unroll
+    for (int i = 0; i < kBwSub; ++i) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) hist[i + 1][v >> 2][v & 3] = hist[i][v >> 2][v & 3];
+      c.step(sb * kBwSub + i + 1, hist[i + 1], pq);
+    }
+#pragma unroll
+    for (int i = kBwSub - 1; i >= 0; --i) {
+      const int sl = sb * kBwSub + i + 1, t = k0 + i;
+      const bool valid = t < a.T, last = t >= a.T - 1;
+      const float d = c.sDt[sl], l = c.sLam[sl];
+      const float alpha = __expf(d * c.Ah), beta = (1.f - l) * d, gamma = l * d;
+      const float beta_n = (1.f - c.sLam[sl + 1]) * c.sDt[sl + 1];  // zero past the end
+      const float th = c.sTh[sl * (a.N / 2) + kp];
+      float sn, cn;
+      sincos_step(d * th, sn, cn);
+      float pc[2][4], pp[2][4], cd[2][4];
+      c.outer(c.sB, c.sX, sl, pc);
+      c.outer(c.sB, c.sX, sl - 1, pp);
+      c.outer(c.sC, c.sDY, sl, cd);
+      float s_alpha = 0.f, s_gamma = 0.f, s_beta = 0.f, s_psi = 0.f;
+      float dp[2][4], en[2][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float g0 = cd[0][j] + e[0][j], g1 = cd[1][j] + e[1][j];
+        const float u0 = __builtin_fmaf(beta, pp[0][j], hist[i][0][j]);
+        const float u1 = __builtin_fmaf(beta, pp[1][j], hist[i][1][j]);
+        const float v0 = cn * u0 - sn * u1, v1 = sn * u0 + cn * u1;  // R U
+        s_alpha += g0 * v0 + g1 * v1;
+        s_psi += g1 * v0 - g0 * v1;
+        const float du0 = alpha * (cn * g0 + sn * g1), du1 = alpha * (cn * g1 - sn * g0);
+        s_gamma += g0 * pc[0][j] + g1 * pc[1][j];
+        s_beta += du0 * pp[0][j] + du1 * pp[1][j];
+        // dP_t = gamma G_t + beta_{t+1} dU_{t+1} (no dU_{t+1} after the last token)
+        const float un0 = last ? 0.f : e[0][j], un1 = last ? 0.f : e[1][j];
+        dp[0][j] = __builtin_fmaf(beta_n, un0, gamma * g0);
+        dp[1][j] = __builtin_fmaf(beta_n, un1, gamma * g1);
+        en[0][j] = du0;
+        en[1][j] = du1;
+      }
+      // sums over the row pair's columns, complete in its last lane
+      s_psi = group_sum_last<gw>(s_psi);
+      s_alpha = group_sum_last<gw>(s_alpha);
+      s_gamma = group_sum_last<gw>(s_gamma);
+      s_beta = group_sum_last<gw>(s_beta);
+      // the row pair's last lane stores its sums (the others into their null
+      // slots, so no branch splits the step)
+      const bool lead = q == gw - 1;
+      *reinterpret_cast<float4*>(lead ? sSc + ((size_t)kp * kBwSub + i) * 4 : sNull) =
+          float4{s_alpha, s_gamma, s_beta, alpha * s_psi * th};
+      *(lead ? sdTh + i * (a.N / 2) + kp : sNull) = alpha * s_psi * d;
+      // per rank: dB = dP x, dC = h_t dy (sums over columns), dx = dP^T B
+      // (sums over the wave's row pairs here, over waves after the block)
+#pragma nounroll
+      for (int r = 0; r < R; ++r) {
+        float xv[4], dyv[4], b0, b1;
+        c.quad(c.sX, sl, r, xv);
+        c.quad(c.sDY, sl, r, dyv);
+        c.pair(c.sB, sl, r, b0, b1);
+        float dB0 = 0.f, dB1 = 0.f, dC0 = 0.f, dC1 = 0.f, dxr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dB0 = __builtin_fmaf(dp[0][j], xv[j], dB0);
+          dB1 = __builtin_fmaf(dp[1][j], xv[j], dB1);
+          dC0 = __builtin_fmaf(hist[i + 1][0][j], dyv[j], dC0);
+          dC1 = __builtin_fmaf(hist[i + 1][1][j], dyv[j], dC1);
+          dxr[j] = cross_group_sum<gw>(dp[0][j] * b0 + dp[1][j] * b1, kFull || full);
+        }
+        dB0 = group_sum_last<gw>(dB0);
+        dB1 = group_sum_last<gw>(dB1);
+        dC0 = group_sum_last<gw>(dC0);
+        dC1 = group_sum_last<gw>(dC1);
+        const int o = (i * R + r) * a.N + 2 * kp;
+        *reinterpret_cast<float2*>(lead ? sdB + o : sNull) = float2{dB0, dB1};
+        *reinterpret_cast<float2*>(lead ? sdC + o : sNull + 2) = float2{dC0, dC1};
+        *reinterpret_cast<float4*>((tid & 63) < gw
+                                       ? sDx + ((size_t)(wave * kBwSub + i) * R + r) * P + 4 * q
+                                       : sNull) = float4{dxr[0], dxr[1], dxr[2], dxr[3]};
+      }
+      if (valid) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          e[0][j] = en[0][j];
+          e[1][j] = en[1][j];
+        }
+      }
+    }
+    __syncthreads();
+    // the block's dx (sums over waves), dB, dC, dtheta rows and per-token
+    // scalars (sums over row pairs)
+    const int nv = min(kBwSub, a.T - k0);  // tokens of the block in the sequence
+    const size_t row0 = (tok_base + k0) * a.H + hh;
+    for (int o = tid; o < nv * RP; o += nt) {
+      const int i = o / RP, rp = o - i * RP;
+      float sum = 0.f;
+      for (int w = 0; w < nw; ++w) sum += sDx[(size_t)(w * kBwSub + i) * RP + rp];
+      a.dx[(row0 + (size_t)i * a.H) * RP + rp] = sum;
+    }
+    const int RN = R * a.N;
+    for (int o = tid; o < nv * RN; o += nt) {
+      const int i = o / RN, rn = o - i * RN;
+      const size_t g = (row0 + (size_t)i * a.H) * RN + rn;
+      a.dB[g] = sdB[o];
+      a.dC[g] = sdC[o];
+    }
+    for (int o = tid; o < nv * (a.N / 2); o += nt) {
+      const int i = o / (a.N / 2), k = o - i * (a.N / 2);
+      a.dtheta[(row0 + (size_t)i * a.H) * (a.N / 2) + k] = sdTh[o];
+    }
+    if (tid < 4 * kBwSub) {
+      const int i = tid >> 2, cc = tid & 3, t = k0 + i;
+      float sum = 0.f;
+      for (int k = 0; k < a.N / 2; ++k) sum += sSc[((size_t)k * kBwSub + i) * 4 + cc];
+      const int b4 = tid & ~3;
+      const float dal = __shfl(sum, b4), dga = __shfl(sum, b4 + 1), dbe = __shfl(sum, b4 + 2),
+                  dth = __shfl(sum, b4 + 3);
+      if (cc == 0 && t < a.T) {
+        const int sl = sb * kBwSub + i + 1;
+        const float d = c.sDt[sl], l = c.sLam[sl];
+        const float alpha = __expf(d * c.Ah);
+        const size_t tok = (tok_base + t) * a.H + hh;
+        a.ddt[tok] = dal * alpha * c.Ah + dbe * (1.f - l) + dga * l + dth;
+        a.dlam[tok] = (dga - dbe) * d;
+        a.dAc[tok] = dal * alpha * d;
+      }
+    }
+    __syncthreads();  // sDx and sSc are rewritten by the next block
+  }
+}
+
+// Segment-local walks, one workgroup per (batch, head, segment), thread
+// layout as seg_grads_kernel: the state at the segment's end from a zero
+// entry state (into slot s of hs), the adjoint dU at its first token from a
+// zero exit adjoint (slot s of gs), and the segment's transfer: decay
+// prod_t alpha_t = exp(A sum_t dt_t) and, per row pair, rotation angle
+// sum_t dt_t theta_t.  The recurrence is linear and its 2 x 2 rotations of
+// a row pair commute, so over a segment h_end = D R(psi) h_entry + h_local
+// and dU_first = D R(psi)^T E + dU_local, E the adjoint the segment's last
+// token inherits.
+template <typename T, int R, int P>
+__global__ void __launch_bounds__(kBwMaxThreads) seg_local_kernel(BackwardArgs a, int nseg) {
+  extern __shared__ __align__(16) unsigned char sm[];
+  constexpr int es = sizeof(T);
+  constexpr int gw = P / 4;
+  const int S = a.S;
+  const int nt = blockDim.x, tid = threadIdx.x;
+  const int kp = tid / gw, q = tid - kp * gw;
+  const int unit = blockIdx.x / nseg, seg = blockIdx.x - unit * nseg;
+  const int bidx = unit / a.H, hh = unit - bidx * a.H;
+  const int t0 = seg * S;
+  const BwSegLayout L = bw_seg_layout(S, R, a.N, P, es);
+  const size_t NP = (size_t)a.N * a.P;
+  const size_t tok_base = (size_t)bidx * a.T;
+  stage_segment<T>(a, L, sm, t0, tok_base, hh, tid, nt);
+  __syncthreads();
+  SegCtx<T, R, P> c;
+  c.sB = sm + L.oB;
+  c.sC = sm + L.oC;
+  c.sX = sm + L.oX;
+  c.sDY = sm + L.oDY;
+  c.sTh = reinterpret_cast<const float*>(sm + L.oTh);
+  c.sDt = reinterpret_cast<const float*>(sm + L.oDt);
+  c.sLam = reinterpret_cast<const float*>(sm + L.oLam);
+  c.rowB = L.wB * 4;
+  c.rowX = L.wX * 4;
+  c.offB = (uint32_t)(2 * kp) * es;
+  c.offX = (uint32_t)(4 * q) * es;
+  c.N = a.N;
+  c.kp = kp;
+  c.Ah = a.A[hh];
+  const size_t slot = ((size_t)unit * nseg + seg) * NP + (size_t)(2 * kp) * P + 4 * q;
+
+  float h[2][4], pq[2][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) h[0][j] = h[1][j] = 0.f;
+  c.outer(c.sB, c.sX, 0, pq);
+  float dsum = 0.f, psum = 0.f;
+#pragma unroll 4
+  for (int i = 1; i <= S; ++i) {
+    c.step(i, h, pq);
+    const float d = c.sDt[i];
+    dsum += d;
+    psum = __builtin_fmaf(d, c.sTh[i * (a.N / 2) + kp], psum);
+  }
+  *reinterpret_cast<float4*>(a.hs + slot) = float4{h[0][0], h[0][1], h[0][2], h[0][3]};
+  *reinterpret_cast<float4*>(a.hs + slot + P) = float4{h[1][0], h[1][1], h[1][2], h[1][3]};
+  if (q == 0) a.psi[((size_t)unit * nseg + seg) * (a.N / 2) + kp] = psum;
+  if (tid == 0) a.dseg[(size_t)unit * nseg + seg] = __expf(c.Ah * dsum);
+
+  float e[2][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) e[0][j] = e[1][j] = 0.f;
+#pragma unroll 4
+  for (int i = S; i >= 1; --i) {
+    const float d = c.sDt[i];
+    const float alpha = __expf(d * c.Ah);
+    float sn, cn;
+    sincos_step(d * c.sTh[i * (a.N / 2) + kp], sn, cn);
+    float cd[2][4];
+    c.outer(c.sC, c.sDY, i, cd);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float g0 = cd[0][j] + e[0][j], g1 = cd[1][j] + e[1][j];
+      e[0][j] = alpha * (cn * g0 + sn * g1);
+      e[1][j] = alpha * (cn * g1 - sn * g0);
+    }
+  }
+  *reinterpret_cast<float4*>(a.gs + slot) = float4{e[0][0], e[0][1], e[0][2], e[0][3]};
+  *reinterpret_cast<float4*>(a.gs + slot + P) = float4{e[1][0], e[1][1], e[1][2], e[1][3]};
+}
+
+// The chain over a sequence's segments, in place (blockIdx.y 0: states
+// forward, 1: adjoints backward): slot s of hs becomes the entry state of
+// segment s, slot s of gs the adjoint its last token inherits (dh_final, or
+// zero, for the last segment).
+template <int P>
+__global__ void __launch_bounds__(kBwMaxThreads) seg_chain_kernel(BackwardArgs a, int nseg) {
+  constexpr int gw = P / 4;
+  const int tid = threadIdx.x;
+  const int kp = tid / gw, q = tid - kp * gw;
+  const int unit = blockIdx.x;
+  const size_t NP = (size_t)a.N * a.P;
+  const size_t el0 = (size_t)(2 * kp) * P + 4 * q;
+  const float* D = a.dseg + (size_t)unit * nseg;
+  const float* psi = a.psi + (size_t)unit * nseg * (a.N / 2) + kp;
+  float v[2][4];
+  if (blockIdx.y == 0) {
+    float* base = a.hs + (size_t)unit * nseg * NP + el0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[0][j] = v[1][j] = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < nseg; ++s) {
+      float* sp = base + (size_t)s * NP;
+      const float4 l0 = *reinterpret_cast<const float4*>(sp);
+      const float4 l1 = *reinterpret_cast<const float4*>(sp + P);
+      const float dd = D[s];
+      float sn, cn;
+      sincos_step(psi[(size_t)s * (a.N / 2)], sn, cn);
+      *reinterpret_cast<float4*>(sp) = float4{v[0][0], v[0][1], v[0][2], v[0][3]};
+      *reinterpret_cast<float4*>(sp + P) = float4{v[1][0], v[1][1], v[1][2], v[1][3]};
+      const float lc[2][4] = {{l0.x, l0.y, l0.z, l0.w}, {l1.x, l1.y, l1.z, l1.w}};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float h0 = v[0][j], h1 = v[1][j];
+        v[0][j] = __builtin_fmaf(dd, cn * h0 - sn * h1, lc[0][j]);
+        v[1][j] = __builtin_fmaf(dd, sn * h0 + cn * h1, lc[1][j]);
+      }
+    }
+  } else {
+    float* base = a.gs + (size_t)unit * nseg * NP + el0;
+    if (a.dh_final) {
+      const float* df = a.dh_final + (size_t)unit * NP + el0;
+      const float4 r0 = *reinterpret_cast<const float4*>(df);
+      const float4 r1 = *reinterpret_cast<const float4*>(df + P);
+      v[0][0] = r0.x; v[0][1] = r0.y; v[0][2] = r0.z; v[0][3] = r0.w;
+      v[1][0] = r1.x; v[1][1] = r1.y; v[1][2] = r1.z; v[1][3] = r1.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[0][j] = v[1][j] = 0.f;
+    }
+#pragma unroll 4
+    for (int s = nseg - 1; s >= 0; --s) {
+      float* sp = base + (size_t)s * NP;
+      const float4 l0 = *reinterpret_cast<const float4*>(sp);
+      const float4 l1 = *reinterpret_cast<const float4*>(sp + P);
+      const float dd = D[s];
+      float sn, cn;
+      sincos_step(psi[(size_t)s * (a.N / 2)], sn, cn);
+      *reinterpret_cast<float4*>(sp) = float4{v[0][0], v[0][1], v[0][2], v[0][3]};
+      *reinterpret_cast<float4*>(sp + P) = float4{v[1][0], v[1][1], v[1][2], v[1][3]};
+      const float lc[2][4] = {{l0.x, l0.y, l0.z, l0.w}, {l1.x, l1.y, l1.z, l1.w}};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e0 = v[0][j], e1 = v[1][j];
+        v[0][j] = __builtin_fmaf(dd, cn * e0 + sn * e1, lc[0][j]);
+        v[1][j] = __builtin_fmaf(dd, cn * e1 - sn * e0, lc[1][j]);
+      }
+    }
+  }
+}
+
 __global__ void zero_kernel(float* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.f;
@@ -485,8 +1040,43 @@ __global__ void __launch_bounds__(256) dA_kernel(BackwardArgs a) {
   if (threadIdx.x == 0) a.dA[hh] = s[0];
 }
 
+template <typename T, int R, int P>
+hipError_t launch_segments(const BackwardArgs& a, hipStream_t stream) {
+  const int units = a.nb * a.H;
+  const int nseg = (a.T + a.S - 1) / a.S;
+  const BwSegLayout L = bw_seg_layout(a.S, R, a.N, P, (int)sizeof(T));
+  const dim3 block(a.N * P / 8);
+  // the local walks need only the staged inputs (the LDS up to the dx partials)
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&seg_local_kernel<T, R, P>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.oDx);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((seg_local_kernel<T, R, P>), dim3((unsigned)((size_t)units * nseg)), block,
+                     L.oDx, stream, a, nseg);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((seg_chain_kernel<P>), dim3((unsigned)units, 2), block, 0, stream, a, nseg);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&seg_grads_kernel<T, R, P>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((seg_grads_kernel<T, R, P>), dim3((unsigned)((size_t)units * nseg)),
+                     block, L.total, stream, a, nseg);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dA_kernel, dim3(a.H), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <typename T, int R>
 hipError_t launch_typed(const BackwardArgs& a, hipStream_t stream) {
+  if (a.S > 0) switch (a.P) {
+      case 16: return launch_segments<T, R, 16>(a, stream);
+      case 32: return launch_segments<T, R, 32>(a, stream);
+      case 64: return launch_segments<T, R, 64>(a, stream);
+      case 128: return launch_segments<T, R, 128>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
   const int units = a.nb * a.H;
   const dim3 sgrid(units, (unsigned)(((a.N / 2) * a.P + kScanThreads - 1) / kScanThreads));
   hipLaunchKernelGGL((fwd_states_kernel<T, R>), sgrid, dim3(kScanThreads), 0, stream, a);

@@ -78,8 +78,74 @@ struct BackwardArgs {
   const void *x, *B, *C, *dy;                       // storage type of the call
   const float *dt, *A, *lam, *theta, *dh_final;     // dh_final may be null
   float *dx, *ddt, *dA, *dlam, *dtheta, *dB, *dC;   // gradients, float
-  float *hs, *gs, *dAc;                             // workspace: h_t, G_t, dA terms
+  // workspace: the states (every token's h_t and G_t, or with segments of S
+  // tokens the segment-entry h and segment-exit dU checkpoints) and the
+  // per-token dA terms
+  float *hs, *gs, *dAc;
+  int S;  // segment length of the checkpointed path (0: states per token)
+  // per segment: its decay prod_t alpha_t and, per row pair, its rotation
+  // angle sum_t dt_t theta_t (checkpointed path)
+  float *dseg, *psi;
 };
+
+// Segment path of the backward: one workgroup of N P / 8 threads per
+// (sequence, head, segment of S tokens); thread (kp, q) holds rows 2 kp,
+// 2 kp + 1 and columns 4 q .. 4 q + 3 of the state.  Tokens are recomputed
+// in blocks of kBwSub.
+constexpr int kBwSub = 8;
+constexpr int kBwMaxThreads = 512;
+
+// LDS of one segment workgroup (byte offsets, 16-aligned): the segment's
+// inputs for tokens t0 - 1 .. t0 + S (S + 2 slots) as stored; for one block,
+// the per-wave dx partials, per-row-pair scalar partials and the dB, dC and
+// dtheta rows; a 16-byte slot per lane that the lanes with nothing to store
+// write instead (so the stores need no branch); each thread's block-entry
+// states.
+struct BwSegLayout {
+  int nslot;
+  uint32_t wB, wX;  // 32-bit words per token-head row of B (and C), of x (and dy)
+  size_t oB, oC, oX, oDY, oTh, oDt, oLam, oDx, oSc, odB, odC, odTh, oNull, oHs, total;
+};
+
+__host__ __device__ inline BwSegLayout bw_seg_layout(int S, int R, int N, int P, int es) {
+  BwSegLayout l;
+  const int nt = N * P / 8, nw = (nt + 63) / 64;
+  l.nslot = S + 2;
+  l.wB = (uint32_t)(R * N * es / 4);
+  l.wX = (uint32_t)(R * P * es / 4);
+  size_t o = 0;
+  auto take = [&o](size_t bytes) {
+    const size_t at = o;
+    o = (o + bytes + 15) / 16 * 16;
+    return at;
+  };
+  l.oB = take((size_t)l.nslot * l.wB * 4);
+  l.oC = take((size_t)l.nslot * l.wB * 4);
+  l.oX = take((size_t)l.nslot * l.wX * 4);
+  l.oDY = take((size_t)l.nslot * l.wX * 4);
+  l.oTh = take((size_t)l.nslot * (N / 2) * 4);
+  l.oDt = take((size_t)l.nslot * 4);
+  l.oLam = take((size_t)l.nslot * 4);
+  l.oDx = take((size_t)nw * kBwSub * R * P * 4);
+  l.oSc = take((size_t)(N / 2) * kBwSub * 16);
+  l.odB = take((size_t)kBwSub * R * N * 4);
+  l.odC = take((size_t)kBwSub * R * N * 4);
+  l.odTh = take((size_t)kBwSub * (N / 2) * 4);
+  l.oNull = take(64 * 16);
+  l.oHs = take((size_t)(S / kBwSub) * 8 * nt * 4);
+  l.total = o;
+  return l;
+}
+
+// Segment length of the backward's checkpointed path for a shape (32, else
+// 16 or 8 to fit the LDS), or 0 when the shape takes the per-token states
+// (N P > 8 kBwMaxThreads).
+__host__ __device__ inline int bw_segment_len(int R, int N, int P, int es) {
+  if (N * P > 8 * kBwMaxThreads || P < 16) return 0;
+  for (int S = 32; S >= kBwSub; S /= 2)
+    if (bw_seg_layout(S, R, N, P, es).total <= kLdsLimit) return S;
+  return 0;
+}
 
 // Block-side passes (BCNorm + bias, MIMO projections).
 struct BlockArgs {

@@ -372,15 +372,25 @@ m3_status check_backward_dims(const m3_dims* d, m3_dtype dtype) {
 }
 
 struct BwCarve {
-  size_t off_gs, off_dAc, total;
+  int S;  // segment length of the checkpointed path, 0 for per-token states
+  size_t off_gs, off_dAc, off_dseg, off_psi, total;
 };
 
-BwCarve bw_carve(const m3_dims* d) {
+// The states: with segments of S tokens one entry state and one exit
+// adjoint per segment, else h_t and G_t of every token.
+BwCarve bw_carve(const m3_dims* d, m3_dtype dtype) {
   BwCarve w;
-  const size_t states = (size_t)d->batch * d->nheads * d->seqlen * d->dstate_n * d->headdim_p;
+  w.S = m3::bw_segment_len((int)d->rank_r, (int)d->dstate_n, (int)d->headdim_p,
+                           (int)esize_of(dtype));
+  const size_t slots = w.S ? (size_t)(d->seqlen + w.S - 1) / w.S : (size_t)d->seqlen;
+  const size_t states = (size_t)d->batch * d->nheads * slots * d->dstate_n * d->headdim_p;
   w.off_gs = round256(states * sizeof(float));
   w.off_dAc = w.off_gs + round256(states * sizeof(float));
-  w.total = w.off_dAc + round256((size_t)d->batch * d->seqlen * d->nheads * sizeof(float));
+  w.off_dseg = w.off_dAc + round256((size_t)d->batch * d->seqlen * d->nheads * sizeof(float));
+  // per segment: decay and one rotation angle per row pair
+  const size_t segs = w.S ? (size_t)d->batch * d->nheads * slots : 0;
+  w.off_psi = w.off_dseg + round256(segs * sizeof(float));
+  w.total = w.off_psi + round256(segs * (d->dstate_n / 2) * sizeof(float));
   return w;
 }
 
@@ -391,7 +401,7 @@ extern "C" {
 size_t m3_backward_workspace_size(const m3_dims* dims, m3_dtype dtype) {
   if (check_backward_dims(dims, dtype) != M3_SUCCESS) return 0;
   if (dims->batch == 0 || dims->seqlen == 0) return 0;
-  return bw_carve(dims).total;
+  return bw_carve(dims, dtype).total;
 }
 
 m3_status m3_backward(const m3_dims* dims, m3_dtype dtype, const void* x, const float* dt,
@@ -428,8 +438,9 @@ m3_status m3_backward(const m3_dims* dims, m3_dtype dtype, const void* x, const 
     const hipError_t e = m3::launch_backward(a, dtype, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;
   }
-  const BwCarve w = bw_carve(dims);
+  const BwCarve w = bw_carve(dims, dtype);
   if (!workspace || workspace_bytes < w.total) return M3_ERR_WORKSPACE;
+  a.S = w.S;
   if (!aligned(workspace, 256)) return M3_ERR_INVALID_VALUE;
   a.x = x;
   a.B = B;
@@ -451,6 +462,8 @@ m3_status m3_backward(const m3_dims* dims, m3_dtype dtype, const void* x, const 
   a.hs = reinterpret_cast<float*>(ws);
   a.gs = reinterpret_cast<float*>(ws + w.off_gs);
   a.dAc = reinterpret_cast<float*>(ws + w.off_dAc);
+  a.dseg = reinterpret_cast<float*>(ws + w.off_dseg);
+  a.psi = reinterpret_cast<float*>(ws + w.off_psi);
   const hipError_t e = m3::launch_backward(a, dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;
 }

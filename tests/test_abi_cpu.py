@@ -300,6 +300,17 @@ def test_backward_validation(lib):
         assert call(d, p) == m3.M3_ERR_INVALID_VALUE
     assert call(d, ws=None) == m3.M3_ERR_WORKSPACE
     need = lib.m3_backward_workspace_size(ctypes.byref(d), m3.M3_F32)
-    assert need == 2 * 2 * 2 * 16 * 64 * 64 * 4 + 256  # h_t and G_t of every token-head, dA terms
+    # N P <= 4096: segments of 16 tokens at this shape (float, R = 2: the
+    # LDS does not fit 32), one entry state and one exit adjoint per
+    # segment and head; the dA terms; per segment a decay and N / 2 angles
+    # (each area rounded up to 256 bytes)
+    assert need == 2 * (2 * 2 * 1 * 64 * 64 * 4) + 256 + 256 + 512
+    d40 = dims(b=2, t=40, h=2, p=64, n=64, r=2)
+    assert lib.m3_backward_workspace_size(ctypes.byref(d40), m3.M3_F32) == \
+        2 * (2 * 2 * 3 * 64 * 64 * 4) + 768 + 256 + 12 * 32 * 4
+    # N P = 8192: h_t and G_t of every token-head
+    d8k = dims(b=2, t=16, h=2, p=64, n=128, r=1)
+    assert lib.m3_backward_workspace_size(ctypes.byref(d8k), m3.M3_BF16) == \
+        2 * (2 * 2 * 16 * 128 * 64 * 4) + 256
     assert call(d, wsb=need - 1) == m3.M3_ERR_WORKSPACE
     assert lib.m3_backward_workspace_size(ctypes.byref(dims(b=0)), m3.M3_F32) == 0

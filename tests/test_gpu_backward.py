@@ -27,6 +27,12 @@ CASES = [
     ("bf16", 2, 50, 2, 64, 64, 1, True),
     ("bf16", 1, 70, 2, 128, 64, 1, False),
     ("bf16", 1, 30, 2, 64, 64, 4, True),
+    # checkpointed segments: several segments with a ragged last one, column
+    # groups of 32, 8 and 4 lanes, segment lengths 32, 16 and 8
+    ("bf16", 1, 200, 2, 32, 128, 1, True),
+    ("bf16", 2, 129, 1, 16, 32, 4, True),
+    ("f32", 1, 97, 1, 256, 16, 2, False),
+    ("f32", 1, 45, 1, 64, 64, 4, True),
 ]
 
 
