@@ -512,9 +512,10 @@ __device__ __forceinline__ void lds_quad(const unsigned char* p, float (&v)[4]) 
   }
 }
 
-// Sum over each aligned group of gw consecutive lanes (gw = 4, 8, 16 or 32),
+// Sum over each aligned group of gw consecutive lanes (gw = 4 .. 64),
 // complete in the group's last lane: shifts within rows of 16, then row 0's
-// (row 2's) last lane added into row 1 (row 3).
+// (row 2's) last lane added into row 1 (row 3), then lane 31 into rows 2
+// and 3.
 template <int gw>
 __device__ __forceinline__ float group_sum_last(float v) {
   v += dpp_move<0x111>(v);  // row_shr:1
@@ -522,6 +523,7 @@ __device__ __forceinline__ float group_sum_last(float v) {
   if constexpr (gw >= 8) v += dpp_move<0x114>(v);   // row_shr:4
   if constexpr (gw >= 16) v += dpp_move<0x118>(v);  // row_shr:8
   if constexpr (gw >= 32) v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  if constexpr (gw >= 64) v += dpp_move<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
@@ -532,6 +534,7 @@ __device__ __forceinline__ float group_sum_last(float v) {
 // lanes active.
 template <int gw>
 __device__ __forceinline__ float cross_group_sum(float v, bool full) {
+  if constexpr (gw >= 64) return v;  // one group per wave
   if constexpr (gw <= 8) v += dpp_move<0x128>(v);  // row_ror:8
   if constexpr (gw <= 4) v += dpp_move<0x124>(v);  // row_ror:4
   if constexpr (gw <= 16) {
@@ -602,48 +605,77 @@ __device__ __forceinline__ void stage_segment(const BackwardArgs& a, const BwSeg
   }
 }
 
-template <typename T, int R, int P>
+// Rows 2kp, 2kp + 1 (row stride P floats) of W columns of a float state.
+template <int W>
+__device__ __forceinline__ void load_piece(const float* p, int P, float (&v)[2][W]) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if constexpr (W == 4) {
+      const float4 f = *reinterpret_cast<const float4*>(p + r * P);
+      v[r][0] = f.x;
+      v[r][1] = f.y;
+      v[r][2] = f.z;
+      v[r][3] = f.w;
+    } else {
+      const float2 f = *reinterpret_cast<const float2*>(p + r * P);
+      v[r][0] = f.x;
+      v[r][1] = f.y;
+    }
+  }
+}
+
+// W consecutive elements (W = 2 or 4) of a staged row, as float.
+template <typename T, int W>
+__device__ __forceinline__ void lds_piece(const unsigned char* p, float (&v)[W]) {
+  if constexpr (W == 4) {
+    lds_quad<T>(p, v);
+  } else {
+    lds_pair<T>(p, v[0], v[1]);
+  }
+}
+
+template <typename T, int R, int P, int W = 4>
 struct SegCtx {
   const unsigned char *sB, *sC, *sX, *sDY;
   const float *sTh, *sDt, *sLam;
   uint32_t rowB, rowX;  // staged bytes per token slot
-  uint32_t offB, offX;  // this thread's pair / quad within a rank's row
+  uint32_t offB, offX;  // this thread's pair / W-piece within a rank's row
   int N, kp;
   float Ah;
 
   __device__ void pair(const unsigned char* base, int slot, int r, float& b0, float& b1) const {
     lds_pair<T>(base + slot * rowB + (uint32_t)(r * N) * sizeof(T) + offB, b0, b1);
   }
-  __device__ void quad(const unsigned char* base, int slot, int r, float (&v)[4]) const {
-    lds_quad<T>(base + slot * rowX + (uint32_t)(r * P) * sizeof(T) + offX, v);
+  __device__ void quad(const unsigned char* base, int slot, int r, float (&v)[W]) const {
+    lds_piece<T, W>(base + slot * rowX + (uint32_t)(r * P) * sizeof(T) + offX, v);
   }
   // sum_r B_r x_r^T (or C dy^T) over this thread's rows and columns
   __device__ void outer(const unsigned char* bb, const unsigned char* xb, int slot,
-                        float (&o)[2][4]) const {
+                        float (&o)[2][W]) const {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[0][j] = o[1][j] = 0.f;
+    for (int j = 0; j < W; ++j) o[0][j] = o[1][j] = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float b0, b1, xv[4];
+      float b0, b1, xv[W];
       pair(bb, slot, r, b0, b1);
       quad(xb, slot, r, xv);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < W; ++j) {
         o[0][j] = __builtin_fmaf(b0, xv[j], o[0][j]);
         o[1][j] = __builtin_fmaf(b1, xv[j], o[1][j]);
       }
     }
   }
   // h_t from h_{t-1} (in place); pq: P_{t-1} in, P_t out
-  __device__ void step(int slot, float (&h)[2][4], float (&pq)[2][4]) const {
+  __device__ void step(int slot, float (&h)[2][W], float (&pq)[2][W]) const {
     const float d = sDt[slot], l = sLam[slot];
     const float alpha = __expf(d * Ah), beta = (1.f - l) * d, gamma = l * d;
     float sn, cn;
     sincos_step(d * sTh[slot * (N / 2) + kp], sn, cn);
-    float pc[2][4];
+    float pc[2][W];
     outer(sB, sX, slot, pc);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < W; ++j) {
       const float u0 = __builtin_fmaf(beta, pq[0][j], h[0][j]);
       const float u1 = __builtin_fmaf(beta, pq[1][j], h[1][j]);
       h[0][j] = __builtin_fmaf(alpha, cn * u0 - sn * u1, gamma * pc[0][j]);
@@ -654,25 +686,134 @@ struct SegCtx {
   }
 };
 
-template <typename T, int R, int P>
-__global__ void __launch_bounds__(kBwMaxThreads) seg_grads_kernel(BackwardArgs a, int nseg) {
+// The backward walk over one block of kBwSub tokens (last to first): the
+// staged inputs and the block's LDS outputs arrive as separate restrict
+// pointers, so a token's input loads may be scheduled ahead of the previous
+// token's partial-sum stores.
+template <typename T, int R, int P, int W>
+__device__ __forceinline__ void reverse_block(
+    const SegCtx<T, R, P, W>& c, const unsigned char* __restrict__ sB,
+    const unsigned char* __restrict__ sC, const unsigned char* __restrict__ sX,
+    const unsigned char* __restrict__ sDY, const float* __restrict__ sTh,
+    const float* __restrict__ sDt, const float* __restrict__ sLam, float* __restrict__ sSc,
+    float* __restrict__ sDx, float* __restrict__ sdB, float* __restrict__ sdC,
+    float* __restrict__ sdTh, float* __restrict__ sNull, int sb, int k0, int nT, int N, int kp,
+    int q, int tid, int wave, bool full, const float (&hist)[kBwSub + 1][2][W],
+    float (&e)[2][W]) {
+  constexpr int gw = P / W;
+  constexpr bool kFull = 8 * P / W >= 64;  // N >= 16: a full wave
+  float pc[2][W];  // P_t of the token at hand
+  c.outer(sB, sX, sb * kBwSub + kBwSub, pc);
+#pragma unroll
+  for (int i = kBwSub - 1; i >= 0; --i) {
+    const int sl = sb * kBwSub + i + 1, t = k0 + i;
+    const bool valid = t < nT, last = t >= nT - 1;
+    const float d = sDt[sl], l = sLam[sl];
+    const float alpha = __expf(d * c.Ah), beta = (1.f - l) * d, gamma = l * d;
+    const float beta_n = (1.f - sLam[sl + 1]) * sDt[sl + 1];  // zero past the end
+    const float th = sTh[sl * (N / 2) + kp];
+    float sn, cn;
+    sincos_step(d * th, sn, cn);
+    float pp[2][W], cd[2][W];
+    c.outer(sB, sX, sl - 1, pp);
+    c.outer(sC, sDY, sl, cd);
+    float s_alpha = 0.f, s_gamma = 0.f, s_beta = 0.f, s_psi = 0.f;
+    float dp[2][W], en[2][W];
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      const float g0 = cd[0][j] + e[0][j], g1 = cd[1][j] + e[1][j];
+      const float u0 = __builtin_fmaf(beta, pp[0][j], hist[i][0][j]);
+      const float u1 = __builtin_fmaf(beta, pp[1][j], hist[i][1][j]);
+      const float v0 = cn * u0 - sn * u1, v1 = sn * u0 + cn * u1;  // R U
+      s_alpha += g0 * v0 + g1 * v1;
+      s_psi += g1 * v0 - g0 * v1;
+      const float du0 = alpha * (cn * g0 + sn * g1), du1 = alpha * (cn * g1 - sn * g0);
+      s_gamma += g0 * pc[0][j] + g1 * pc[1][j];
+      s_beta += du0 * pp[0][j] + du1 * pp[1][j];
+      // dP_t = gamma G_t + beta_{t+1} dU_{t+1} (no dU_{t+1} after the last token)
+      const float un0 = last ? 0.f : e[0][j], un1 = last ? 0.f : e[1][j];
+      dp[0][j] = __builtin_fmaf(beta_n, un0, gamma * g0);
+      dp[1][j] = __builtin_fmaf(beta_n, un1, gamma * g1);
+      en[0][j] = du0;
+      en[1][j] = du1;
+    }
+    // sums over the row pair's columns, complete in its last lane
+    s_psi = group_sum_last<gw>(s_psi);
+    s_alpha = group_sum_last<gw>(s_alpha);
+    s_gamma = group_sum_last<gw>(s_gamma);
+    s_beta = group_sum_last<gw>(s_beta);
+    // the row pair's last lane stores its sums (the others into their null
+    // slots, so no branch splits the step)
+    const bool lead = q == gw - 1;
+    *reinterpret_cast<float4*>(lead ? sSc + ((size_t)kp * kBwSub + i) * 4 : sNull) =
+        float4{s_alpha, s_gamma, s_beta, alpha * s_psi * th};
+    *(lead ? sdTh + i * (N / 2) + kp : sNull) = alpha * s_psi * d;
+    // per rank: dB = dP x, dC = h_t dy (sums over columns), dx = dP^T B
+    // (sums over the wave's row pairs here, over waves after the block)
+#pragma nounroll
+    for (int r = 0; r < R; ++r) {
+      float xv[W], dyv[W], b0, b1;
+      c.quad(sX, sl, r, xv);
+      c.quad(sDY, sl, r, dyv);
+      c.pair(sB, sl, r, b0, b1);
+      float dB0 = 0.f, dB1 = 0.f, dC0 = 0.f, dC1 = 0.f, dxr[W];
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        dB0 = __builtin_fmaf(dp[0][j], xv[j], dB0);
+        dB1 = __builtin_fmaf(dp[1][j], xv[j], dB1);
+        dC0 = __builtin_fmaf(hist[i + 1][0][j], dyv[j], dC0);
+        dC1 = __builtin_fmaf(hist[i + 1][1][j], dyv[j], dC1);
+        dxr[j] = cross_group_sum<gw>(dp[0][j] * b0 + dp[1][j] * b1, kFull || full);
+      }
+      dB0 = group_sum_last<gw>(dB0);
+      dB1 = group_sum_last<gw>(dB1);
+      dC0 = group_sum_last<gw>(dC0);
+      dC1 = group_sum_last<gw>(dC1);
+      const int o = (i * R + r) * N + 2 * kp;
+      *reinterpret_cast<float2*>(lead ? sdB + o : sNull) = float2{dB0, dB1};
+      *reinterpret_cast<float2*>(lead ? sdC + o : sNull + 2) = float2{dC0, dC1};
+      float* dxo = (tid & 63) < gw ? sDx + ((size_t)(wave * kBwSub + i) * R + r) * P + W * q : sNull;
+      if constexpr (W == 4)
+        *reinterpret_cast<float4*>(dxo) = float4{dxr[0], dxr[1], dxr[2], dxr[3]};
+      else
+        *reinterpret_cast<float2*>(dxo) = float2{dxr[0], dxr[1]};
+    }
+    if (valid) {
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        e[0][j] = en[0][j];
+        e[1][j] = en[1][j];
+      }
+    }
+    // the next (earlier) token's P_t is this one's P_{t-1}
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      pc[0][j] = pp[0][j];
+      pc[1][j] = pp[1][j];
+    }
+  }
+}
+
+template <typename T, int R, int P, int W>
+__global__ void __launch_bounds__(kBwMaxThreads * 4 / W) seg_grads_kernel(BackwardArgs a, int nseg,
+                                                                          int nbuf) {
   extern __shared__ __align__(16) unsigned char sm[];
   constexpr int es = sizeof(T);
-  constexpr int gw = P / 4;  // lanes per row pair
+  constexpr int gw = P / W;  // lanes per row pair
   const int S = a.S, NSUB = S / kBwSub;
   const int nt = blockDim.x, tid = threadIdx.x;
   const int kp = tid / gw, q = tid - kp * gw;
   const int unit = blockIdx.x / nseg, seg = blockIdx.x - unit * nseg;
   const int bidx = unit / a.H, hh = unit - bidx * a.H;
   const int t0 = seg * S;
-  const BwSegLayout L = bw_seg_layout(S, R, a.N, P, es);
+  const BwSegLayout L = bw_seg_layout(S, R, a.N, P, es, W, nbuf);
   const size_t NP = (size_t)a.N * a.P;
   const size_t tok_base = (size_t)bidx * a.T;  // (batch, token) row of token 0
 
   stage_segment<T>(a, L, sm, t0, tok_base, hh, tid, nt);
   __syncthreads();
 
-  SegCtx<T, R, P> c;
+  SegCtx<T, R, P, W> c;
   c.sB = sm + L.oB;
   c.sC = sm + L.oC;
   c.sX = sm + L.oX;
@@ -683,7 +824,7 @@ __global__ void __launch_bounds__(kBwMaxThreads) seg_grads_kernel(BackwardArgs a
   c.rowB = L.wB * 4;
   c.rowX = L.wX * 4;
   c.offB = (uint32_t)(2 * kp) * es;
-  c.offX = (uint32_t)(4 * q) * es;
+  c.offX = (uint32_t)(W * q) * es;
   c.N = a.N;
   c.kp = kp;
   c.Ah = a.A[hh];
@@ -694,136 +835,54 @@ __global__ void __launch_bounds__(kBwMaxThreads) seg_grads_kernel(BackwardArgs a
   float* sdC = reinterpret_cast<float*>(sm + L.odC);
   float* sdTh = reinterpret_cast<float*>(sm + L.odTh);
   float* sNull = reinterpret_cast<float*>(sm + L.oNull) + (tid & 63) * 4;
-  const size_t el0 = (size_t)(2 * kp) * P + 4 * q;  // this thread's first element
+  const size_t el0 = (size_t)(2 * kp) * P + W * q;  // this thread's first element
 
   // ---- forward walk: block-entry states ----------------------------------------
-  float h[2][4], pq[2][4];
+  float h[2][W], pq[2][W];
   if (seg == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) h[0][j] = h[1][j] = 0.f;
+    for (int j = 0; j < W; ++j) h[0][j] = h[1][j] = 0.f;
   } else {
-    const float* hk = a.hs + ((size_t)unit * nseg + seg) * NP + el0;
-    const float4 r0 = *reinterpret_cast<const float4*>(hk);
-    const float4 r1 = *reinterpret_cast<const float4*>(hk + P);
-    h[0][0] = r0.x; h[0][1] = r0.y; h[0][2] = r0.z; h[0][3] = r0.w;
-    h[1][0] = r1.x; h[1][1] = r1.y; h[1][2] = r1.z; h[1][3] = r1.w;
+    load_piece<W>(a.hs + ((size_t)unit * nseg + seg) * NP + el0, P, h);
   }
   c.outer(c.sB, c.sX, 0, pq);  // P of token t0 - 1
 #pragma nounroll
   for (int sb = 0; sb < NSUB; ++sb) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sHs[(sb * 8 + e) * nt + tid] = h[e >> 2][e & 3];
+    for (int v = 0; v < 2 * W; ++v) sHs[(sb * 2 * W + v) * nt + tid] = h[v / W][v % W];
 #pragma unroll
     for (int i = 0; i < kBwSub; ++i) c.step(sb * kBwSub + i + 1, h, pq);
   }
 
   // ---- backward, block by block --------------------------------------------------
-  float e[2][4];  // dU_{t+1} (dh_final, or zero, after the last token)
-  {
-    const float* ek = a.gs + ((size_t)unit * nseg + seg) * NP + el0;
-    const float4 r0 = *reinterpret_cast<const float4*>(ek);
-    const float4 r1 = *reinterpret_cast<const float4*>(ek + P);
-    e[0][0] = r0.x; e[0][1] = r0.y; e[0][2] = r0.z; e[0][3] = r0.w;
-    e[1][0] = r1.x; e[1][1] = r1.y; e[1][2] = r1.z; e[1][3] = r1.w;
-  }
+  float e[2][W];  // dU_{t+1} (dh_final, or zero, after the last token)
+  load_piece<W>(a.gs + ((size_t)unit * nseg + seg) * NP + el0, P, e);
   const int nw = (nt + 63) >> 6, wave = tid >> 6;
   const bool full = nt >= 64;
-  constexpr bool kFull = P >= 32;  // N >= 16: at least 64 threads
   constexpr int RP = R * P;
 #pragma nounroll
   for (int sb = NSUB - 1; sb >= 0; --sb) {
     const int k0 = t0 + sb * kBwSub;
-    float hist[kBwSub + 1][2][4];
+    float hist[kBwSub + 1][2][W];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) hist[0][v >> 2][v & 3] = sHs[(sb * 8 + v) * nt + tid];
+    for (int v = 0; v < 2 * W; ++v) hist[0][v / W][v % W] = sHs[(sb * 2 * W + v) * nt + tid];
     c.outer(c.sB, c.sX, sb * kBwSub, pq);
 #pragma unroll
     for (int i = 0; i < kBwSub; ++i) {
 #pragma unroll
-      for (int v = 0; v < 8; ++v) hist[i + 1][v >> 2][v & 3] = hist[i][v >> 2][v & 3];
+      for (int v = 0; v < 2 * W; ++v) hist[i + 1][v / W][v % W] = hist[i][v / W][v % W];
       c.step(sb * kBwSub + i + 1, hist[i + 1], pq);
     }
-#pragma unroll
-    for (int i = kBwSub - 1; i >= 0; --i) {
-      const int sl = sb * kBwSub + i + 1, t = k0 + i;
-      const bool valid = t < a.T, last = t >= a.T - 1;
-      const float d = c.sDt[sl], l = c.sLam[sl];
-      const float alpha = __expf(d * c.Ah), beta = (1.f - l) * d, gamma = l * d;
-      const float beta_n = (1.f - c.sLam[sl + 1]) * c.sDt[sl + 1];  // zero past the end
-      const float th = c.sTh[sl * (a.N / 2) + kp];
-      float sn, cn;
-      sincos_step(d * th, sn, cn);
-      float pc[2][4], pp[2][4], cd[2][4];
-      c.outer(c.sB, c.sX, sl, pc);
-      c.outer(c.sB, c.sX, sl - 1, pp);
-      c.outer(c.sC, c.sDY, sl, cd);
-      float s_alpha = 0.f, s_gamma = 0.f, s_beta = 0.f, s_psi = 0.f;
-      float dp[2][4], en[2][4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float g0 = cd[0][j] + e[0][j], g1 = cd[1][j] + e[1][j];
-        const float u0 = __builtin_fmaf(beta, pp[0][j], hist[i][0][j]);
-        const float u1 = __builtin_fmaf(beta, pp[1][j], hist[i][1][j]);
-        const float v0 = cn * u0 - sn * u1, v1 = sn * u0 + cn * u1;  // R U
-        s_alpha += g0 * v0 + g1 * v1;
-        s_psi += g1 * v0 - g0 * v1;
-        const float du0 = alpha * (cn * g0 + sn * g1), du1 = alpha * (cn * g1 - sn * g0);
-        s_gamma += g0 * pc[0][j] + g1 * pc[1][j];
-        s_beta += du0 * pp[0][j] + du1 * pp[1][j];
-        // dP_t = gamma G_t + beta_{t+1} dU_{t+1} (no dU_{t+1} after the last token)
-        const float un0 = last ? 0.f : e[0][j], un1 = last ? 0.f : e[1][j];
-        dp[0][j] = __builtin_fmaf(beta_n, un0, gamma * g0);
-        dp[1][j] = __builtin_fmaf(beta_n, un1, gamma * g1);
-        en[0][j] = du0;
-        en[1][j] = du1;
-      }
-      // sums over the row pair's columns, complete in its last lane
-      s_psi = group_sum_last<gw>(s_psi);
-      s_alpha = group_sum_last<gw>(s_alpha);
-      s_gamma = group_sum_last<gw>(s_gamma);
-      s_beta = group_sum_last<gw>(s_beta);
-      // the row pair's last lane stores its sums (the others into their null
-      // slots, so no branch splits the step)
-      const bool lead = q == gw - 1;
-      *reinterpret_cast<float4*>(lead ? sSc + ((size_t)kp * kBwSub + i) * 4 : sNull) =
-          float4{s_alpha, s_gamma, s_beta, alpha * s_psi * th};
-      *(lead ? sdTh + i * (a.N / 2) + kp : sNull) = alpha * s_psi * d;
-      // per rank: dB = dP x, dC = h_t dy (sums over columns), dx = dP^T B
-      // (sums over the wave's row pairs here, over waves after the block)
-#pragma nounroll
-      for (int r = 0; r < R; ++r) {
-        float xv[4], dyv[4], b0, b1;
-        c.quad(c.sX, sl, r, xv);
-        c.quad(c.sDY, sl, r, dyv);
-        c.pair(c.sB, sl, r, b0, b1);
-        float dB0 = 0.f, dB1 = 0.f, dC0 = 0.f, dC1 = 0.f, dxr[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          dB0 = __builtin_fmaf(dp[0][j], xv[j], dB0);
-          dB1 = __builtin_fmaf(dp[1][j], xv[j], dB1);
-          dC0 = __builtin_fmaf(hist[i + 1][0][j], dyv[j], dC0);
-          dC1 = __builtin_fmaf(hist[i + 1][1][j], dyv[j], dC1);
-          dxr[j] = cross_group_sum<gw>(dp[0][j] * b0 + dp[1][j] * b1, kFull || full);
-        }
-        dB0 = group_sum_last<gw>(dB0);
-        dB1 = group_sum_last<gw>(dB1);
-        dC0 = group_sum_last<gw>(dC0);
-        dC1 = group_sum_last<gw>(dC1);
-        const int o = (i * R + r) * a.N + 2 * kp;
-        *reinterpret_cast<float2*>(lead ? sdB + o : sNull) = float2{dB0, dB1};
-        *reinterpret_cast<float2*>(lead ? sdC + o : sNull + 2) = float2{dC0, dC1};
-        *reinterpret_cast<float4*>((tid & 63) < gw
-                                       ? sDx + ((size_t)(wave * kBwSub + i) * R + r) * P + 4 * q
-                                       : sNull) = float4{dxr[0], dxr[1], dxr[2], dxr[3]};
-      }
-      if (valid) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          e[0][j] = en[0][j];
-          e[1][j] = en[1][j];
-        }
-      }
-    }
+    // this block's half of the partial-sum and output rows (with one half,
+    // a second barrier after the post-pass below)
+    const int hb = sb & (nbuf - 1);
+    float* bDx = sDx + hb * (nw * kBwSub * RP);
+    float* bSc = sSc + hb * ((a.N / 2) * kBwSub * 4);
+    float* bdB = sdB + hb * (kBwSub * R * a.N);
+    float* bdC = sdC + hb * (kBwSub * R * a.N);
+    float* bdTh = sdTh + hb * (kBwSub * (a.N / 2));
+    reverse_block<T, R, P, W>(c, c.sB, c.sC, c.sX, c.sDY, c.sTh, c.sDt, c.sLam, bSc, bDx, bdB, bdC,
+                              bdTh, sNull, sb, k0, a.T, a.N, kp, q, tid, wave, full, hist, e);
     __syncthreads();
     // the block's dx (sums over waves), dB, dC, dtheta rows and per-token
     // scalars (sums over row pairs)
@@ -832,24 +891,24 @@ __global__ void __launch_bounds__(kBwMaxThreads) seg_grads_kernel(BackwardArgs a
     for (int o = tid; o < nv * RP; o += nt) {
       const int i = o / RP, rp = o - i * RP;
       float sum = 0.f;
-      for (int w = 0; w < nw; ++w) sum += sDx[(size_t)(w * kBwSub + i) * RP + rp];
+      for (int w = 0; w < nw; ++w) sum += bDx[(size_t)(w * kBwSub + i) * RP + rp];
       a.dx[(row0 + (size_t)i * a.H) * RP + rp] = sum;
     }
     const int RN = R * a.N;
     for (int o = tid; o < nv * RN; o += nt) {
       const int i = o / RN, rn = o - i * RN;
       const size_t g = (row0 + (size_t)i * a.H) * RN + rn;
-      a.dB[g] = sdB[o];
-      a.dC[g] = sdC[o];
+      a.dB[g] = bdB[o];
+      a.dC[g] = bdC[o];
     }
     for (int o = tid; o < nv * (a.N / 2); o += nt) {
       const int i = o / (a.N / 2), k = o - i * (a.N / 2);
-      a.dtheta[(row0 + (size_t)i * a.H) * (a.N / 2) + k] = sdTh[o];
+      a.dtheta[(row0 + (size_t)i * a.H) * (a.N / 2) + k] = bdTh[o];
     }
     if (tid < 4 * kBwSub) {
       const int i = tid >> 2, cc = tid & 3, t = k0 + i;
       float sum = 0.f;
-      for (int k = 0; k < a.N / 2; ++k) sum += sSc[((size_t)k * kBwSub + i) * 4 + cc];
+      for (int k = 0; k < a.N / 2; ++k) sum += bSc[((size_t)k * kBwSub + i) * 4 + cc];
       const int b4 = tid & ~3;
       const float dal = __shfl(sum, b4), dga = __shfl(sum, b4 + 1), dbe = __shfl(sum, b4 + 2),
                   dth = __shfl(sum, b4 + 3);
@@ -863,7 +922,7 @@ __global__ void __launch_bounds__(kBwMaxThreads) seg_grads_kernel(BackwardArgs a
         a.dAc[tok] = dal * alpha * d;
       }
     }
-    __syncthreads();  // sDx and sSc are rewritten by the next block
+    if (nbuf == 1) __syncthreads();  // the rows are rewritten by the next block
   }
 }
 
@@ -1040,6 +1099,21 @@ __global__ void __launch_bounds__(256) dA_kernel(BackwardArgs a) {
   if (threadIdx.x == 0) a.dA[hh] = s[0];
 }
 
+template <typename T, int R, int P, int W>
+hipError_t launch_grads(const BackwardArgs& a, int nseg, hipStream_t stream) {
+  const int nbuf = bw_seg_buffers(a.S, R, a.N, P, (int)sizeof(T));
+  const BwSegLayout L = bw_seg_layout(a.S, R, a.N, P, (int)sizeof(T), W, nbuf);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&seg_grads_kernel<T, R, P, W>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((seg_grads_kernel<T, R, P, W>), dim3((unsigned)((size_t)a.nb * a.H * nseg)),
+                     dim3(a.N * P / (2 * W)), L.total, stream, a, nseg, nbuf);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dA_kernel, dim3(a.H), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <typename T, int R, int P>
 hipError_t launch_segments(const BackwardArgs& a, hipStream_t stream) {
   const int units = a.nb * a.H;
@@ -1057,15 +1131,10 @@ hipError_t launch_segments(const BackwardArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((seg_chain_kernel<P>), dim3((unsigned)units, 2), block, 0, stream, a, nseg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&seg_grads_kernel<T, R, P>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((seg_grads_kernel<T, R, P>), dim3((unsigned)((size_t)units * nseg)),
-                     block, L.total, stream, a, nseg);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dA_kernel, dim3(a.H), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  // two columns per thread (twice the waves) needs more than the 128 VGPRs
+  // that four waves per SIMD leave, and its spills cost more than the
+  // waves gain, so the pass keeps four
+  return launch_grads<T, R, P, 4>(a, nseg, stream);
 }
 
 template <typename T, int R>

@@ -88,28 +88,30 @@ struct BackwardArgs {
   float *dseg, *psi;
 };
 
-// Segment path of the backward: one workgroup of N P / 8 threads per
+// Segment path of the backward: one workgroup of N P / (2 W) threads per
 // (sequence, head, segment of S tokens); thread (kp, q) holds rows 2 kp,
-// 2 kp + 1 and columns 4 q .. 4 q + 3 of the state.  Tokens are recomputed
-// in blocks of kBwSub.
+// 2 kp + 1 and columns W q .. W q + W - 1 of the state (W = 4).  Tokens are
+// recomputed in blocks of kBwSub.
 constexpr int kBwSub = 8;
-constexpr int kBwMaxThreads = 512;
+constexpr int kBwMaxThreads = 512;  // at W = 4
 
 // LDS of one segment workgroup (byte offsets, 16-aligned): the segment's
-// inputs for tokens t0 - 1 .. t0 + S (S + 2 slots) as stored; for one block,
-// the per-wave dx partials, per-row-pair scalar partials and the dB, dC and
-// dtheta rows; a 16-byte slot per lane that the lanes with nothing to store
-// write instead (so the stores need no branch); each thread's block-entry
-// states.
+// inputs for tokens t0 - 1 .. t0 + S (S + 2 slots) as stored; for nbuf
+// blocks (with two, alternate blocks use alternate halves and one barrier
+// per block suffices), the per-wave dx partials, per-row-pair scalar
+// partials and the dB, dC and dtheta rows; a 16-byte slot per lane that the
+// lanes with nothing to store write instead (so the stores need no branch);
+// each thread's block-entry states.
 struct BwSegLayout {
   int nslot;
   uint32_t wB, wX;  // 32-bit words per token-head row of B (and C), of x (and dy)
   size_t oB, oC, oX, oDY, oTh, oDt, oLam, oDx, oSc, odB, odC, odTh, oNull, oHs, total;
 };
 
-__host__ __device__ inline BwSegLayout bw_seg_layout(int S, int R, int N, int P, int es) {
+__host__ __device__ inline BwSegLayout bw_seg_layout(int S, int R, int N, int P, int es,
+                                                     int W = 4, int nbuf = 1) {
   BwSegLayout l;
-  const int nt = N * P / 8, nw = (nt + 63) / 64;
+  const int nt = N * P / (2 * W), nw = (nt + 63) / 64;
   l.nslot = S + 2;
   l.wB = (uint32_t)(R * N * es / 4);
   l.wX = (uint32_t)(R * P * es / 4);
@@ -126,13 +128,13 @@ __host__ __device__ inline BwSegLayout bw_seg_layout(int S, int R, int N, int P,
   l.oTh = take((size_t)l.nslot * (N / 2) * 4);
   l.oDt = take((size_t)l.nslot * 4);
   l.oLam = take((size_t)l.nslot * 4);
-  l.oDx = take((size_t)nw * kBwSub * R * P * 4);
-  l.oSc = take((size_t)(N / 2) * kBwSub * 16);
-  l.odB = take((size_t)kBwSub * R * N * 4);
-  l.odC = take((size_t)kBwSub * R * N * 4);
-  l.odTh = take((size_t)kBwSub * (N / 2) * 4);
+  l.oDx = take(nbuf * (size_t)nw * kBwSub * R * P * 4);
+  l.oSc = take(nbuf * (size_t)(N / 2) * kBwSub * 16);
+  l.odB = take(nbuf * (size_t)kBwSub * R * N * 4);
+  l.odC = take(nbuf * (size_t)kBwSub * R * N * 4);
+  l.odTh = take(nbuf * (size_t)kBwSub * (N / 2) * 4);
   l.oNull = take(64 * 16);
-  l.oHs = take((size_t)(S / kBwSub) * 8 * nt * 4);
+  l.oHs = take((size_t)(S / kBwSub) * 2 * W * nt * 4);
   l.total = o;
   return l;
 }
@@ -146,6 +148,14 @@ __host__ __device__ inline int bw_segment_len(int R, int N, int P, int es) {
     if (bw_seg_layout(S, R, N, P, es).total <= kLdsLimit) return S;
   return 0;
 }
+
+// Blocks' worth of partial-sum rows the gradient pass keeps at segment
+// length S: 2 where they fit the LDS, else 1.
+__host__ __device__ inline int bw_seg_buffers(int S, int R, int N, int P, int es) {
+  return bw_seg_layout(S, R, N, P, es, 4, 2).total <= kLdsLimit ? 2 : 1;
+}
+
+
 
 // Block-side passes (BCNorm + bias, MIMO projections).
 struct BlockArgs {
