@@ -935,8 +935,13 @@ __global__ void __launch_bounds__(kBwMaxThreads * 4 / W) seg_grads_kernel(Backwa
 // a row pair commute, so over a segment h_end = D R(psi) h_entry + h_local
 // and dU_first = D R(psi)^T E + dU_local, E the adjoint the segment's last
 // token inherits.
+// Eight waves per SIMD (at most 64 VGPRs: four workgroups per CU; float
+// inputs at R = 4 would spill there and keep five); the walks are
+// latency-bound, so resident waves matter more than the registers that hold
+// a step's operands.
 template <typename T, int R, int P>
-__global__ void __launch_bounds__(kBwMaxThreads) seg_local_kernel(BackwardArgs a, int nseg) {
+__global__ void __launch_bounds__(kBwMaxThreads, (R == 4 && sizeof(T) == 4) ? 5 : 8)
+    seg_local_kernel(BackwardArgs a, int nseg) {
   extern __shared__ __align__(16) unsigned char sm[];
   constexpr int es = sizeof(T);
   constexpr int gw = P / 4;
