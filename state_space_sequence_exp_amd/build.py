@@ -4,7 +4,8 @@
 
 compiles every ``csrc/*.hip`` with hipcc for gfx950 (in parallel) and links
 ``state_space_sequence_exp_amd/libm3ssm.so``.  Packed-fp32 VALU instructions
-are disabled for all device code.
+are disabled for all device code; a few prefill sources take a measured
+instruction-scheduling strategy (SCHED).
 """
 from __future__ import annotations
 
@@ -38,6 +39,32 @@ def compile_flags():
             "-Wno-unused-command-line-argument"]
 
 
+# Instruction-scheduling strategy per source file, where a measured one beats
+# the default: the kernels are latency-bound at few waves per SIMD, and
+# LLVM's AMDGPU schedulers trade registers for latency hiding differently
+# per shape.  Cold per-call times against the default on one MI355X:
+# - N = 128 SISO prefill (B1 T16384 H64 P64): 559 -> 515 us, iterative-ilp;
+# - MIMO R = 4 prefill (B4 T4096 H16 N64 P64): 278 -> 274 us, iterative-ilp;
+# - N = 64 SISO prefill (B4 T2048 H16 P64): 67.7 -> 66.2 us,
+#   max-memory-clause (iterative-ilp: 67.8);
+# - decode, S256 H32 N128 P64 R4 bf16: 89.9 -> 87.6 us, and S128 H64 N64
+#   R4 fp32: 57.1 -> 51.0 us, iterative-ilp;
+# - backward, SISO B4 T2048 H16 N64 P64: 1.061 -> 1.044 ms,
+#   max-memory-clause.
+SCHED = {
+    "prefill_bf16_r1.hip": "max-memory-clause",
+    "prefill_bf16_r1_n128.hip": "iterative-ilp",
+    "prefill_bf16_r4.hip": "iterative-ilp",
+    "decode.hip": "iterative-ilp",
+    "backward.hip": "max-memory-clause",
+}
+
+
+def file_flags(src: str):
+    st = SCHED.get(os.path.basename(src))
+    return ["-mllvm", "-amdgpu-sched-strategy=" + st] if st else []
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     hipcc = _hipcc()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
@@ -47,7 +74,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     try:
         def compile_one(src):
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [hipcc] + compile_flags() + ["-c", src, "-o", obj]
+            cmd = [hipcc] + compile_flags() + file_flags(src) + ["-c", src, "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout, r.stderr))

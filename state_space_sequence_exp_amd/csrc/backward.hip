@@ -472,14 +472,14 @@ __global__ void __launch_bounds__(512) token_grads_kernel(BackwardArgs a) {
 // and seg_chain_kernel chains the segments, giving every segment's entry
 // state and exit adjoint.  seg_grads_kernel then takes one workgroup per
 // (batch, head, segment), thread (kp, q) holding rows 2kp, 2kp+1 and
-// columns 4q .. 4q+3 of h and G.  From the entry state it walks the segment
-// forward,
-// keeping each kBwSub-token block's entry state in its own LDS slots; then,
-// block by block from the last, it recomputes the block's states into
-// registers and walks it backward from the segment-exit adjoint, forming
-// every token's gradients as token_grads_kernel does.  Sums over columns
-// run in DPP steps within the row pair's lanes, sums over row pairs across
-// lanes and then waves through LDS, all in a fixed order.
+// columns Wq .. Wq+W-1 of h and G (W = 4).  From the entry state it walks
+// the segment forward, keeping each kBwSub-token block's entry state in its
+// own LDS slots; then, block by block from the last, it recomputes the
+// block's states into registers and walks it backward from the
+// segment-exit adjoint, forming every token's gradients as
+// token_grads_kernel does.  Sums over columns run in DPP steps within the
+// row pair's lanes, sums over row pairs across lanes and then waves through
+// LDS, all in a fixed order.
 
 // Two consecutive elements (a B or C pair) and four (an x or dy quad) of a
 // staged row, as float.

@@ -1506,6 +1506,14 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+}  // namespace pf
+
+// bfloat16, R = 1, N = 128 fixed: compiled on its own
+// (prefill_bf16_r1_n128.hip) so that it can take other scheduling options.
+hipError_t launch_prefill_bf16_r1_n128(const PrefillArgs& a, hipStream_t stream);
+
+namespace pf {
+
 // bfloat16 (the fast path) has instantiations with N fixed for the common
 // state sizes and chunks of at most 64 tokens (every tile geometry a
 // compile-time constant); float32 and other shapes take N at run time.
@@ -1517,7 +1525,9 @@ hipError_t launch_trp(const PrefillArgs& a, hipStream_t stream) {
         fl.items <= kPrefillThreads && fl.xitems <= kPrefillThreads)
       switch (a.N) {
         case 64: return launch_cfg<Cfg<T, R, P, 64>>(a, stream);
-        case 128: return launch_cfg<Cfg<T, R, P, 128>>(a, stream);
+        case 128:
+          if constexpr (R == 1) return launch_prefill_bf16_r1_n128(a, stream);
+          else return launch_cfg<Cfg<T, R, P, 128>>(a, stream);
         default: break;
       }
   }
