@@ -1089,15 +1089,15 @@ __global__ void zero_kernel(float* p, int n) {
 
 // dA[h] = sum over (batch, time) of the per-token contributions, in a fixed
 // order: each thread a strided partial sum, then a tree over the block.
-__global__ void __launch_bounds__(256) dA_kernel(BackwardArgs a) {
-  __shared__ float s[256];
+__global__ void __launch_bounds__(1024) dA_kernel(BackwardArgs a) {
+  __shared__ float s[1024];
   const int hh = blockIdx.x;
   const size_t n = (size_t)a.nb * a.T;
   float v = 0.f;
-  for (size_t i = threadIdx.x; i < n; i += 256) v += a.dAc[i * a.H + hh];
+  for (size_t i = threadIdx.x; i < n; i += 1024) v += a.dAc[i * a.H + hh];
   s[threadIdx.x] = v;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (int w = 512; w > 0; w >>= 1) {
     if ((int)threadIdx.x < w) s[threadIdx.x] += s[threadIdx.x + w];
     __syncthreads();
   }
@@ -1115,7 +1115,7 @@ hipError_t launch_grads(const BackwardArgs& a, int nseg, hipStream_t stream) {
                      dim3(a.N * P / (2 * W)), L.total, stream, a, nseg, nbuf);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dA_kernel, dim3(a.H), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(dA_kernel, dim3(a.H), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1169,7 +1169,7 @@ hipError_t launch_typed(const BackwardArgs& a, hipStream_t stream) {
                      dim3(threads), lds, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dA_kernel, dim3(a.H), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(dA_kernel, dim3(a.H), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
