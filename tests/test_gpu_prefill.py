@@ -58,6 +58,14 @@ SMALL = [
     ("bf16", 1, 90, 2, 256, 32, 1, 32),
     ("bf16", 1, 33, 1, 64, 128, 2, 16),
     ("bf16", 1, 700, 1, 64, 64, 1, 128),
+    # the bf16 R = 1 kernels with N fixed at the head dimensions besides 64
+    # (N = 64: the split output pass at P = 16 and 32; N = 128, which has
+    # its own source file and scheduling strategy, at P = 16 and 32; N P is
+    # at most 8192)
+    ("bf16", 1, 120, 2, 64, 32, 1, 64),
+    ("bf16", 1, 90, 1, 64, 16, 1, 64),
+    ("bf16", 1, 150, 2, 128, 32, 1, 64),
+    ("bf16", 1, 100, 1, 128, 16, 1, 32),
 ]
 
 
