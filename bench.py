@@ -13,12 +13,17 @@ none of the step's data, timed with HIP events on the stream the kernels run
 on.  The same line carries, measured in the same run:
 
   roofline      the prefill path against the HBM roofline (algorithmic bytes
-                per call / measured call duration, peak 8 TB/s)
+                per call / measured call duration, peak 8 TB/s), also as a
+                fraction of the measured copy bandwidth
   cpu_baseline  the fp64 oracle on the host cores for the same workload
-  secondary     MIMO R=4 prefill (B4 T4096 H16 N64 P64), long-context SISO
-                prefill (B1 T16384 H64 N128 P64) and the decode step
-                (256 sequences x 32 heads, N128 P64 R4; us/step and HBM GB/s
-                with its own roofline)
+  device_anchors  this GPU's measured copy bandwidth (512 MiB) and bf16
+                GEMM rate, beside the published peaks
+  secondary     the tiny fp32 workload (latency), MIMO R=4 prefill (B4 T4096
+                H16 N64 P64), long-context SISO prefill (B1 T16384 H64 N128
+                P64) and the decode step (256 sequences x 32 heads, N128 P64
+                R4; us/step and HBM GB/s with its own roofline), each with
+                the oracle's CPU baseline; the decode-latency sweep, the
+                block-side passes and the backward
 
 Inputs follow the seeded recipe of state_space_sequence_exp_amd.inputs.
 """
@@ -348,6 +353,12 @@ def time_prefill(cfg, g, steps, warmup, flush=True):
     e0.record()
     torch.cuda.synchronize()
     b2b = s0.elapsed_time(e0) / steps
+    if ws_bytes > 0:
+        err = m3.prefill_workspace_error(ws)
+        if err != 0:
+            raise RuntimeError("prefill chain error word %d after the timed calls of %s "
+                               "(a timed-out wait or dirty counters): outputs invalid"
+                               % (err, cfg.name))
     del scratch
     return times, b2b
 
@@ -380,16 +391,31 @@ def time_decode(cfg, g, steps, warmup):
     return reps[len(reps) // 2]
 
 
+def host_cpu():
+    """(cores this process may run on, cores the oracle uses, CPU model)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    # one GPU's share of the host: at most 16 worker threads
+    return avail, max(1, min(avail, 16)), model
+
+
 def cpu_baseline(cfg, inp, budget_s=20.0):
     """The fp64 oracle on the host cores: whole (b, h) units of the same
     workload, as many as fit the time budget; scaled to tokens/s of the full
     workload (units are independent)."""
     import oracle
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+    avail, cores, model = host_cpu()
     nunits = cfg.batch * cfg.nheads
     # calibrate with one wave of `cores` units, then run a sample within budget
     n = min(nunits, cores)
@@ -417,9 +443,103 @@ def cpu_baseline(cfg, inp, budget_s=20.0):
         dt = (time.perf_counter() - t0) / reps
     full_time = dt * nunits / n
     return {"value": cfg.batch * cfg.seqlen / full_time, "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cores_available": avail, "cores_capped_at": 16,
+            "cpu_model": model,
             "sample": "%d of %d (batch, head) units over all %d tokens, fp64 C oracle, "
-                      "%d run(s) of %.2f s" % (n, nunits, cfg.seqlen, reps, dt)}
+                      "%d run(s) of %.3f s" % (n, nunits, cfg.seqlen, reps, dt)}
+
+
+def cpu_baseline_decode(cfg, inp, steps=10):
+    """The fp64 oracle's decode step on the full batch (every sequence and
+    head), timed over `steps` consecutive steps: us per step."""
+    import numpy as np
+    import oracle
+    avail, cores, model = host_cpu()
+    K = inp["x"].shape[0]
+    h = inp["h0"].astype(np.float64)
+    t0 = time.perf_counter()
+    for t in range(steps):
+        cur, prev = t % K, (t - 1) % K
+        _, h = oracle.decode_step(h, inp["x"][cur], inp["x"][prev], inp["B"][cur],
+                                  inp["B"][prev], inp["C"][cur], inp["dt"][cur], inp["A"],
+                                  inp["lam"][cur], inp["theta"][cur], nthreads=cores)
+    us = (time.perf_counter() - t0) / steps * 1e6
+    return {"value": us, "unit": "us/step", "cores": cores, "kind": "oracle",
+            "cores_available": avail, "cores_capped_at": 16, "cpu_model": model,
+            "sample": "full batch (%d sequences x %d heads), %d consecutive steps"
+                      % (cfg.batch, cfg.nheads, steps)}
+
+
+def device_anchors(log):
+    """Measured peaks of this GPU, beside the published ones: a 512 MiB
+    device-to-device copy (read + write, GB/s) and a large bf16 GEMM
+    (TFLOP/s), each the median of several event-timed repeats."""
+    import ctypes
+    import numpy as np
+    import torch
+    n = 512 * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    probe = ctypes.CDLL(os.path.join(ROOT, "state_space_sequence_exp_amd", "libm3probe.so"))
+    probe.m3probe_copy.restype = ctypes.c_int
+    probe.m3probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_void_p]
+
+    def probe_copy():
+        rc = probe.m3probe_copy(src.data_ptr(), dst.data_ptr(), n * 4,
+                                torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError("copy probe failed: %d" % rc)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record()
+            fn()
+            e0.record()
+            torch.cuda.synchronize()
+            ts.append(s0.elapsed_time(e0))
+        return float(np.median(ts))
+
+    ms = timed(probe_copy)
+    copy_gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
+    if not torch.equal(dst[: 1 << 20], src[: 1 << 20]):
+        raise RuntimeError("copy probe produced wrong data")
+    tms = timed(lambda: dst.copy_(src))
+    torch_gbs = 2 * n * 4 / (tms * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device="cuda:0").to(torch.bfloat16)
+    b = torch.randn(m, m, device="cuda:0").to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(10):
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        torch.matmul(a, b)
+        e0.record()
+        torch.cuda.synchronize()
+        ts.append(s0.elapsed_time(e0))
+    gms = float(np.median(ts))
+    tflops = 2 * m ** 3 / (gms * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    log("anchors: copy %.0f GB/s (torch copy_ %.0f), bf16 GEMM %.0f TFLOP/s"
+        % (copy_gbs, torch_gbs, tflops))
+    return {"hbm_copy_gbs": copy_gbs,
+            "hbm_copy": "512 MiB device-to-device copy (read + write) by a streaming HIP "
+                        "kernel (libm3probe, 16-byte non-temporal loads and stores), median of "
+                        "10, %.3f ms" % ms,
+            "torch_copy_gbs": torch_gbs,
+            "bf16_gemm_tflops": tflops,
+            "bf16_gemm": "torch.matmul bf16 %dx%dx%d, median of 10, %.3f ms" % (m, m, m, gms),
+            "hbm_peak_spec_gbs": HBM_PEAK_GBS, "bf16_peak_spec_tflops": BF16_PEAK_TFLOPS}
 
 
 def counter_sequence():
@@ -489,6 +609,10 @@ def main():
         counter_sequence()
         return
 
+    # measured peaks of this GPU (context for every fraction below)
+    anchors = device_anchors(log)
+    copy_gbs = anchors["hbm_copy_gbs"]
+
     # ---- headline: SISO prefill (configuration 1) ----
     cfg = I.WORKLOADS[1]
     log("generating %s" % cfg.name)
@@ -522,8 +646,10 @@ def main():
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": nbytes,
+                     "frac_of_measured_copy": achieved / copy_gbs,
                      "mfma_frac": prefill_flops(cfg) / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "prefill_ms_back_to_back_no_flush": b2b,
+        "device_anchors": anchors,
     }
 
     if not args.no_cpu_baseline:
@@ -534,12 +660,22 @@ def main():
 
     if not args.no_secondary:
         sec = {}
+        # configuration 0: latency only (a few hundred tokens: launch-bound)
+        c = I.WORKLOADS[0]
+        ii = I.config_inputs(0)
+        gg = upload(ii)
+        log("timing prefill %s" % c.name)
+        tt, bb = time_prefill(c, gg, args.steps, args.warmup, flush=not args.no_flush)
+        sec[c.name] = {"us": float(np.median(tt)) * 1e3, "us_back_to_back_no_flush": bb * 1e3,
+                       "tokens_per_s": c.batch * c.seqlen / (float(np.median(tt)) * 1e-3)}
+        if not args.no_cpu_baseline:
+            sec[c.name]["cpu_baseline"] = cpu_baseline(c, ii, budget_s=2.0)
+        del gg, ii
         for idx in (2, 3):
             c = I.WORKLOADS[idx]
             log("generating %s" % c.name)
             ii = I.config_inputs(idx)
             gg = upload(ii)
-            del ii
             steps = max(3, args.steps // 2)
             log("timing prefill %s" % c.name)
             tt, bb = time_prefill(c, gg, steps, max(1, args.warmup // 2), flush=not args.no_flush)
@@ -548,15 +684,19 @@ def main():
             sec[c.name] = {"tokens_per_s": c.batch * c.seqlen / (m * 1e-3), "ms": m,
                            "ms_back_to_back_no_flush": bb, "hbm_gbs": nb / (m * 1e-3) / 1e9,
                            "hbm_frac": nb / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "hbm_frac_of_measured_copy": nb / (m * 1e-3) / 1e9 / copy_gbs,
                            "mfma_frac": prefill_flops(c) / (m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                            "algorithmic_bytes": nb, "chunk": c.chunk}
             del gg
             torch.cuda.empty_cache()
+            if not args.no_cpu_baseline:
+                log("cpu baseline %s" % c.name)
+                sec[c.name]["cpu_baseline"] = cpu_baseline(c, ii, budget_s=10.0)
+            del ii
         c = I.WORKLOADS[4]
         log("generating %s" % c.name)
         ii = I.decode_config_inputs()
         gg = upload(ii)
-        del ii
         log("timing decode: %d steps x 3" % args.decode_steps)
         us = time_decode(c, gg, args.decode_steps, 10) * 1e3
         nb = decode_bytes(c)
@@ -566,7 +706,14 @@ def main():
                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                     "frac": gbs / HBM_PEAK_GBS,
                                     "traffic": measured_traffic("decode_config4"),
-                                    "algorithmic_bytes": nb}}
+                                    "algorithmic_bytes": nb,
+                                    "frac_of_measured_copy": gbs / copy_gbs}}
+        del gg
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            log("cpu baseline decode")
+            sec[c.name]["cpu_baseline"] = cpu_baseline_decode(c, ii, steps=10)
+        del ii
         if not args.no_decode_sweep:
             sec["decode_sweep_b128_h64_p64"] = decode_sweep(20, log)
         if not args.no_block:

@@ -61,14 +61,16 @@
 extern "C" {
 #endif
 
-#define M3SSM_VERSION 120 /* 1.2.0 */
+#define M3SSM_VERSION 130 /* 1.3.0 */
 
 typedef enum {
   M3_SUCCESS = 0,
   M3_ERR_INVALID_VALUE = 1, /* null pointer, bad size, misalignment, bad chunk */
   M3_ERR_NOT_SUPPORTED = 2, /* valid but outside the compiled shape set */
   M3_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
-  M3_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+  M3_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
+  M3_ERR_CHAIN = 5          /* a prefill workspace's error word is set (see
+                               m3_prefill_workspace_error) */
 } m3_status;
 
 typedef enum {
@@ -131,10 +133,24 @@ size_t m3_prefill_workspace_size(const m3_dims* dims, int chunk, m3_dtype dtype)
  * zero-filled once serves every later call as long as batch * nheads <=
  * 1020 (then 4 + G <= 1024 words), or as long as no call has more segments
  * than the call before it on this buffer; otherwise zero the counter bytes
- * before the call.  The error word is left nonzero, and stays so, if a
- * segment ever waited beyond its bounded spin for a predecessor (1), or if a
- * call found the counters not zero on entry (2; that call computes
- * nothing).  Concurrent calls need distinct workspaces.
+ * before the call.
+ *
+ * Chain errors.  The error word is left nonzero, and stays so until cleared
+ * (m3_prefill_workspace_error), when:
+ *  1  a segment waited beyond its bounded spin (about a quarter of a second)
+ *     for a predecessor.  Its entry state is then unknown: it continues from
+ *     NaN, so its y, every state it hands on (hence the rest of that
+ *     sequence's y) and h_final are NaN.
+ *  2  the counters were not zero on entry, as seen by a workgroup whose
+ *     ticket lies past the grid (the ticket word was not zero) or whose own
+ *     status word was not zero.  That workgroup computes nothing; others may
+ *     then time out (1).  A nonzero finished-workgroup word (word 2) is not
+ *     detected: it makes the reset at the end of the call happen early or
+ *     not at all, so zero-fill the counter bytes after any call that did not
+ *     finish normally.
+ * m3_prefill returns once the work is enqueued, so it cannot report these;
+ * m3_prefill_workspace_error reads the word back.  Concurrent calls need
+ * distinct workspaces.
  *
  * Returns M3_SUCCESS once the kernel is enqueued (one launch per call).  y and h_final must not
  * overlap the inputs.  batch == 0 or seqlen == 0 enqueues nothing (h_final,
@@ -144,6 +160,19 @@ m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void*
                      const float* dt, const float* A, const float* lam, const float* theta,
                      const void* B, const void* C, void* y, float* h_final, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * Error word of a prefill workspace (see "Chain errors" above), read once
+ * all work enqueued on `stream` so far has finished: this call synchronises
+ * `stream` (so it cannot be captured into a graph).  Stores the word in
+ * *error_word if error_word is not NULL and, if `clear` is nonzero and the
+ * word is not 0, resets it to 0.  Returns M3_SUCCESS for a zero word,
+ * M3_ERR_CHAIN for a nonzero one, M3_ERR_INVALID_VALUE if workspace is NULL,
+ * not 256-byte aligned or smaller than 16 bytes (nothing is enqueued then),
+ * and M3_ERR_HIP if a HIP call fails.
+ */
+m3_status m3_prefill_workspace_error(void* workspace, size_t workspace_bytes, int clear,
+                                     int* error_word, void* stream);
 
 /*
  * Prefill that continues a sequence: the same computation as m3_prefill, but

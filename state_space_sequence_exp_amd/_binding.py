@@ -19,12 +19,13 @@ M3_ERR_INVALID_VALUE = 1
 M3_ERR_NOT_SUPPORTED = 2
 M3_ERR_WORKSPACE = 3
 M3_ERR_HIP = 4
+M3_ERR_CHAIN = 5
 M3_F32 = 0
 M3_BF16 = 1
 
 # every function declared in include/m3ssm.h
 ABI_SYMBOLS = ("m3_version", "m3_status_string", "m3_prefill_workspace_size", "m3_prefill",
-               "m3_prefill_from_state", "m3_decode_step", "m3_block_prepass", "m3_block_postpass",
+               "m3_prefill_workspace_error", "m3_prefill_from_state", "m3_decode_step", "m3_block_prepass", "m3_block_postpass",
                "m3_backward_workspace_size", "m3_backward")
 
 
@@ -64,6 +65,9 @@ def load_library(path: Optional[str] = None):
     lib.m3_prefill.restype = ctypes.c_int
     lib.m3_prefill.argtypes = [dp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp,
                                vp, vp, ctypes.c_size_t, vp]
+    lib.m3_prefill_workspace_error.restype = ctypes.c_int
+    lib.m3_prefill_workspace_error.argtypes = [vp, ctypes.c_size_t, ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_int), vp]
     lib.m3_prefill_from_state.restype = ctypes.c_int
     lib.m3_prefill_from_state.argtypes = [dp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp,
                                           vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -137,9 +141,23 @@ def prefill_workspace_size(batch, seqlen, nheads, P, N, R, chunk, dtype) -> int:
     return int(load_library().m3_prefill_workspace_size(ctypes.byref(d), int(chunk), code))
 
 
+def prefill_workspace_error(workspace, *, clear: bool = False, stream=None) -> int:
+    """The error word of a prefill workspace once the stream's work has
+    finished (m3_prefill_workspace_error; synchronises the stream): 0 when
+    every chain wait completed, 1 after a timed-out wait (outputs NaN), 2
+    after dirty counters.  With clear=True a nonzero word is reset."""
+    word = ctypes.c_int(0)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().m3_prefill_workspace_error(_ptr(workspace), nbytes, int(bool(clear)),
+                                                   ctypes.byref(word), _stream(stream))
+    if st not in (M3_SUCCESS, M3_ERR_CHAIN):
+        raise M3Error(st, "m3_prefill_workspace_error")
+    return int(word.value)
+
+
 def prefill(x, dt, A, lam, theta, B, C, chunk: int, *, h0=None, x_prev=None, B_prev=None,
             y=None, h_final=None, want_h_final: bool = True, workspace=None,
-            stream=None) -> Tuple:
+            check: bool = False, stream=None) -> Tuple:
     """Chunked prefill on the GPU.
 
     x [Bt,T,H,R,P] (or [Bt,T,H,P] for R=1); B, C [Bt,T,H,R,N] (or [Bt,T,H,N]);
@@ -151,6 +169,8 @@ def prefill(x, dt, A, lam, theta, B, C, chunk: int, *, h0=None, x_prev=None, B_p
     first token) and/or x_prev [Bt,H,R,P] with B_prev [Bt,H,R,N] (the
     previous token's x and B, x's dtype; R axis optional for R=1); this calls
     m3_prefill_from_state.  h_final may be h0 (in-place update).
+    check=True synchronises the stream after the call and raises M3Error
+    (M3_ERR_CHAIN) if the workspace's error word is set.
     Returns (y with x's shape and dtype, h_final [Bt,H,N,P] float32 or None).
     """
     import torch
@@ -206,6 +226,9 @@ def prefill(x, dt, A, lam, theta, B, C, chunk: int, *, h0=None, x_prev=None, B_p
                             _ptr(workspace), ws_bytes, _stream(stream))
     if st != M3_SUCCESS:
         raise M3Error(st, "m3_prefill_from_state" if cont else "m3_prefill")
+    if check and workspace is not None:
+        if prefill_workspace_error(workspace, stream=stream) != 0:
+            raise M3Error(M3_ERR_CHAIN, "m3_prefill_from_state" if cont else "m3_prefill")
     return y, h_final
 
 

@@ -65,7 +65,10 @@ def file_flags(src: str):
     return ["-mllvm", "-amdgpu-sched-strategy=" + st] if st else []
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def build(verbose: bool = False, jobs: int = 8, extra_flags=(), out: str = LIB_PATH) -> str:
+    """Compile every source and link the shared library at `out` (default:
+    the in-tree libm3ssm.so).  extra_flags go to every compile line (for
+    instance host-only sanitizer flags, each behind -Xarch_host)."""
     hipcc = _hipcc()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
@@ -74,7 +77,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     try:
         def compile_one(src):
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [hipcc] + compile_flags() + file_flags(src) + ["-c", src, "-o", obj]
+            cmd = ([hipcc] + compile_flags() + file_flags(src) + list(extra_flags)
+                   + ["-c", src, "-o", obj])
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout, r.stderr))
@@ -84,16 +88,32 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
         with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
             objs = list(ex.map(compile_one, srcs))
-        out_tmp = LIB_PATH + ".tmp%d" % os.getpid()
+        out_tmp = out + ".tmp%d" % os.getpid()
         cmd = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", out_tmp] + objs
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))
-        os.replace(out_tmp, LIB_PATH)
+        os.replace(out_tmp, out)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB_PATH
+    return out
+
+
+PROBE_SRC = os.path.join(CSRC, "probe", "copy_probe.hip")
+PROBE_PATH = os.path.join(PKG, "libm3probe.so")
+
+
+def build_probe() -> str:
+    """The copy kernel that anchors bandwidth measurements (libm3probe.so)."""
+    out_tmp = PROBE_PATH + ".tmp%d" % os.getpid()
+    cmd = [_hipcc()] + compile_flags() + ["-shared", PROBE_SRC, "-o", out_tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (PROBE_SRC, r.stdout, r.stderr))
+    os.replace(out_tmp, PROBE_PATH)
+    return PROBE_PATH
 
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe())

@@ -4,6 +4,7 @@
 // nothing.
 #include <limits.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "m3_internal.h"
 #include "m3ssm.h"
@@ -18,6 +19,19 @@ bool valid_p(int64_t P) { return P == 16 || P == 32 || P == 64 || P == 128; }
 bool valid_r(int64_t R) { return R == 1 || R == 2 || R == 4; }
 
 size_t esize_of(m3_dtype d) { return d == M3_BF16 ? 2 : 4; }
+
+// The C callers may pass any int for an enum parameter; in C++ reading an
+// enum object that holds a value outside its enumerators' range is undefined,
+// so the public entry points first read the object's bytes as an int.
+int enum_bits(const void* e) {
+  int v;
+  memcpy(&v, e, sizeof v);
+  return v;
+}
+bool dtype_ok(const m3_dtype* d) {
+  const int v = enum_bits(d);
+  return v == M3_F32 || v == M3_BF16;
+}
 
 // Shape checks shared by prefill and its workspace query.
 m3_status check_prefill_shape(const m3_dims* d, int chunk, m3_dtype dtype) {
@@ -81,18 +95,41 @@ extern "C" {
 int m3_version(void) { return M3SSM_VERSION; }
 
 const char* m3_status_string(m3_status s) {
-  switch (s) {
+  switch (enum_bits(&s)) {
     case M3_SUCCESS: return "M3_SUCCESS: no error";
     case M3_ERR_INVALID_VALUE:
       return "M3_ERR_INVALID_VALUE: null pointer, bad size, misaligned pointer or bad chunk";
     case M3_ERR_NOT_SUPPORTED: return "M3_ERR_NOT_SUPPORTED: shape outside the compiled set";
     case M3_ERR_WORKSPACE: return "M3_ERR_WORKSPACE: workspace missing or too small";
     case M3_ERR_HIP: return "M3_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case M3_ERR_CHAIN:
+      return "M3_ERR_CHAIN: a prefill chain wait timed out (outputs NaN) or the workspace "
+             "counters were dirty on entry";
   }
   return "unknown m3_status";
 }
 
+m3_status m3_prefill_workspace_error(void* workspace, size_t workspace_bytes, int clear,
+                                     int* error_word, void* stream) {
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < 16) return M3_ERR_INVALID_VALUE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int* word = static_cast<int*>(workspace) + 1;  // word 1 of the counters
+  int host = 0;
+  if (hipMemcpyAsync(&host, word, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return M3_ERR_HIP;
+  if (error_word) *error_word = host;
+  if (host != 0 && clear) {
+    static const int kZero = 0;
+    if (hipMemcpyAsync(word, &kZero, sizeof(int), hipMemcpyHostToDevice, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return M3_ERR_HIP;
+  }
+  return host == 0 ? M3_SUCCESS : M3_ERR_CHAIN;
+}
+
 size_t m3_prefill_workspace_size(const m3_dims* dims, int chunk, m3_dtype dtype) {
+  if (!dtype_ok(&dtype)) return 0;
   if (check_prefill_shape(dims, chunk, dtype) != M3_SUCCESS) return 0;
   if (dims->batch == 0 || dims->seqlen == 0) return 0;
   return carve(dims, chunk, dtype).total;
@@ -187,6 +224,7 @@ m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void*
                      const float* dt, const float* A, const float* lam, const float* theta,
                      const void* B, const void* C, void* y, float* h_final, void* workspace,
                      size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(&dtype)) return M3_ERR_INVALID_VALUE;
   return prefill_impl(dims, dtype, chunk, nullptr, nullptr, nullptr, x, dt, A, lam, theta, B, C,
                       y, h_final, workspace, workspace_bytes, stream);
 }
@@ -197,6 +235,7 @@ m3_status m3_prefill_from_state(const m3_dims* dims, m3_dtype dtype, int chunk, 
                                 const float* theta, const void* B, const void* C, void* y,
                                 float* h_final, void* workspace, size_t workspace_bytes,
                                 void* stream) {
+  if (!dtype_ok(&dtype)) return M3_ERR_INVALID_VALUE;
   return prefill_impl(dims, dtype, chunk, h0, x_prev, B_prev, x, dt, A, lam, theta, B, C, y,
                       h_final, workspace, workspace_bytes, stream);
 }
@@ -205,6 +244,7 @@ m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in,
                          const void* x_t, const void* x_prev, const void* B_t,
                          const void* B_prev, const void* C_t, const float* dt, const float* A,
                          const float* lam, const float* theta, void* y_t, void* stream) {
+  if (!dtype_ok(&dtype)) return M3_ERR_INVALID_VALUE;
   if (!dims) return M3_ERR_INVALID_VALUE;
   if (dtype != M3_F32 && dtype != M3_BF16) return M3_ERR_INVALID_VALUE;
   const m3_dims* d = dims;
@@ -296,6 +336,7 @@ m3_status m3_block_prepass(const m3_dims* dims, m3_dtype dtype, const void* x, c
                            const void* C, const float* norm_B, const float* norm_C,
                            const float* bias_B, const float* bias_C, const float* up, float eps,
                            void* x_out, void* B_out, void* C_out, void* stream) {
+  if (!dtype_ok(&dtype)) return M3_ERR_INVALID_VALUE;
   const m3_status st = check_block_dims(dims, dtype);
   if (st != M3_SUCCESS) return st;
   if (!(eps >= 0.f) || !(eps < 3.0e38f)) return M3_ERR_INVALID_VALUE;  // also rejects NaN
@@ -326,6 +367,7 @@ m3_status m3_block_prepass(const m3_dims* dims, m3_dtype dtype, const void* x, c
 
 m3_status m3_block_postpass(const m3_dims* dims, m3_dtype dtype, const void* y,
                             const float* down, void* y_out, void* stream) {
+  if (!dtype_ok(&dtype)) return M3_ERR_INVALID_VALUE;
   const m3_status st = check_block_dims(dims, dtype);
   if (st != M3_SUCCESS) return st;
   m3::BlockArgs a = block_args(dims);
@@ -399,6 +441,7 @@ BwCarve bw_carve(const m3_dims* d, m3_dtype dtype) {
 extern "C" {
 
 size_t m3_backward_workspace_size(const m3_dims* dims, m3_dtype dtype) {
+  if (!dtype_ok(&dtype)) return 0;
   if (check_backward_dims(dims, dtype) != M3_SUCCESS) return 0;
   if (dims->batch == 0 || dims->seqlen == 0) return 0;
   return bw_carve(dims, dtype).total;
@@ -409,6 +452,7 @@ m3_status m3_backward(const m3_dims* dims, m3_dtype dtype, const void* x, const 
                       const void* C, const void* dy, const float* dh_final, float* dx,
                       float* ddt, float* dA, float* dlam, float* dtheta, float* dB, float* dC,
                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(&dtype)) return M3_ERR_INVALID_VALUE;
   const m3_status st = check_backward_dims(dims, dtype);
   if (st != M3_SUCCESS) return st;
   const uintptr_t es = esize_of(dtype);

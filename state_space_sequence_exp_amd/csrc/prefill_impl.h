@@ -291,7 +291,9 @@ __device__ __forceinline__ void scalar_loads(const PrefillArgs& a, const Ctx& s,
                                              float (&wd)[3], float (&wl)[3]) {
   const int t0 = c * a.L;
   const size_t hrow = ((size_t)s.b * a.T + t0) * a.H + s.h;
-  const uint32_t bytes = (uint32_t)(a.T - t0 - 1) * s.rowDt + 4;
+  // the range covers the 3 * 64 tokens read at most (a range over the rest of
+  // the sequence could wrap 32 bits on long sequences with many heads)
+  const uint32_t bytes = (uint32_t)(min(a.T - t0, 3 * kWave) - 1) * s.rowDt + 4;
   const rsrc rw = make_rsrc(a.dt + hrow, bytes);
   const rsrc rl = a.lam ? make_rsrc(a.lam + hrow, bytes) : make_rsrc(nullptr, 0);
 #pragma unroll
@@ -1332,7 +1334,17 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     // previous group's exit state
     const bool ok = wait_statuses(a, (s.seg - 1) * BH + s.bh, BH, nprev,
                                   g0 > 0 ? (g0 - 1) * BH + s.bh : -1, s_misc + 2);
-    if (ok) {
+    if (!ok) {
+      // a wait timed out (error word 1): the entry state is unknown, so the
+      // segment continues from NaN and every y it writes, every state it
+      // publishes and h_final are NaN -- a failed call cannot pass for a
+      // correct one
+#pragma unroll
+      for (int q = 0; q < kMaxStTiles; ++q) {
+        const float qn = __builtin_nanf("");
+        ent[q] = f32x4{qn, qn, qn, qn};
+      }
+    } else {
       // newest first, several aggregates' loads in flight at a time (fewer
       // with more state per wave: registers)
       constexpr int NB = C::NC == 64 ? kBatch : (C::NC != 0 ? kBatch / 2 : 1);
@@ -1442,11 +1454,20 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
   }
 }
 
-// The workgroup's ticket (its segment).  A ticket outside the grid means the
-// counters were not zero at entry: the caller reports it (bad_ticket) and
-// touches nothing else.  s_misc: two ints of LDS.
+// The workgroup's ticket (its segment), or -1.  Only the holder of a ticket
+// writes its status word, and the previous call's last workgroup zeroed it,
+// so the word is zero here on a clean workspace.  A ticket outside the grid
+// (the ticket word was not zero at entry) or a nonzero status word of its
+// own means dirty counters: the caller reports it (bad_ticket) and touches
+// nothing else.  s_misc: two ints of LDS.
 __device__ __forceinline__ int take_ticket(const PrefillArgs& a, int* s_misc) {
-  if (threadIdx.x == 0) s_misc[0] = atomicAdd(a.ticket, 1);
+  if (threadIdx.x == 0) {
+    int t = atomicAdd(a.ticket, 1);
+    if (t >= 0 && t < (int)gridDim.x &&
+        __hip_atomic_load(a.status + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+      t = -1;
+    s_misc[0] = t;
+  }
   __syncthreads();
   return s_misc[0];
 }

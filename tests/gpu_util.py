@@ -75,8 +75,9 @@ def gpu_prefill(inp, chunk, dev_inp=None, calls=1):
         y, hf = m3.prefill(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"], chunk,
                            workspace=ws)
     if need > 0:
+        err = m3.prefill_workspace_error(ws)
+        assert err == 0, "error word set: %d" % err
         words = ws[:4 * counter_words(nb, nt, nh, chunk)].view(torch.int32).cpu().numpy()
-        assert words[1] == 0, "error word set: %d" % words[1]
         assert not words.any(), "chain counters not reset: %s" % words
     return y, hf
 
@@ -88,6 +89,8 @@ def oracle_prefill(inp, units=None):
 
 
 def oracle_threads():
+    """Host threads for the oracle: the cores this process may run on, at
+    most 16 (the CPU share that goes with one GPU on the test machines)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -105,6 +108,27 @@ def worst_unit_rel(y, y_ref):
     """Worst rel-L2 over (b, h) units of a [B,T,H,...] output."""
     nb, _, nh = y.shape[:3]
     return max(rel_l2(y[b, :, h], y_ref[b, :, h]) for b in range(nb) for h in range(nh))
+
+
+def worst_state_rel(h, h_ref):
+    """Worst rel-L2 over (b, h) units of a [B,H,N,P] state (0 where the
+    reference state is exactly zero and so is the result)."""
+    nb, nh = h.shape[:2]
+    worst = 0.0
+    for b in range(nb):
+        for k in range(nh):
+            den = np.linalg.norm(h_ref[b, k])
+            num = np.linalg.norm(h[b, k] - h_ref[b, k])
+            worst = max(worst, num / den if den > 0 else (0.0 if num == 0 else np.inf))
+    return float(worst)
+
+
+# parity results of this session, printed in the terminal summary (conftest)
+PARITY = []
+
+
+def record_parity(label, **errs):
+    PARITY.append((label, errs))
 
 
 def log(msg):

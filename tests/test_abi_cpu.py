@@ -40,11 +40,25 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.m3_version() == 120
-    for code in range(5):
+    assert lib.m3_version() == 130
+    for code in range(6):
         s = m3.status_string(code)
         assert s.startswith("M3_")
     assert "unknown" in m3.status_string(99)
+
+
+def test_workspace_error_validation(lib):
+    """Invalid workspaces are rejected on the host, before any HIP call."""
+    word = ctypes.c_int(-7)
+    f = lib.m3_prefill_workspace_error
+    assert f(None, 4096, 0, ctypes.byref(word), None) == m3.M3_ERR_INVALID_VALUE
+    buf = ctypes.create_string_buffer(4096 + 512)
+    base = ctypes.addressof(buf)
+    aligned = (base + 255) // 256 * 256
+    assert f(ctypes.c_void_p(aligned + 4), 4096, 0, ctypes.byref(word), None) == \
+        m3.M3_ERR_INVALID_VALUE
+    assert f(ctypes.c_void_p(aligned), 8, 0, ctypes.byref(word), None) == m3.M3_ERR_INVALID_VALUE
+    assert word.value == -7
 
 
 def dims(b=1, t=64, h=1, p=16, n=16, r=1):

@@ -5,8 +5,8 @@ import pytest
 
 from state_space_sequence_exp_amd import inputs as I
 
-from gpu_util import (TOL, from_gpu, gpu_prefill, log, oracle_prefill, oracle_threads, rel_l2,
-                      to_gpu_f32, to_gpu_storage, upload_prefill)
+from gpu_util import (TOL, from_gpu, gpu_prefill, log, oracle_prefill, oracle_threads, record_parity,
+                      rel_l2, to_gpu_f32, to_gpu_storage, upload_prefill, worst_state_rel)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +71,29 @@ def test_decode_small(case):
     assert ey <= TOL[dtype] and eh <= TOL[dtype]
 
 
+def worst_decode_y(y, y_ref):
+    """Worst rel-L2 over (sequence, head) units of y [S,H,R,P]."""
+    return max(rel_l2(y[s, k], y_ref[s, k]) for s in range(y.shape[0]) for k in range(y.shape[1]))
+
+
+def test_decode_config4_full_batch():
+    """The whole decode workload (256 sequences x 32 heads, N=128, P=64,
+    R=4, bf16) for 32 steps from the seeded initial state, every unit against
+    the oracle: whole-tensor and worst-unit rel-L2 of y and of the state."""
+    inp = I.decode_config_inputs()
+    sel = np.arange(inp["h0"].shape[0])
+    log("decode config4: 32 steps, oracle on the full batch")
+    y, y_ref, h, h_ref, errs = run_decode(inp, 32, sel, record_steps=(0, 15, 31))
+    ey, eh = rel_l2(y, y_ref), rel_l2(h, h_ref)
+    wy, wh = worst_decode_y(y, y_ref), worst_state_rel(h, h_ref)
+    log("   rel_l2 y=%.3e h=%.3e worst-unit y=%.3e h=%.3e; y along the way: %s"
+        % (ey, eh, wy, wh, errs))
+    record_parity("decode config4 full batch, 32 steps", y=ey, h=eh, worst_y=wy, worst_h=wh,
+                  tol=TOL["bf16"])
+    assert max(ey, eh, wy, wh) <= TOL["bf16"]
+    assert all(e <= TOL["bf16"] for _, e in errs)
+
+
 def test_decode_config4_1000_steps():
     """Full batch (256 sequences x 32 heads, N=128, P=64, R=4) on the GPU for
     1000 steps; the oracle follows sequences 0-7 (all heads)."""
@@ -79,9 +102,27 @@ def test_decode_config4_1000_steps():
     log("decode config4: 1000 steps, oracle on sequences 0-7")
     y, y_ref, h, h_ref, errs = run_decode(inp, 1000, sel, record_steps=(0, 1, 2, 499, 999))
     ey, eh = rel_l2(y, y_ref), rel_l2(h, h_ref)
-    log("   rel_l2 y=%.3e h=%.3e; y along the way: %s" % (ey, eh, errs))
-    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    wy, wh = worst_decode_y(y, y_ref), worst_state_rel(h, h_ref)
+    log("   rel_l2 y=%.3e h=%.3e worst-unit y=%.3e h=%.3e; y along the way: %s"
+        % (ey, eh, wy, wh, errs))
+    record_parity("decode config4 sequences 0-7, 1000 steps", y=ey, h=eh, worst_y=wy,
+                  worst_h=wh, tol=TOL["bf16"])
+    assert max(ey, eh, wy, wh) <= TOL["bf16"]
     assert all(e <= TOL["bf16"] for _, e in errs)
+
+
+@pytest.mark.parametrize("dtype,R", [("f32", 1), ("f32", 4), ("bf16", 4)])
+def test_decode_lambda_zero(dtype, R):
+    """lam = 0: the current input enters only through the next step's beta
+    term."""
+    inp = I.decode_inputs(3, 2, 64, 64, R, dtype, ring=4, seed=83 + R)
+    inp["lam"][:] = 0.0
+    log("decode lam=0 %s R=%d" % (dtype, R))
+    sel = np.arange(3)
+    y, y_ref, h, h_ref, _ = run_decode(inp, 6, sel)
+    ey, eh = rel_l2(y, y_ref), rel_l2(h, h_ref)
+    log("   rel_l2 y=%.3e h=%.3e" % (ey, eh))
+    assert ey <= TOL[dtype] and eh <= TOL[dtype]
 
 
 def test_decode_in_place_equals_out_of_place():
