@@ -39,10 +39,11 @@
  *
  * Ownership and threading: every pointer is caller-owned DEVICE memory on the
  * current HIP device, aligned to its element size and further as each call
- * states (vector loads).  The library allocates nothing and
- * keeps no mutable global state; calls enqueue work on `stream` (a
- * hipStream_t; NULL = the default stream) and return without synchronising.
- * Calls on different streams that write different buffers may overlap.
+ * states (vector loads).  The library allocates nothing and, apart from the
+ * per-GPU scratch of m3_prefill_noalloc, keeps no mutable global state;
+ * calls enqueue work on `stream` (a hipStream_t; NULL = the default stream)
+ * and return without synchronising.  Calls on different streams that write
+ * different buffers may overlap.
  *
  * Errors: every argument is validated on the host before anything is
  * enqueued; an invalid call returns an error code and enqueues nothing.  A
@@ -173,6 +174,32 @@ m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void*
  */
 m3_status m3_prefill_workspace_error(void* workspace, size_t workspace_bytes, int clear,
                                      int* error_word, void* stream);
+
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): m3_prefill without a
+ * workspace argument.  The same computation and kernels as m3_prefill; the
+ * workspace is instead a scratch array inside the library, one per GPU (each
+ * GPU the call runs on holds M3_PREFILL_NOALLOC_SCRATCH_BYTES of device
+ * memory from its first such call until the process ends).  The call
+ * allocates nothing: before the prefill kernel it clears the scratch's chain
+ * counters with a small fill kernel (two launches per call; no memset), so
+ * no state carries over between calls.  Every call on one GPU shares that
+ * GPU's scratch: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.  Returns
+ * M3_ERR_WORKSPACE when the shape needs more workspace than the scratch holds
+ * (m3_prefill_workspace_size(dims, chunk, dtype) >
+ * M3_PREFILL_NOALLOC_SCRATCH_BYTES), before any HIP call; otherwise
+ * arguments, layouts, alignment and errors are as for m3_prefill.  A chain
+ * wait that times out shows as NaN outputs (the error word is cleared by the
+ * next call and cannot be read back).
+ */
+#define M3_PREFILL_NOALLOC_SCRATCH_BYTES (32u << 20) /* 32 MiB per GPU */
+
+m3_status m3_prefill_noalloc(const m3_dims* dims, m3_dtype dtype, int chunk, const void* x,
+                             const float* dt, const float* A, const float* lam,
+                             const float* theta, const void* B, const void* C, void* y,
+                             float* h_final, void* stream);
 
 /*
  * Prefill that continues a sequence: the same computation as m3_prefill, but

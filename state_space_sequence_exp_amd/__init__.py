@@ -7,6 +7,7 @@ Python entry points (ctypes; PyTorch tensors supply device memory and the
 current stream):
 
     prefill(x, dt, A, lam, theta, B, C, chunk[, h0, x_prev, B_prev]) -> (y, h_final)
+    prefill_noalloc(x, dt, A, lam, theta, B, C, chunk, y[, h_final])   (no workspace)
     decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta) -> (y_t, h)
     block_prepass(x, B, C, norm_B, norm_C, bias_B, bias_C, up, eps) -> (X, B~, C~)
     block_postpass(y, down) -> y_out
@@ -21,9 +22,10 @@ from ._binding import (ABI_SYMBOLS, LIB_PATH, M3_BF16, M3_ERR_CHAIN, M3_ERR_HIP,
                        M3_ERR_INVALID_VALUE, M3_ERR_NOT_SUPPORTED, M3_ERR_WORKSPACE, M3_F32,
                        M3_SUCCESS, M3Dims, M3Error, backward, backward_workspace_size,
                        block_postpass, block_prepass, decode_step, load_library, prefill,
-                       prefill_workspace_error, prefill_workspace_size, status_string, version)
+                       prefill_noalloc, prefill_workspace_error, prefill_workspace_size,
+                       status_string, version)
 
-__all__ = ["prefill", "decode_step", "block_prepass", "block_postpass", "backward",
+__all__ = ["prefill", "prefill_noalloc", "decode_step", "block_prepass", "block_postpass", "backward",
            "backward_workspace_size", "prefill_workspace_size", "prefill_workspace_error",
            "version", "status_string",
            "load_library", "M3Error", "M3Dims", "ABI_SYMBOLS", "LIB_PATH", "M3_SUCCESS",

@@ -25,7 +25,7 @@ M3_BF16 = 1
 
 # every function declared in include/m3ssm.h
 ABI_SYMBOLS = ("m3_version", "m3_status_string", "m3_prefill_workspace_size", "m3_prefill",
-               "m3_prefill_workspace_error", "m3_prefill_from_state", "m3_decode_step", "m3_block_prepass", "m3_block_postpass",
+               "m3_prefill_workspace_error", "m3_prefill_noalloc", "m3_prefill_from_state", "m3_decode_step", "m3_block_prepass", "m3_block_postpass",
                "m3_backward_workspace_size", "m3_backward")
 
 
@@ -68,6 +68,9 @@ def load_library(path: Optional[str] = None):
     lib.m3_prefill_workspace_error.restype = ctypes.c_int
     lib.m3_prefill_workspace_error.argtypes = [vp, ctypes.c_size_t, ctypes.c_int,
                                                ctypes.POINTER(ctypes.c_int), vp]
+    lib.m3_prefill_noalloc.restype = ctypes.c_int
+    lib.m3_prefill_noalloc.argtypes = [dp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                                       vp, vp, vp, vp]
     lib.m3_prefill_from_state.restype = ctypes.c_int
     lib.m3_prefill_from_state.argtypes = [dp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp,
                                           vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -229,6 +232,46 @@ def prefill(x, dt, A, lam, theta, B, C, chunk: int, *, h0=None, x_prev=None, B_p
     if check and workspace is not None:
         if prefill_workspace_error(workspace, stream=stream) != 0:
             raise M3Error(M3_ERR_CHAIN, "m3_prefill_from_state" if cont else "m3_prefill")
+    return y, h_final
+
+
+# device scratch of m3_prefill_noalloc, per GPU (M3_PREFILL_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def prefill_noalloc(x, dt, A, lam, theta, B, C, chunk: int, y, h_final=None,
+                    stream=None) -> Tuple:
+    """Chunked prefill through m3_prefill_noalloc: no workspace, and nothing
+    allocated by this call (y, and h_final if wanted, are the caller's).  The
+    library's per-GPU scratch stands in for the workspace, so calls that
+    overlap on one GPU race.  Shapes as for prefill()."""
+    import torch
+    lib = load_library()
+    x5 = x.unsqueeze(3) if x.dim() == 4 else x
+    B5 = B.unsqueeze(3) if B.dim() == 4 else B
+    C5 = C.unsqueeze(3) if C.dim() == 4 else C
+    nb, nt, nh, nr, npd = x5.shape
+    nn = B5.shape[-1]
+    dev = x.device
+    code = _dtype_code(x)
+    _check(x5, "x", x.dtype, (nb, nt, nh, nr, npd), dev)
+    _check(B5, "B", x.dtype, (nb, nt, nh, nr, nn), dev)
+    _check(C5, "C", x.dtype, (nb, nt, nh, nr, nn), dev)
+    _check(dt, "dt", torch.float32, (nb, nt, nh), dev)
+    if lam is not None:
+        _check(lam, "lam", torch.float32, (nb, nt, nh), dev)
+    if theta is not None:
+        _check(theta, "theta", torch.float32, (nb, nt, nh, nn // 2), dev)
+    _check(A, "A", torch.float32, (nh,), dev)
+    _check(y, "y", x.dtype, tuple(x.shape), dev)
+    if h_final is not None:
+        _check(h_final, "h_final", torch.float32, (nb, nh, nn, npd), dev)
+    d = _dims(nb, nt, nh, npd, nn, nr)
+    st = lib.m3_prefill_noalloc(ctypes.byref(d), code, int(chunk), _ptr(x5), _ptr(dt), _ptr(A),
+                                _ptr(lam), _ptr(theta), _ptr(B5), _ptr(C5), _ptr(y),
+                                _ptr(h_final), _stream(stream))
+    if st != M3_SUCCESS:
+        raise M3Error(st, "m3_prefill_noalloc")
     return y, h_final
 
 

@@ -6,8 +6,13 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "m3_internal.h"
 #include "m3ssm.h"
+
+// Scratch of m3_prefill_noalloc (see device_scratch below): one copy per GPU.
+static __device__ __align__(256) unsigned char scratch[M3_PREFILL_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -139,11 +144,42 @@ size_t m3_prefill_workspace_size(const m3_dims* dims, int chunk, m3_dtype dtype)
 
 namespace {
 
+// ---- scratch of the no-allocation entry point -----------------------------
+// A file-scope device array: each GPU the library runs on holds its own copy
+// (kNoAllocScratchBytes) until the process ends.  Host code never uses the
+// array's name as an address: the device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and kept here.
+constexpr size_t kNoAllocScratchBytes = M3_PREFILL_NOALLOC_SCRATCH_BYTES;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, or nullptr on a HIP error.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// Zero n int32 words (the chain counters of the no-allocation entry point's
+// scratch); a plain fill kernel, so a caller may capture the call into a graph.
+__global__ void zero_words_kernel(int* w, int n) {
+  for (int i = (int)(blockIdx.x * blockDim.x + threadIdx.x); i < n; i += (int)(gridDim.x * blockDim.x))
+    w[i] = 0;
+}
+
 m3_status prefill_impl(const m3_dims* dims, m3_dtype dtype, int chunk, const float* h0,
                        const void* x_prev, const void* B_prev, const void* x, const float* dt,
                        const float* A, const float* lam, const float* theta, const void* B,
                        const void* C, void* y, float* h_final, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, void* stream, bool noalloc = false) {
   const m3_status st = check_prefill_shape(dims, chunk, dtype);
   if (st != M3_SUCCESS) return st;
   const bool work = dims->batch > 0 && dims->seqlen > 0;
@@ -174,6 +210,14 @@ m3_status prefill_impl(const m3_dims* dims, m3_dtype dtype, int chunk, const flo
   if (work) {
     w = carve(dims, chunk, dtype);
     need = w.total;
+    if (noalloc) {
+      // the library's scratch instead of a caller's workspace: the first HIP
+      // call of a no-allocation call, after every argument check
+      if (need > kNoAllocScratchBytes) return M3_ERR_WORKSPACE;
+      workspace = device_scratch();
+      if (!workspace) return M3_ERR_HIP;
+      workspace_bytes = kNoAllocScratchBytes;
+    }
     if (!workspace || workspace_bytes < need) return M3_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return M3_ERR_INVALID_VALUE;
   }
@@ -212,6 +256,13 @@ m3_status prefill_impl(const m3_dims* dims, m3_dtype dtype, int chunk, const flo
     a.done = a.ticket + 2;
     a.status = a.ticket + 4;
   }
+  if (noalloc && work) {
+    const int nwords = (int)(4 + w.grid);
+    const int blocks = (nwords + 255) / 256;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(blocks < 1024 ? blocks : 1024), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a.ticket, nwords);
+    if (hipGetLastError() != hipSuccess) return M3_ERR_HIP;
+  }
   const hipError_t e = m3::launch_prefill(a, dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;
 }
@@ -227,6 +278,15 @@ m3_status m3_prefill(const m3_dims* dims, m3_dtype dtype, int chunk, const void*
   if (!dtype_ok(&dtype)) return M3_ERR_INVALID_VALUE;
   return prefill_impl(dims, dtype, chunk, nullptr, nullptr, nullptr, x, dt, A, lam, theta, B, C,
                       y, h_final, workspace, workspace_bytes, stream);
+}
+
+m3_status m3_prefill_noalloc(const m3_dims* dims, m3_dtype dtype, int chunk, const void* x,
+                             const float* dt, const float* A, const float* lam,
+                             const float* theta, const void* B, const void* C, void* y,
+                             float* h_final, void* stream) {
+  if (!dtype_ok(&dtype)) return M3_ERR_INVALID_VALUE;
+  return prefill_impl(dims, dtype, chunk, nullptr, nullptr, nullptr, x, dt, A, lam, theta, B, C,
+                      y, h_final, nullptr, 0, stream, true);
 }
 
 m3_status m3_prefill_from_state(const m3_dims* dims, m3_dtype dtype, int chunk, const float* h0,
