@@ -311,6 +311,10 @@ hipError_t launch_prefill_bf16_r1(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16_r2(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16_r4(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+// The token-lane kernel (prefill_tok.h) for the shapes it takes (bfloat16,
+// rank 1, 64-token chunks, N = P = 64): *taken says whether it took the
+// shape (else nothing was launched).
+hipError_t launch_prefill_tok(const PrefillArgs& a, hipStream_t stream, bool* taken);
 
 // Largest N the decode kernel handles for a given P.
 int decode_max_n(int P);

@@ -82,6 +82,13 @@ hipError_t launch_prefill(const PrefillArgs& a, m3_dtype dtype, hipStream_t stre
     if (e != hipSuccess) return e;
   }
   if (dtype != M3_BF16) return launch_prefill_f32(a, stream);
+  // the token-lane kernel where it takes the shape (bfloat16, rank 1, 64-token
+  // chunks, N = P = 64; its y stores are 8-byte vectors)
+  if (reinterpret_cast<uintptr_t>(a.y) % 8 == 0) {
+    bool taken = false;
+    const hipError_t e = launch_prefill_tok(a, stream, &taken);
+    if (taken) return e;
+  }
   switch (a.R) {
     case 1: return launch_prefill_bf16_r1(a, stream);
     case 2: return launch_prefill_bf16_r2(a, stream);

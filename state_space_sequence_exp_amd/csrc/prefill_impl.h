@@ -1179,6 +1179,139 @@ __device__ __forceinline__ void compose_map(const PrefillArgs& a, const WaveRole
   accD *= g_.d;
 }
 
+// Phase 2 of a segment (its chain step), shared by the prefill kernels.
+// On entry stt holds this segment's exit state for a zero entry state (its
+// local pass), s_srot (LDS, visible to the workgroup) the segment's total
+// rotation per pair and segD its total decay.  Each segment's map from entry
+// to exit state is x -> R(Phi) D x + E_local (linear recurrence).  Segments
+// form groups of kGroup consecutive segments.  Inside a group a segment
+// publishes its map (its aggregate) as soon as its local pass is done; the
+// group's last segment publishes its exit state instead.  A segment's entry
+// state is its group predecessors' maps, composed newest first, applied to
+// the previous group's exit state (or to the sequence's start).  So only the
+// groups chain one after another, and every entry is computed by the same
+// operations on every call (the result does not depend on timing).
+// On return ent holds the segment's entry state; for a group's last segment
+// (and the sequence's last) stt holds its exit state, which was published
+// (or written to h_final).  s_misc: the workgroup's LDS words.
+template <class C>
+__device__ __forceinline__ void chain_phase(const PrefillArgs& a, const WaveRoles& wr, int seg,
+                                            int bh, int ticket, float segD,
+                                            const float2* s_srot, int* s_misc,
+                                            f32x4 (&stt)[kMaxStTiles],
+                                            f32x4 (&ent)[kMaxStTiles]) {
+  constexpr int P = C::P;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int npair = a.N / 2;
+  const int ntn = a.N / 16, ntiles = ntn * (P / 16);
+  const bool last = seg == a.nSeg - 1;
+  const bool group_end = seg % kGroup == kGroup - 1;
+  const size_t np = (size_t)a.N * P;
+  const size_t slotf = prefill_slot_floats(a.N, P);
+  float* mine = a.slots + (size_t)ticket * slotf;
+#pragma unroll
+  for (int q = 0; q < kMaxStTiles; ++q) ent[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (!last && !group_end) {
+    // aggregate: E_local, the segment's rotation per pair, its decay
+    store_state_tiles<C>(a, wr, stt, mine);
+    for (int kp = tid; kp < npair; kp += kT) {
+      __hip_atomic_store(mine + 2 * np + 2 * kp, s_srot[kp].x, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(mine + 2 * np + 2 * kp + 1, s_srot[kp].y, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0)
+      __hip_atomic_store(mine + 2 * np + a.N, segD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    publish_status(a, ticket, 1);
+  }
+  {
+    // the accumulated map: per state tile the rotation of its lane's two
+    // pairs, one decay, and the accumulated offset (in ent)
+    float2 accr[kMaxStTiles][2];
+#pragma unroll
+    for (int q = 0; q < kMaxStTiles; ++q) accr[q][0] = accr[q][1] = make_float2(1.f, 0.f);
+    float accD = 1.f;
+    const int BH = a.nb * a.H;
+    const int g0 = seg - seg % kGroup;  // first segment of the group
+    const int nprev = seg - g0;           // aggregates to compose
+    // every wait at once: the group predecessors' aggregates and the
+    // previous group's exit state
+    const bool ok = wait_statuses(a, (seg - 1) * BH + bh, BH, nprev,
+                                  g0 > 0 ? (g0 - 1) * BH + bh : -1, s_misc + 2);
+    if (!ok) {
+      // a wait timed out (error word 1): the entry state is unknown, so the
+      // segment continues from NaN and every y it writes, every state it
+      // publishes and h_final are NaN -- a failed call cannot pass for a
+      // correct one
+#pragma unroll
+      for (int q = 0; q < kMaxStTiles; ++q) {
+        const float qn = __builtin_nanf("");
+        ent[q] = f32x4{qn, qn, qn, qn};
+      }
+    } else {
+      // newest first, several aggregates' loads in flight at a time (fewer
+      // with more state per wave: registers)
+      constexpr int NB = C::NC == 64 ? kBatch : (C::NC != 0 ? kBatch / 2 : 1);
+      for (int j0 = seg - 1; j0 >= g0; j0 -= NB) {
+        Agg ag[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+          if (j0 - k >= g0) load_agg<C>(a, wr, a.slots + (size_t)((j0 - k) * BH + bh) * slotf, ag[k]);
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+          if (j0 - k >= g0) compose_map<C>(a, wr, ag[k], accr, accD, ent);
+      }
+      // applied to the previous group's exit state, or the sequence's start
+      // (zero, or the continuation's entry state)
+      if (g0 > 0 || a.cont) {
+        const float* src = g0 > 0 ? a.slots + (size_t)((g0 - 1) * BH + bh) * slotf + np
+                                  : a.cont_entry + (size_t)bh * np;
+        f32x4 v[kMaxStTiles];
+        load_state_tiles<C>(a, wr, src, v);
+        apply_map<C>(a, wr, accr, accD, v, ent);
+      }
+    }
+  }
+  if (last || group_end) {
+    // exit state = R(Phi_seg) (D_seg * entry) + local
+#pragma unroll
+    for (int q = 0; q < kMaxStTiles; ++q) {
+      const int i = state_tile(wr, wave, q, ntiles);
+      if (i >= 0) {
+        const int nt = i % ntn;
+        const int kq = nt * 8 + 2 * g;
+        const float2 r0 = s_srot[kq], r1 = s_srot[kq + 1];
+        f32x4 e;
+        const float v0 = segD * ent[q][0], v1 = segD * ent[q][1];
+        const float v2 = segD * ent[q][2], v3 = segD * ent[q][3];
+        e[0] = r0.x * v0 - r0.y * v1 + stt[q][0];
+        e[1] = r0.y * v0 + r0.x * v1 + stt[q][1];
+        e[2] = r1.x * v2 - r1.y * v3 + stt[q][2];
+        e[3] = r1.y * v2 + r1.x * v3 + stt[q][3];
+        stt[q] = e;
+      }
+    }
+    if (!last) {
+      store_state_tiles<C>(a, wr, stt, mine + np);
+      publish_status(a, ticket, 2);
+    } else if (a.h_final) {
+#pragma unroll
+      for (int q = 0; q < kMaxStTiles; ++q) {
+        const int i = state_tile(wr, wave, q, ntiles);
+        if (i >= 0) {
+          const int nt = i % ntn, pt = i / ntn;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            a.h_final[(size_t)bh * np + (size_t)(nt * 16 + 4 * g + j) * P + pt * 16 + li] =
+                stt[q][j];
+        }
+      }
+    }
+  }
+}
+
 // One workgroup's segment: local exit state, chain, outputs.  `ticket` is
 // known to lie inside the grid.
 template <class C>
@@ -1280,16 +1413,7 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     buf ^= 1;
   }
 
-  // ---- phase 2: chain (look-back in groups) ---------------------------------
-  // Each segment's map from entry to exit state is x -> R(Phi) D x + E_local
-  // (linear recurrence).  Segments form groups of kGroup consecutive
-  // segments.  Inside a group a segment publishes its map (its aggregate) as
-  // soon as its local pass is done; the group's last segment publishes its
-  // exit state instead.  A segment's entry state is its group predecessors'
-  // maps, composed newest first, applied to the previous group's exit state
-  // (or to the sequence's start).  So only the groups chain one after
-  // another, and every entry is computed by the same operations on every
-  // call (the result does not depend on timing).
+  // ---- phase 2: chain (look-back in groups; see chain_phase) ---------------
   __syncthreads();
   for (int kp = tid; kp < npair; kp += kT) {
     float sn, cn;
@@ -1297,113 +1421,10 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     s_srot[kp] = make_float2(cn, sn);
   }
   const float segD = __expf(seg_logdecay);
-  const bool last = s.seg == a.nSeg - 1;
-  const bool group_end = s.seg % kGroup == kGroup - 1;
-  const size_t np = (size_t)a.N * P;
-  const size_t slotf = prefill_slot_floats(a.N, P);
-  float* mine = a.slots + (size_t)ticket * slotf;
   int* s_misc = reinterpret_cast<int*>(smem + lay.off_misc);
   f32x4 ent[kMaxStTiles];
-#pragma unroll
-  for (int q = 0; q < kMaxStTiles; ++q) ent[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();  // s_srot
-  if (!last && !group_end) {
-    // aggregate: E_local, the segment's rotation per pair, its decay
-    store_state_tiles<C>(a, wr, stt, mine);
-    for (int kp = tid; kp < npair; kp += kT) {
-      __hip_atomic_store(mine + 2 * np + 2 * kp, s_srot[kp].x, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(mine + 2 * np + 2 * kp + 1, s_srot[kp].y, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (tid == 0)
-      __hip_atomic_store(mine + 2 * np + a.N, segD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    publish_status(a, ticket, 1);
-  }
-  {
-    // the accumulated map: per state tile the rotation of its lane's two
-    // pairs, one decay, and the accumulated offset (in ent)
-    float2 accr[kMaxStTiles][2];
-#pragma unroll
-    for (int q = 0; q < kMaxStTiles; ++q) accr[q][0] = accr[q][1] = make_float2(1.f, 0.f);
-    float accD = 1.f;
-    const int BH = a.nb * a.H;
-    const int g0 = s.seg - s.seg % kGroup;  // first segment of the group
-    const int nprev = s.seg - g0;           // aggregates to compose
-    // every wait at once: the group predecessors' aggregates and the
-    // previous group's exit state
-    const bool ok = wait_statuses(a, (s.seg - 1) * BH + s.bh, BH, nprev,
-                                  g0 > 0 ? (g0 - 1) * BH + s.bh : -1, s_misc + 2);
-    if (!ok) {
-      // a wait timed out (error word 1): the entry state is unknown, so the
-      // segment continues from NaN and every y it writes, every state it
-      // publishes and h_final are NaN -- a failed call cannot pass for a
-      // correct one
-#pragma unroll
-      for (int q = 0; q < kMaxStTiles; ++q) {
-        const float qn = __builtin_nanf("");
-        ent[q] = f32x4{qn, qn, qn, qn};
-      }
-    } else {
-      // newest first, several aggregates' loads in flight at a time (fewer
-      // with more state per wave: registers)
-      constexpr int NB = C::NC == 64 ? kBatch : (C::NC != 0 ? kBatch / 2 : 1);
-      for (int j0 = s.seg - 1; j0 >= g0; j0 -= NB) {
-        Agg ag[NB];
-#pragma unroll
-        for (int k = 0; k < NB; ++k)
-          if (j0 - k >= g0) load_agg<C>(a, wr, a.slots + (size_t)((j0 - k) * BH + s.bh) * slotf, ag[k]);
-#pragma unroll
-        for (int k = 0; k < NB; ++k)
-          if (j0 - k >= g0) compose_map<C>(a, wr, ag[k], accr, accD, ent);
-      }
-      // applied to the previous group's exit state, or the sequence's start
-      // (zero, or the continuation's entry state)
-      if (g0 > 0 || a.cont) {
-        const float* src = g0 > 0 ? a.slots + (size_t)((g0 - 1) * BH + s.bh) * slotf + np
-                                  : a.cont_entry + (size_t)s.bh * np;
-        f32x4 v[kMaxStTiles];
-        load_state_tiles<C>(a, wr, src, v);
-        apply_map<C>(a, wr, accr, accD, v, ent);
-      }
-    }
-  }
-  if (last || group_end) {
-    // exit state = R(Phi_seg) (D_seg * entry) + local
-#pragma unroll
-    for (int q = 0; q < kMaxStTiles; ++q) {
-      const int i = state_tile(wr, wave, q, ntiles);
-      if (i >= 0) {
-        const int nt = i % ntn;
-        const int kq = nt * 8 + 2 * g;
-        const float2 r0 = s_srot[kq], r1 = s_srot[kq + 1];
-        f32x4 e;
-        const float v0 = segD * ent[q][0], v1 = segD * ent[q][1];
-        const float v2 = segD * ent[q][2], v3 = segD * ent[q][3];
-        e[0] = r0.x * v0 - r0.y * v1 + stt[q][0];
-        e[1] = r0.y * v0 + r0.x * v1 + stt[q][1];
-        e[2] = r1.x * v2 - r1.y * v3 + stt[q][2];
-        e[3] = r1.y * v2 + r1.x * v3 + stt[q][3];
-        stt[q] = e;
-      }
-    }
-    if (!last) {
-      store_state_tiles<C>(a, wr, stt, mine + np);
-      publish_status(a, ticket, 2);
-    } else if (a.h_final) {
-#pragma unroll
-      for (int q = 0; q < kMaxStTiles; ++q) {
-        const int i = state_tile(wr, wave, q, ntiles);
-        if (i >= 0) {
-          const int nt = i % ntn, pt = i / ntn;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            a.h_final[(size_t)s.bh * np + (size_t)(nt * 16 + 4 * g + j) * P + pt * 16 + li] =
-                stt[q][j];
-        }
-      }
-    }
-  }
+  chain_phase<C>(a, wr, s.seg, s.bh, ticket, segD, s_srot, s_misc, stt, ent);
   // the output pass's state distribution (see Cfg::kSplit3): the entry
   // state moves to its waves through LDS
   WaveRoles wr3 = wr;
