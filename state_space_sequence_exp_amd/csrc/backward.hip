@@ -1108,8 +1108,7 @@ template <typename T, int R, int P, int W>
 hipError_t launch_grads(const BackwardArgs& a, int nseg, hipStream_t stream) {
   const int nbuf = bw_seg_buffers(a.S, R, a.N, P, (int)sizeof(T));
   const BwSegLayout L = bw_seg_layout(a.S, R, a.N, P, (int)sizeof(T), W, nbuf);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&seg_grads_kernel<T, R, P, W>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+  hipError_t e = lds_limit(reinterpret_cast<const void*>(&seg_grads_kernel<T, R, P, W>), L.total);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((seg_grads_kernel<T, R, P, W>), dim3((unsigned)((size_t)a.nb * a.H * nseg)),
                      dim3(a.N * P / (2 * W)), L.total, stream, a, nseg, nbuf);
@@ -1126,8 +1125,7 @@ hipError_t launch_segments(const BackwardArgs& a, hipStream_t stream) {
   const BwSegLayout L = bw_seg_layout(a.S, R, a.N, P, (int)sizeof(T));
   const dim3 block(a.N * P / 8);
   // the local walks need only the staged inputs (the LDS up to the dx partials)
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&seg_local_kernel<T, R, P>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.oDx);
+  hipError_t e = lds_limit(reinterpret_cast<const void*>(&seg_local_kernel<T, R, P>), L.oDx);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((seg_local_kernel<T, R, P>), dim3((unsigned)((size_t)units * nseg)), block,
                      L.oDx, stream, a, nseg);
@@ -1161,8 +1159,7 @@ hipError_t launch_typed(const BackwardArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int threads = (a.N / 2) * (a.P / 8);
   const size_t lds = sizeof(float) * ((size_t)(a.N / 2) * R * a.P + 4 * ((threads + 63) / 64));
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&token_grads_kernel<T, R>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  e = lds_limit(reinterpret_cast<const void*>(&token_grads_kernel<T, R>), lds);
   if (e != hipSuccess) return e;
   const size_t nblk_t = ((size_t)a.T + kTokPerBlock - 1) / kTokPerBlock;
   hipLaunchKernelGGL((token_grads_kernel<T, R>), dim3((unsigned)((size_t)a.nb * a.H * nblk_t)),

@@ -7,13 +7,18 @@
 //   post-pass  y_out = sum_r D[h,r] * y[r]                         (MIMO down-projection)
 //
 // Both passes stream their operands once and are bound by HBM bandwidth, so
-// they are laid out for coalescing rather than for the matrix cores: lanes
-// move 16-byte vectors (8 bfloat16 or 4 float), consecutive lanes
-// consecutive vectors, each thread kU of them a grid-stride apart with all
-// loads issued first.  The pre-pass is one launch over three row spaces
-// (blockIdx.y: B rows, C rows, x rows); a B or C row of N channels is N / E
-// consecutive lanes (E elements per vector, N / E a power of two dividing the
-// wave), whose sum of squares is reduced by lane shuffles inside that group.
+// they are laid out for coalescing rather than for the matrix cores.  Each
+// tensor is seen as [token][M] 16-byte vectors (8 bfloat16 or 4 float; M the
+// vectors of one token, over all heads and ranks); thread j owns column
+// m = j % M of the kU consecutive tokens of group j / M, issuing all their
+// loads first.  So consecutive lanes move consecutive vectors, a workgroup
+// touches a few contiguous runs (one per token of its group), and a thread's
+// weights, which depend on the column only, are read once.  The pre-pass is
+// one launch over three row spaces (blockIdx.y: B rows, C rows, x rows); a B
+// or C row of N channels is N / E consecutive lanes (E elements per vector,
+// N / E a power of two dividing the wave), whose sum of squares is reduced by
+// lane shuffles inside that group.
+#include <algorithm>
 #include <initializer_list>
 
 #include "m3_device.h"
@@ -57,13 +62,18 @@ __device__ __forceinline__ uint4 pack16(const float (&v)[4], const float*) {
                     __float_as_uint(v[3]));
 }
 
-// Vectors per thread: each thread handles kU vectors a grid-stride apart
-// (the stride is a multiple of the wave, so a row's lane group stays in one
-// wave), issuing all their loads before any arithmetic.  The stride is also a
-// multiple of every row space's period M (heads x ranks x 16-byte pieces per
-// row; launch_block_*), so all of a thread's vectors share one (head, rank,
-// piece) and the thread reads its weights once.
+// Tokens per thread (its column's vectors in kU consecutive tokens).
 constexpr int kU = 8;
+
+// Thread j of a row space of M columns and `ntok` tokens: its column and its
+// first token (ntok or beyond: the thread has nothing to do).
+struct Slot {
+  size_t m, t0;
+};
+__device__ __forceinline__ Slot slot_of(size_t M, int u_per) {
+  const size_t j = (size_t)blockIdx.x * kBlkThreads + threadIdx.x;
+  return Slot{j % M, (j / M) * (size_t)u_per};
+}
 
 template <int E>
 __device__ __forceinline__ void load_w(const float* p, float (&w)[E]) {
@@ -77,25 +87,26 @@ __device__ __forceinline__ void load_w(const float* p, float (&w)[E]) {
 template <typename T>
 __global__ void __launch_bounds__(kBlkThreads) prepass_kernel(BlockArgs a) {
   constexpr int E = Vec16<T>::E;
-  const size_t stride = (size_t)gridDim.x * kBlkThreads;
-  const size_t i0 = (size_t)blockIdx.x * kBlkThreads + threadIdx.x;  // first vector
+  const size_t ntok = a.rows / a.H;
   const int part = blockIdx.y;
   if (part < 2) {
     // BCNorm + bias on 16-byte pieces of B or C rows
     const int cpr = a.N / E;  // lanes per row: a power of two that divides the wave
-    const size_t nvec = a.rows * a.R * (size_t)cpr;
+    const size_t M = (size_t)a.H * a.R * cpr;
+    const Slot sl = slot_of(M, kU);
+    // a lane group of one row shares its token group, so whole groups leave
+    if (sl.t0 >= ntok) return;
     const uint4* src = static_cast<const uint4*>(part == 0 ? a.B : a.C);
     uint4* dst = static_cast<uint4*>(part == 0 ? a.B_out : a.C_out);
     uint4 raw[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const size_t i = i0 + u * stride;
-      raw[u] = i < nvec ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+      const size_t t = sl.t0 + u;
+      raw[u] = t < ntok ? src[t * M + sl.m] : make_uint4(0u, 0u, 0u, 0u);
     }
-    // this thread's (head, rank, piece): vector i is piece i % cpr of rank
-    // (i / cpr) % R of head (i / (cpr R)) % H
-    const size_t m = i0 % ((size_t)a.H * a.R * cpr);
-    const int n0 = (int)(m % cpr) * E, r = (int)((m / cpr) % a.R), h = (int)(m / ((size_t)cpr * a.R));
+    // column m is piece m % cpr of rank (m / cpr) % R of head m / (cpr R)
+    const int n0 = (int)(sl.m % cpr) * E, r = (int)((sl.m / cpr) % a.R);
+    const int h = (int)(sl.m / ((size_t)cpr * a.R));
     float w[E], b[E];
     load_w<E>((part == 0 ? a.norm_B : a.norm_C) + (size_t)h * a.N + n0, w);
     load_w<E>((part == 0 ? a.bias_B : a.bias_C) + ((size_t)h * a.R + r) * a.N + n0, b);
@@ -107,45 +118,47 @@ __global__ void __launch_bounds__(kBlkThreads) prepass_kernel(BlockArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) ss[u] = __builtin_fmaf(v[u][e], v[u][e], ss[u]);
     }
-    // every lane takes part (out-of-range lanes with zeros); groups never
-    // straddle rows
+    // every lane of a group takes part (tokens past the end with zeros)
     for (int off = cpr >> 1; off > 0; off >>= 1)
 #pragma unroll
       for (int u = 0; u < kU; ++u) ss[u] += __shfl_xor(ss[u], off, cpr);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const size_t i = i0 + u * stride;
-      if (i < nvec) {
+      const size_t t = sl.t0 + u;
+      if (t < ntok) {
         const float scale = 1.f / sqrtf(ss[u] / (float)a.N + a.eps);
 #pragma unroll
         for (int e = 0; e < E; ++e) v[u][e] = __builtin_fmaf(v[u][e] * scale, w[e], b[e]);
-        dst[i] = pack16(v[u], (const T*)nullptr);
+        dst[t * M + sl.m] = pack16(v[u], (const T*)nullptr);
       }
     }
   } else {
     // up-projection of 16-byte pieces of x into R pieces of X
     constexpr int kRMax = 4;
     const int cpr = a.P / E;
-    const size_t nvec = a.rows * (size_t)cpr;
+    const size_t M = (size_t)a.H * cpr;
+    const Slot sl = slot_of(M, kU);
+    if (sl.t0 >= ntok) return;
     const uint4* src = static_cast<const uint4*>(a.x);
     uint4* dst = static_cast<uint4*>(a.x_out);
     uint4 raw[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const size_t i = i0 + u * stride;
-      raw[u] = i < nvec ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+      const size_t t = sl.t0 + u;
+      raw[u] = t < ntok ? src[t * M + sl.m] : make_uint4(0u, 0u, 0u, 0u);
     }
-    const size_t m = i0 % ((size_t)a.H * cpr);
-    const int c = (int)(m % cpr), p0 = c * E, h = (int)(m / cpr);
+    // column m is piece c of head h; X row (token, head) holds R pieces per
+    // column, rank-major
+    const int c = (int)(sl.m % cpr), p0 = c * E, h = (int)(sl.m / cpr);
     float up[kRMax][E];
 #pragma unroll
     for (int r = 0; r < kRMax; ++r)
       if (r < a.R) load_w<E>(a.up + ((size_t)h * a.R + r) * a.P + p0, up[r]);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const size_t i = i0 + u * stride;
-      if (i >= nvec) break;
-      const size_t row = i / cpr;  // (token, head)
+      const size_t t = sl.t0 + u;
+      if (t >= ntok) break;
+      const size_t row = t * a.H + h;  // (token, head)
       float v[E];
       unpack16(raw[u], v, (const T*)nullptr);
 #pragma unroll
@@ -171,29 +184,29 @@ template <typename T, int R>
 __global__ void __launch_bounds__(kBlkThreads) postpass_kernel(BlockArgs a) {
   constexpr int E = Vec16<T>::E;
   constexpr int U = post_pieces<R>();
-  const size_t stride = (size_t)gridDim.x * kBlkThreads;
-  const size_t i0 = (size_t)blockIdx.x * kBlkThreads + threadIdx.x;
+  const size_t ntok = a.rows / a.H;
   const int cpr = a.P / E;
-  const size_t nvec = a.rows * (size_t)cpr;
+  const size_t M = (size_t)a.H * cpr;  // output pieces per token
+  const Slot sl = slot_of(M, U);
+  if (sl.t0 >= ntok) return;
+  const int c = (int)(sl.m % cpr), p0 = c * E, h = (int)(sl.m / cpr);
   const uint4* src = static_cast<const uint4*>(a.y);
   uint4 raw[U][R];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const size_t i = i0 + u * stride;
-    const size_t row = i / cpr;
+    const size_t t = sl.t0 + u;
+    const size_t row = t * a.H + h;  // (token, head)
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      raw[u][r] = i < nvec ? src[(row * R + r) * cpr + (i % cpr)] : make_uint4(0u, 0u, 0u, 0u);
+      raw[u][r] = t < ntok ? src[(row * R + r) * cpr + c] : make_uint4(0u, 0u, 0u, 0u);
   }
-  const size_t m = i0 % ((size_t)a.H * cpr);
-  const int p0 = (int)(m % cpr) * E, h = (int)(m / cpr);
   float dw[R][E];
 #pragma unroll
   for (int r = 0; r < R; ++r) load_w<E>(a.down + ((size_t)h * R + r) * a.P + p0, dw[r]);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const size_t i = i0 + u * stride;
-    if (i >= nvec) break;
+    const size_t t = sl.t0 + u;
+    if (t >= ntok) break;
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
@@ -204,31 +217,20 @@ __global__ void __launch_bounds__(kBlkThreads) postpass_kernel(BlockArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(v[e], dw[r][e], acc[e]);
     }
-    static_cast<uint4*>(a.y_out)[i] = pack16(acc, (const T*)nullptr);
+    static_cast<uint4*>(a.y_out)[t * M + sl.m] = pack16(acc, (const T*)nullptr);
   }
 }
 
-size_t gcd_sz(size_t x, size_t y) {
-  while (y) {
-    const size_t t = x % y;
-    x = y;
-    y = t;
+// Blocks for the threads of row spaces of M columns over ntok tokens, u
+// tokens per thread: M times the token groups, the widest space.
+dim3 grid_for(size_t ntok, int u, unsigned parts, std::initializer_list<size_t> widths) {
+  size_t threads = 0;
+  for (size_t M : widths) {
+    const size_t t = M * ((ntok + u - 1) / u);
+    if (t > threads) threads = t;
   }
-  return x;
-}
-
-// Blocks for nvec vectors, u per thread, rounded up so that the grid's
-// thread count is a multiple of every period in `periods` (see kU).
-dim3 grid_for(size_t nvec, int u, unsigned parts, std::initializer_list<size_t> periods) {
-  size_t q = 1;  // blocks must be a multiple of q
-  for (size_t M : periods) {
-    const size_t need = M / gcd_sz(M, kBlkThreads);
-    q = q / gcd_sz(q, need) * need;
-  }
-  const size_t per_block = (size_t)kBlkThreads * u;
-  size_t blocks = (nvec + per_block - 1) / per_block;
-  blocks = (blocks + q - 1) / q * q;
-  return dim3((unsigned)blocks, parts);
+  return dim3((unsigned)std::min<size_t>((threads + kBlkThreads - 1) / kBlkThreads, 0xffffffffu),
+              parts);
 }
 
 }  // namespace
@@ -236,8 +238,7 @@ dim3 grid_for(size_t nvec, int u, unsigned parts, std::initializer_list<size_t> 
 hipError_t launch_block_prepass(const BlockArgs& a, m3_dtype dtype, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
   const size_t es = dtype == M3_BF16 ? 2 : 4, E = 16 / es;
-  const size_t nbc = a.rows * a.R * (a.N / E), nx = a.rows * (a.P / E);
-  const dim3 grid = grid_for(nbc > nx ? nbc : nx, kU, 3,
+  const dim3 grid = grid_for(a.rows / a.H, kU, 3,
                              {(size_t)a.H * a.R * (a.N / E), (size_t)a.H * (a.P / E)});
   if (grid.x > 0x7fffffffu) return hipErrorInvalidValue;
   if (dtype == M3_BF16)
@@ -250,7 +251,7 @@ hipError_t launch_block_prepass(const BlockArgs& a, m3_dtype dtype, hipStream_t 
 template <typename T, int R>
 hipError_t launch_post(const BlockArgs& a, hipStream_t stream) {
   constexpr size_t E = Vec16<T>::E;
-  const dim3 grid = grid_for(a.rows * (a.P / E), post_pieces<R>(), 1, {(size_t)a.H * (a.P / E)});
+  const dim3 grid = grid_for(a.rows / a.H, post_pieces<R>(), 1, {(size_t)a.H * (a.P / E)});
   if (grid.x > 0x7fffffffu) return hipErrorInvalidValue;
   hipLaunchKernelGGL((postpass_kernel<T, R>), grid, dim3(kBlkThreads), 0, stream, a);
   return hipGetLastError();

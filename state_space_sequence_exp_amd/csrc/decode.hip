@@ -242,7 +242,7 @@ hipError_t launch_decode_npt(const DecodeArgs& a, hipStream_t stream) {
   const int rowgroups = kDecThreads / (a.P / 4);
   const size_t lds = sizeof(float) * (2 * (a.N / 2) + 3 * R * a.N + (size_t)rowgroups * R * a.P);
   const void* k = reinterpret_cast<const void*>(&decode_kernel<T, R, kTrap, kRot, NPT>);
-  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = lds_limit(k, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_kernel<T, R, kTrap, kRot, NPT>), dim3(a.S * a.H), dim3(kDecThreads),
                      lds, stream, a);

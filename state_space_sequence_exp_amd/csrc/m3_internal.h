@@ -19,6 +19,13 @@ constexpr int kLRMax = 256;               // largest chunk * R (rows of a chunk 
 constexpr size_t kLdsLimit = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kMaxStTiles = 8192 / 256 / (kPrefillThreads / 64);  // 16x16 state tiles per wave (N * P <= 8192)
 
+// Raise kernel `fn`'s dynamic LDS limit to at least `bytes` on the current
+// device.  The limit is an attribute of the function on a device, not of a
+// launch, so the runtime call is made only the first time a (function,
+// device) pair needs a larger limit; later launches take a lock-guarded look
+// at a small table.
+hipError_t lds_limit(const void* fn, size_t bytes);
+
 // Shape of one prefill problem plus device pointers (all validated).
 struct PrefillArgs {
   int nb, T, H, P, N, R, L, nC;

@@ -168,6 +168,41 @@ void* device_scratch() {
   return g_scratch_ptr[dev];
 }
 
+}  // namespace
+
+namespace m3 {
+
+hipError_t lds_limit(const void* fn, size_t bytes) {
+  struct Entry {
+    const void* fn;
+    int dev;
+    size_t bytes;
+  };
+  static std::mutex mu;
+  static Entry table[256];
+  static int used = 0;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  int i = 0;
+  while (i < used && !(table[i].fn == fn && table[i].dev == dev)) ++i;
+  if (i < used && table[i].bytes >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  if (i == used) {
+    if (used == 256) return hipSuccess;  // table full: correct, only not cached
+    table[used++] = Entry{fn, dev, bytes};
+  } else {
+    table[i].bytes = bytes;
+  }
+  return hipSuccess;
+}
+
+}  // namespace m3
+
+namespace {
+
 // Zero n int32 words (the chain counters of the no-allocation entry point's
 // scratch); a plain fill kernel, so a caller may capture the call into a graph.
 __global__ void zero_words_kernel(int* w, int n) {

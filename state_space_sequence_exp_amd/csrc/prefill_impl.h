@@ -1540,8 +1540,7 @@ __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a_in) {
 template <class C>
 hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   const PrefillLayout lay = prefill_layout(a.L, C::R, a.N, C::P, C::es, C::NC != 0);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<C>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.total);
+  hipError_t e = lds_limit(reinterpret_cast<const void*>(&prefill_kernel<C>), lay.total);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((prefill_kernel<C>), dim3(a.nb * a.H * a.nSeg), dim3(kT), lay.total, stream,
                      a);

@@ -638,11 +638,7 @@ __global__ void __launch_bounds__(kT) prefill_tok_kernel(PrefillArgs a_in) {
 
 template <class C>
 hipError_t launch_tok(const PrefillArgs& a, hipStream_t stream) {
-  // the dynamic LDS limit is raised once per process (the attribute belongs
-  // to the function, not to a launch)
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&prefill_tok_kernel<C>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kTotal);
+  const hipError_t attr = lds_limit(reinterpret_cast<const void*>(&prefill_tok_kernel<C>), C::kTotal);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((prefill_tok_kernel<C>), dim3(a.nb * a.H * a.nSeg), dim3(kT), C::kTotal,
                      stream, a);
