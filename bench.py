@@ -381,12 +381,18 @@ def time_prefill(cfg, g, steps, warmup, flush=True):
         m3.prefill(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"], cfg.chunk,
                    y=y, h_final=hf, workspace=ws)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    times = []
+    # warm-up takes the timed sequence itself (flush, then the call), so the
+    # first touch of the scratch buffer and of the events is not timed
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+           for _ in range(max(steps, warmup))]
+    for s, e in evs[:warmup]:
+        if flush:
+            flush_mall(scratch)
+        s.record()
+        call()
+        e.record()
+    torch.cuda.synchronize()
+    evs = evs[:steps]
     for s, e in evs:
         if flush:
             flush_mall(scratch)
@@ -413,7 +419,7 @@ def time_prefill(cfg, g, steps, warmup, flush=True):
     return times, b2b
 
 
-def time_decode(cfg, g, steps, warmup):
+def time_decode(cfg, g, steps, warmup, matrix_cores=False):
     import torch
     import state_space_sequence_exp_amd as m3
     K = g["x"].shape[0]
@@ -423,7 +429,8 @@ def time_decode(cfg, g, steps, warmup):
     def step(t):
         cur, prev = t % K, (t - 1) % K
         m3.decode_step(h, g["x"][cur], g["x"][prev], g["B"][cur], g["B"][prev], g["C"][cur],
-                       g["dt"][cur], g["A"], g["lam"][cur], g["theta"][cur], y=y)
+                       g["dt"][cur], g["A"], g["lam"][cur], g["theta"][cur], y=y,
+                       matrix_cores=matrix_cores)
 
     for t in range(warmup):
         step(t)
@@ -677,6 +684,9 @@ def main():
     log("timing prefill %s: %d warmup + %d steps" % (cfg.name, args.warmup, args.steps))
     times, b2b = time_prefill(cfg, g, args.steps, args.warmup, flush=not args.no_flush)
     ms = float(np.mean(times))
+    if max(times) > 3 * float(np.median(times)):
+        log("note: slowest timed step %.3f ms against a median of %.3f ms"
+            % (max(times), float(np.median(times))))
     tokens = cfg.batch * cfg.seqlen
     value = tokens / (ms * 1e-3)
     nbytes = prefill_bytes(cfg)
@@ -690,6 +700,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(times)),
+        "ms_each_step": [round(t, 4) for t in times],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -698,7 +710,7 @@ def main():
         "config": {"workload": "SISO prefill: batch 4, T=2048, 16 heads, N=64, P=64, R=1, "
                                "bf16 x/B/C, fp32 state, chunk 64",
                    "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "none"},
-        "roofline": {"kernel": "prefill_kernel (fused chained prefill, one launch per m3_prefill call)",
+        "roofline": {"kernel": "prefill_tok_kernel (token-lane fused chained prefill, one launch per m3_prefill call)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": nbytes,
@@ -764,6 +776,14 @@ def main():
                                     "traffic": measured_traffic("decode_config4"),
                                     "algorithmic_bytes": nb,
                                     "frac_of_measured_copy": gbs / copy_gbs}}
+        # the same steps with the rank-2R update on the matrix cores
+        log("timing decode (matrix-core variant): %d steps x 3" % args.decode_steps)
+        us_m = time_decode(c, gg, args.decode_steps, 10, matrix_cores=True) * 1e3
+        gbs_m = nb / (us_m * 1e-6) / 1e9
+        sec[c.name]["mfma_variant"] = {"kernel": "decode_mfma_kernel (m3_decode_step_mfma)",
+                                       "us_per_step": us_m, "hbm_gbs": gbs_m,
+                                       "frac": gbs_m / HBM_PEAK_GBS,
+                                       "frac_of_measured_copy": gbs_m / copy_gbs}
         del gg
         torch.cuda.empty_cache()
         if not args.no_cpu_baseline:

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define M3SSM_VERSION 130 /* 1.3.0 */
+#define M3SSM_VERSION 140 /* 1.4.0 */
 
 typedef enum {
   M3_SUCCESS = 0,
@@ -270,6 +270,24 @@ m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in,
                          const void* x_t, const void* x_prev, const void* B_t,
                          const void* B_prev, const void* C_t, const float* dt, const float* A,
                          const float* lam, const float* theta, void* y_t, void* stream);
+
+/*
+ * The same decode step with the MIMO update's rank-2R product on the matrix
+ * cores (the MIMO item of the paper summary, item 3, and the explainer's
+ * "third improvement", which place that product on the tensor units): per
+ * 16 x 16 tile of the state, v_mfma_f32_16x16x4_f32 accumulates
+ * [x_prev | x_t] x [U | V]^T onto the rotated, decayed state.  Arguments,
+ * layouts, alignment, reduced forms and errors are those of m3_decode_step;
+ * results agree with it up to float rounding.  Shapes: R = 2 or 4, P = 64,
+ * N a multiple of 16 up to 128; others return M3_ERR_NOT_SUPPORTED.  The
+ * step is bound by the state's HBM traffic either way, so m3_decode_step
+ * (vector ALU) stays the default.
+ */
+m3_status m3_decode_step_mfma(const m3_dims* dims, m3_dtype dtype, const float* h_in,
+                              float* h_out, const void* x_t, const void* x_prev, const void* B_t,
+                              const void* B_prev, const void* C_t, const float* dt,
+                              const float* A, const float* lam, const float* theta, void* y_t,
+                              void* stream);
 
 /*
  * Gradients of the recurrence (reverse mode) for training: given the

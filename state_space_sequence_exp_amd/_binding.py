@@ -25,7 +25,7 @@ M3_BF16 = 1
 
 # every function declared in include/m3ssm.h
 ABI_SYMBOLS = ("m3_version", "m3_status_string", "m3_prefill_workspace_size", "m3_prefill",
-               "m3_prefill_workspace_error", "m3_prefill_noalloc", "m3_prefill_from_state", "m3_decode_step", "m3_block_prepass", "m3_block_postpass",
+               "m3_prefill_workspace_error", "m3_prefill_noalloc", "m3_prefill_from_state", "m3_decode_step", "m3_decode_step_mfma", "m3_block_prepass", "m3_block_postpass",
                "m3_backward_workspace_size", "m3_backward")
 
 
@@ -76,6 +76,9 @@ def load_library(path: Optional[str] = None):
                                           vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.m3_decode_step.restype = ctypes.c_int
     lib.m3_decode_step.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   vp, vp]
+    lib.m3_decode_step_mfma.restype = ctypes.c_int
+    lib.m3_decode_step_mfma.argtypes = [dp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    vp, vp]
     lib.m3_backward_workspace_size.restype = ctypes.c_size_t
     lib.m3_backward_workspace_size.argtypes = [dp, ctypes.c_int]
@@ -276,7 +279,7 @@ def prefill_noalloc(x, dt, A, lam, theta, B, C, chunk: int, y, h_final=None,
 
 
 def decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta, *, h_out=None, y=None,
-                stream=None) -> Tuple:
+                stream=None, matrix_cores: bool = False) -> Tuple:
     """One decode step on the GPU.
 
     h [S,H,N,P] float32; x_t, x_prev [S,H,R,P]; B_t, B_prev, C_t [S,H,R,N]
@@ -284,7 +287,8 @@ def decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta, *, h_out=No
     lam=None gives the exponential-Euler rule (lam = 1; x_prev and B_prev
     are then not read and may be None) and theta=None a real state.
     h_out defaults to h itself (in-place update).  Returns (y_t [S,H,R,P],
-    h_out).
+    h_out).  matrix_cores=True calls m3_decode_step_mfma (the rank-2R
+    update on MFMA; R 2 or 4, P 64, N a multiple of 16 up to 128).
     """
     import torch
     lib = load_library()
@@ -318,11 +322,12 @@ def decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta, *, h_out=No
     else:
         _check(y, "y", x_t.dtype, (ns, nh, nr, npd), dev)
     d = _dims(ns, 1, nh, npd, nn, nr)
-    st = lib.m3_decode_step(ctypes.byref(d), code, _ptr(h), _ptr(h_out), _ptr(x_t), _ptr(x_prev),
-                            _ptr(B_t), _ptr(B_prev), _ptr(C_t), _ptr(dt), _ptr(A), _ptr(lam),
-                            _ptr(theta), _ptr(y), _stream(stream))
+    fn = lib.m3_decode_step_mfma if matrix_cores else lib.m3_decode_step
+    st = fn(ctypes.byref(d), code, _ptr(h), _ptr(h_out), _ptr(x_t), _ptr(x_prev), _ptr(B_t),
+            _ptr(B_prev), _ptr(C_t), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta), _ptr(y),
+            _stream(stream))
     if st != M3_SUCCESS:
-        raise M3Error(st, "m3_decode_step")
+        raise M3Error(st, "m3_decode_step_mfma" if matrix_cores else "m3_decode_step")
     return y, h_out
 
 

@@ -78,6 +78,11 @@ struct DecodeArgs {
   const float *dt, *A, *lam, *theta;
   void* y;
 };
+// The decode step with its rank-2R update on the matrix cores (decode.hip):
+// the shapes it takes, and its launch (hipErrorInvalidValue for others).
+bool decode_mfma_shape(int R, int N, int P);
+hipError_t launch_decode_mfma(const DecodeArgs& a, m3_dtype dtype, hipStream_t stream);
+
 
 // Gradients of the recurrence (backward.hip).
 struct BackwardArgs {

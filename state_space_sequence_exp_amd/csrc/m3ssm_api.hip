@@ -335,10 +335,16 @@ m3_status m3_prefill_from_state(const m3_dims* dims, m3_dtype dtype, int chunk, 
                       h_final, workspace, workspace_bytes, stream);
 }
 
-m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in, float* h_out,
-                         const void* x_t, const void* x_prev, const void* B_t,
-                         const void* B_prev, const void* C_t, const float* dt, const float* A,
-                         const float* lam, const float* theta, void* y_t, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// m3_decode_step and m3_decode_step_mfma: the same checks, then the vector
+// kernel or the matrix-core one.
+m3_status decode_impl(const m3_dims* dims, m3_dtype dtype, const float* h_in, float* h_out,
+                      const void* x_t, const void* x_prev, const void* B_t, const void* B_prev,
+                      const void* C_t, const float* dt, const float* A, const float* lam,
+                      const float* theta, void* y_t, void* stream, bool mfma) {
   if (!dtype_ok(&dtype)) return M3_ERR_INVALID_VALUE;
   if (!dims) return M3_ERR_INVALID_VALUE;
   if (dtype != M3_F32 && dtype != M3_BF16) return M3_ERR_INVALID_VALUE;
@@ -348,6 +354,8 @@ m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in,
     return M3_ERR_INVALID_VALUE;
   if (!valid_p(d->headdim_p) || !valid_r(d->rank_r)) return M3_ERR_NOT_SUPPORTED;
   if (d->dstate_n > 256 || d->dstate_n > m3::decode_max_n((int)d->headdim_p))
+    return M3_ERR_NOT_SUPPORTED;
+  if (mfma && !m3::decode_mfma_shape((int)d->rank_r, (int)d->dstate_n, (int)d->headdim_p))
     return M3_ERR_NOT_SUPPORTED;
   if (d->batch * d->nheads > INT_MAX) return M3_ERR_NOT_SUPPORTED;
   if (d->batch == 0) return M3_SUCCESS;
@@ -386,8 +394,30 @@ m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in,
   a.lam = lam;
   a.theta = theta;
   a.y = y_t;
-  const hipError_t e = m3::launch_decode(a, dtype, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = mfma ? m3::launch_decode_mfma(a, dtype, st) : m3::launch_decode(a, dtype, st);
   return e == hipSuccess ? M3_SUCCESS : M3_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_decode_step(const m3_dims* dims, m3_dtype dtype, const float* h_in, float* h_out,
+                         const void* x_t, const void* x_prev, const void* B_t,
+                         const void* B_prev, const void* C_t, const float* dt, const float* A,
+                         const float* lam, const float* theta, void* y_t, void* stream) {
+  return decode_impl(dims, dtype, h_in, h_out, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta,
+                     y_t, stream, false);
+}
+
+m3_status m3_decode_step_mfma(const m3_dims* dims, m3_dtype dtype, const float* h_in,
+                              float* h_out, const void* x_t, const void* x_prev, const void* B_t,
+                              const void* B_prev, const void* C_t, const float* dt,
+                              const float* A, const float* lam, const float* theta, void* y_t,
+                              void* stream) {
+  return decode_impl(dims, dtype, h_in, h_out, x_t, x_prev, B_t, B_prev, C_t, dt, A, lam, theta,
+                     y_t, stream, true);
 }
 
 }  // extern "C"

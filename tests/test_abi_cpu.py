@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.m3_version() == 130
+    assert lib.m3_version() == 140
     for code in range(6):
         s = m3.status_string(code)
         assert s.startswith("M3_")

@@ -19,10 +19,11 @@ def upload_ring(inp):
                 A=to_gpu_f32(inp["A"]))
 
 
-def run_decode(inp, steps, sel, record_steps=()):
+def run_decode(inp, steps, sel, record_steps=(), matrix_cores=False):
     """Run `steps` decode steps on the GPU over the whole batch and the oracle
     over sequences `sel`; returns (y_gpu, y_ref, h_gpu, h_ref) at the end and
-    the errors of y at record_steps."""
+    the errors of y at record_steps.  matrix_cores: through
+    m3_decode_step_mfma."""
     import torch
     import oracle
     import state_space_sequence_exp_amd as m3
@@ -35,7 +36,8 @@ def run_decode(inp, steps, sel, record_steps=()):
     for t in range(steps):
         cur, prev = t % K, (t - 1) % K
         y, h = m3.decode_step(h, g["x"][cur], g["x"][prev], g["B"][cur], g["B"][prev],
-                              g["C"][cur], g["dt"][cur], g["A"], g["lam"][cur], g["theta"][cur])
+                              g["C"][cur], g["dt"][cur], g["A"], g["lam"][cur], g["theta"][cur],
+                              matrix_cores=matrix_cores)
         y_ref, h_ref = oracle.decode_step(
             h_ref, inp["x"][cur][sel], inp["x"][prev][sel], inp["B"][cur][sel],
             inp["B"][prev][sel], inp["C"][cur][sel], inp["dt"][cur][sel], inp["A"],
@@ -173,3 +175,89 @@ def test_prefill_then_decode_continues_the_sequence(dtype, R):
     e4 = rel_l2(from_gpu(y_pre), y_ref[:, :T])
     log("   decode vs prefill %.3e, vs oracle %.3e, h %.3e, prefix y %.3e" % (e1, e2, e3, e4))
     assert max(e1, e2, e3, e4) <= tol
+
+
+# ---- the matrix-core variant (m3_decode_step_mfma) --------------------------
+
+MFMA_SMALL = [
+    # dtype, S, H, N, P, R, steps
+    ("f32", 2, 3, 64, 64, 2, 5),
+    ("f32", 2, 2, 128, 64, 4, 9),
+    ("f32", 3, 1, 16, 64, 4, 4),
+    ("bf16", 3, 2, 128, 64, 4, 9),
+    ("bf16", 2, 2, 48, 64, 2, 6),
+    ("bf16", 1, 3, 112, 64, 4, 5),
+]
+
+
+@pytest.mark.parametrize("case", MFMA_SMALL, ids=lambda c: "%s-s%d-h%d-n%d-p%d-r%d-k%d" % c)
+def test_decode_mfma_small(case):
+    dtype, S, H, N, P, R, steps = case
+    inp = I.decode_inputs(S, H, N, P, R, dtype, ring=4, seed=11 + N + P)
+    log("decode mfma small %s" % (case,))
+    sel = np.arange(S)
+    y, y_ref, h, h_ref, _ = run_decode(inp, steps, sel, matrix_cores=True)
+    ey, eh = rel_l2(y, y_ref), rel_l2(h, h_ref)
+    log("   rel_l2 y=%.3e h=%.3e" % (ey, eh))
+    assert ey <= TOL[dtype] and eh <= TOL[dtype]
+
+
+def test_decode_mfma_config4_full_batch():
+    """The matrix-core step on the whole decode workload (256 x 32 heads,
+    N=128, P=64, R=4, bf16), 32 steps, every unit against the oracle, and
+    against the vector kernel's result."""
+    import torch
+    import state_space_sequence_exp_amd as m3
+    inp = I.decode_config_inputs()
+    sel = np.arange(inp["h0"].shape[0])
+    log("decode mfma config4: 32 steps, oracle on the full batch")
+    y, y_ref, h, h_ref, errs = run_decode(inp, 32, sel, record_steps=(0, 31), matrix_cores=True)
+    ey, eh = rel_l2(y, y_ref), rel_l2(h, h_ref)
+    wy, wh = worst_decode_y(y, y_ref), worst_state_rel(h, h_ref)
+    log("   rel_l2 y=%.3e h=%.3e worst-unit y=%.3e h=%.3e; y along the way: %s"
+        % (ey, eh, wy, wh, errs))
+    record_parity("decode config4 full batch, 32 steps, MFMA", y=ey, h=eh, worst_y=wy,
+                  worst_h=wh, tol=TOL["bf16"])
+    assert max(ey, eh, wy, wh) <= TOL["bf16"]
+    # one step of both kernels from the same state: the state agrees to float
+    # rounding (the products are summed in another order)
+    g = upload_ring(inp)
+    h0 = to_gpu_f32(inp["h0"])
+    args = (g["x"][1], g["x"][0], g["B"][1], g["B"][0], g["C"][1], g["dt"][1], g["A"],
+            g["lam"][1], g["theta"][1])
+    ya, ha = m3.decode_step(h0, *args, h_out=torch.empty_like(h0))
+    yb, hb = m3.decode_step(h0, *args, h_out=torch.empty_like(h0), matrix_cores=True)
+    torch.cuda.synchronize()
+    assert rel_l2(from_gpu(hb), from_gpu(ha)) <= 1e-6
+    assert rel_l2(from_gpu(yb), from_gpu(ya)) <= TOL["bf16"]
+
+
+def test_decode_mfma_in_place_equals_out_of_place():
+    import torch
+    import state_space_sequence_exp_amd as m3
+    inp = I.decode_inputs(4, 4, 128, 64, 4, "bf16", ring=2, seed=6)
+    g = upload_ring(inp)
+    h1 = to_gpu_f32(inp["h0"])
+    h2 = h1.clone()
+    out = torch.empty_like(h1)
+    args = (g["x"][1], g["x"][0], g["B"][1], g["B"][0], g["C"][1], g["dt"][1], g["A"],
+            g["lam"][1], g["theta"][1])
+    ya, _ = m3.decode_step(h1, *args, matrix_cores=True)
+    yb, _ = m3.decode_step(h2, *args, h_out=out, matrix_cores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, out) and torch.equal(ya, yb)
+
+
+@pytest.mark.parametrize("N,P,R", [(64, 64, 1), (64, 32, 4), (136, 64, 4), (40, 64, 2)])
+def test_decode_mfma_rejects_other_shapes(N, P, R):
+    """Shapes outside R in {2, 4}, P = 64, N a multiple of 16 up to 128 are
+    refused before any launch."""
+    import state_space_sequence_exp_amd as m3
+    from state_space_sequence_exp_amd._binding import M3Error, M3_ERR_NOT_SUPPORTED
+    inp = I.decode_inputs(1, 1, N, P, R, "f32", ring=2, seed=3)
+    g = upload_ring(inp)
+    h = to_gpu_f32(inp["h0"])
+    with pytest.raises(M3Error) as ei:
+        m3.decode_step(h, g["x"][1], g["x"][0], g["B"][1], g["B"][0], g["C"][1], g["dt"][1],
+                       g["A"], g["lam"][1], g["theta"][1], matrix_cores=True)
+    assert ei.value.status == M3_ERR_NOT_SUPPORTED

@@ -70,7 +70,7 @@ def test_prefill_reduced_forms(case, mode):
     assert rel_l2(y_ref, y_full) > 10 * TOL[dtype]
 
 
-def run_decode_mode(inp, steps, sel, with_lam, with_theta):
+def run_decode_mode(inp, steps, sel, with_lam, with_theta, matrix_cores=False):
     """`steps` decode steps over the whole batch on the GPU (lam / theta
     absent as asked; without lam no previous token is passed) and over
     sequences `sel` in the oracle with lam = 1 / theta = 0."""
@@ -91,7 +91,8 @@ def run_decode_mode(inp, steps, sel, with_lam, with_theta):
         y, h = m3.decode_step(h, g["x"][cur], g["x"][prev] if with_lam else None, g["B"][cur],
                               g["B"][prev] if with_lam else None, g["C"][cur], g["dt"][cur],
                               g["A"], g["lam"][cur] if with_lam else None,
-                              g["theta"][cur] if with_theta else None)
+                              g["theta"][cur] if with_theta else None,
+                              matrix_cores=matrix_cores)
         y_ref, h_ref = oracle.decode_step(
             h_ref, red["x"][cur][sel], red["x"][prev][sel], red["B"][cur][sel],
             red["B"][prev][sel], red["C"][cur][sel], red["dt"][cur][sel], red["A"],
@@ -110,6 +111,21 @@ def test_decode_reduced_forms(case, mode):
     inp = I.decode_inputs(3, 2, N, 64, R, dtype, ring=3, seed=95 + N + R)
     sel = np.arange(3)
     y, y_ref, h, h_ref = run_decode_mode(inp, 6, sel, with_lam, with_theta)
+    ey, eh = rel_l2(y, y_ref), rel_l2(h, h_ref)
+    log("   rel_l2 y=%.3e h=%.3e" % (ey, eh))
+    assert ey <= TOL[dtype] and eh <= TOL[dtype]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: m[0])
+@pytest.mark.parametrize("case", [("f32", 128, 4), ("bf16", 64, 2)], ids=lambda c: "%s-n%d-r%d" % c)
+def test_decode_mfma_reduced_forms(case, mode):
+    """The reduced forms through the matrix-core decode step."""
+    dtype, N, R = case
+    name, with_lam, with_theta = mode
+    log("decode mfma %s %s" % (name, case))
+    inp = I.decode_inputs(3, 2, N, 64, R, dtype, ring=3, seed=96 + N + R)
+    sel = np.arange(3)
+    y, y_ref, h, h_ref = run_decode_mode(inp, 6, sel, with_lam, with_theta, matrix_cores=True)
     ey, eh = rel_l2(y, y_ref), rel_l2(h, h_ref)
     log("   rel_l2 y=%.3e h=%.3e" % (ey, eh))
     assert ey <= TOL[dtype] and eh <= TOL[dtype]
