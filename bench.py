@@ -297,9 +297,11 @@ def backward_bench(steps, log):
     N = P = 64, bf16 inputs, float32 gradients): cold per-call time (MALL
     flushed before each call).  Algorithmic bytes: every input and dy read
     once, every gradient written once; the implementation's own state
-    traffic (at this shape the segment checkpoints: two N x P float states
-    per 32-token segment and head, written by the local pass, rewritten by
-    the chain pass and read by the gradient pass) is reported separately."""
+    traffic (at this shape the chunked path's N x P float states per 64-token
+    chunk and head: the local state S_c written, read and rewritten as the
+    entry state G_c by the chain, read twice by the gradient pass (as G_c
+    and as G_{c+1}); the local adjoint D_c written, read and rewritten as
+    dG_{c+1}, read once) is reported separately."""
     import numpy as np
     import torch
     import state_space_sequence_exp_amd as m3
@@ -333,8 +335,8 @@ def backward_bench(steps, log):
     nbytes = (th * (2 * R * P * es + 2 * R * N * es + 8 + (N // 2) * 4)      # x, dy, B, C, dt, lam, theta
               + th * (R * P * 4 + 2 * R * N * 4 + 8 + (N // 2) * 4)        # dx, dB, dC, ddt, dlam, dtheta
               + cfg.nheads * 8)                                            # A, dA
-    nseg = cfg.batch * cfg.nheads * ((cfg.seqlen + 31) // 32)
-    state_bytes = nseg * 2 * N * P * 4 * 4   # checkpoints: written, read + rewritten, read
+    nchunk = cfg.batch * cfg.nheads * ((cfg.seqlen + 63) // 64)
+    state_bytes = nchunk * N * P * 4 * (5 + 4)   # S/G: 1 + 2 + 2 accesses, D/dG: 1 + 2 + 1
     gbs = nbytes / (ms * 1e-3) / 1e9
     log("backward: %.3f ms, %.0f GB/s algorithmic" % (ms, gbs))
     del g, dy, ws, scratch

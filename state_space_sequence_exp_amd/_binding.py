@@ -53,6 +53,10 @@ def load_library(path: Optional[str] = None):
     if not os.path.exists(p):
         raise RuntimeError("libm3ssm.so not found at %s; build it with "
                            "`python -m state_space_sequence_exp_amd.build`" % p)
+    # torch first: it brings its own HIP runtime, and the library must bind
+    # to the same one (loaded before torch, the library would start the
+    # system runtime, which then sees no device next to torch's)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     vp = ctypes.c_void_p
     dp = ctypes.POINTER(M3Dims)

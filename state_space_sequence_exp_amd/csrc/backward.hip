@@ -1188,6 +1188,7 @@ hipError_t launch_backward(const BackwardArgs& a, m3_dtype dtype, hipStream_t st
                        a.dA, a.H);
     return hipGetLastError();
   }
+  if (a.L > 0) return launch_backward_chunked(a, dtype, stream);
   return dtype == M3_BF16 ? launch_t<bf16>(a, stream) : launch_t<float>(a, stream);
 }
 

@@ -98,7 +98,19 @@ struct BackwardArgs {
   // per segment: its decay prod_t alpha_t and, per row pair, its rotation
   // angle sum_t dt_t theta_t (checkpointed path)
   float *dseg, *psi;
+  // chunked path (L > 0, chunks of L tokens, backward_chunk.hip): hs holds
+  // the entry states of chunks 0 .. nC, gs the exit adjoints of chunks
+  // 0 .. nC - 1, dseg per chunk the cosines and sines of its total rotation
+  // and its decay (65 floats), dAc four per-token partial arrays
+  int L;
 };
+
+// Shapes the chunked backward takes: N = P = 64 (64-column tiles), R of 1, 2
+// or 4 (chunks of 64 / R tokens).
+__host__ __device__ inline bool bw_chunked_shape(int R, int N, int P) {
+  return N == 64 && P == 64 && (R == 1 || R == 2 || R == 4);
+}
+hipError_t launch_backward_chunked(const BackwardArgs& a, m3_dtype dtype, hipStream_t stream);
 
 // Segment path of the backward: one workgroup of N P / (2 W) threads per
 // (sequence, head, segment of S tokens); thread (kp, q) holds rows 2 kp,

@@ -540,13 +540,31 @@ m3_status check_backward_dims(const m3_dims* d, m3_dtype dtype) {
 
 struct BwCarve {
   int S;  // segment length of the checkpointed path, 0 for per-token states
+  int L;  // chunk length of the chunked path, 0 for the other two
   size_t off_gs, off_dAc, off_dseg, off_psi, total;
 };
 
-// The states: with segments of S tokens one entry state and one exit
-// adjoint per segment, else h_t and G_t of every token.
+// The states: with chunks of L tokens (N = P = 64) the entry state of every
+// chunk and the next, the exit adjoint of every chunk, per chunk its
+// rotation and decay and per token four partial scalars; else with segments
+// of S tokens one entry state and one exit adjoint per segment; else h_t and
+// G_t of every token.
 BwCarve bw_carve(const m3_dims* d, m3_dtype dtype) {
   BwCarve w;
+  w.L = 0;
+  if (m3::bw_chunked_shape((int)d->rank_r, (int)d->dstate_n, (int)d->headdim_p)) {
+    w.S = 0;
+    w.L = 64 / (int)d->rank_r;
+    const size_t units = (size_t)d->batch * d->nheads;
+    const size_t nC = (size_t)(d->seqlen + w.L - 1) / w.L;
+    const size_t np = (size_t)d->dstate_n * d->headdim_p;
+    w.off_gs = round256(units * (nC + 1) * np * sizeof(float));
+    w.off_dAc = w.off_gs + round256(units * nC * np * sizeof(float));
+    w.off_dseg = w.off_dAc + round256(4 * units * d->seqlen * sizeof(float));
+    w.off_psi = w.off_dseg + round256(units * nC * 65 * sizeof(float));
+    w.total = w.off_psi;
+    return w;
+  }
   w.S = m3::bw_segment_len((int)d->rank_r, (int)d->dstate_n, (int)d->headdim_p,
                            (int)esize_of(dtype));
   const size_t slots = w.S ? (size_t)(d->seqlen + w.S - 1) / w.S : (size_t)d->seqlen;
@@ -610,6 +628,7 @@ m3_status m3_backward(const m3_dims* dims, m3_dtype dtype, const void* x, const 
   const BwCarve w = bw_carve(dims, dtype);
   if (!workspace || workspace_bytes < w.total) return M3_ERR_WORKSPACE;
   a.S = w.S;
+  a.L = w.L;
   if (!aligned(workspace, 256)) return M3_ERR_INVALID_VALUE;
   a.x = x;
   a.B = B;

@@ -314,14 +314,21 @@ def test_backward_validation(lib):
         assert call(d, p) == m3.M3_ERR_INVALID_VALUE
     assert call(d, ws=None) == m3.M3_ERR_WORKSPACE
     need = lib.m3_backward_workspace_size(ctypes.byref(d), m3.M3_F32)
-    # N P <= 4096: segments of 16 tokens at this shape (float, R = 2: the
-    # LDS does not fit 32), one entry state and one exit adjoint per
-    # segment and head; the dA terms; per segment a decay and N / 2 angles
+    # N = P = 64: chunks of 64 / R = 32 tokens; per head the entry state of
+    # every chunk and of the next (nC + 1 states), the exit adjoint of every
+    # chunk (nC states), four partial scalars per token, 65 floats per chunk
     # (each area rounded up to 256 bytes)
-    assert need == 2 * (2 * 2 * 1 * 64 * 64 * 4) + 256 + 256 + 512
+    st = 64 * 64 * 4
+    assert need == 4 * 2 * st + 4 * 1 * st + 4 * 4 * 16 * 4 + 1280
     d40 = dims(b=2, t=40, h=2, p=64, n=64, r=2)
     assert lib.m3_backward_workspace_size(ctypes.byref(d40), m3.M3_F32) == \
-        2 * (2 * 2 * 3 * 64 * 64 * 4) + 768 + 256 + 12 * 32 * 4
+        4 * 3 * st + 4 * 2 * st + 4 * 4 * 40 * 4 + 2304
+    # other N P <= 4096: segments (32 tokens here), one entry state and one
+    # exit adjoint per segment and head; the dA terms; per segment a decay
+    # and N / 2 angles
+    d32 = dims(b=2, t=16, h=2, p=32, n=32, r=1)
+    assert lib.m3_backward_workspace_size(ctypes.byref(d32), m3.M3_F32) == \
+        2 * (2 * 2 * 1 * 32 * 32 * 4) + 256 + 256 + 256
     # N P = 8192: h_t and G_t of every token-head
     d8k = dims(b=2, t=16, h=2, p=64, n=128, r=1)
     assert lib.m3_backward_workspace_size(ctypes.byref(d8k), m3.M3_BF16) == \

@@ -70,6 +70,93 @@ def test_backward_against_oracle(case):
     assert max(errs.values()) <= TOL, errs
 
 
+# the chunked path (N = P = 64; chunks of 64 / R tokens): one token, a chunk
+# short, exactly one and several chunks, ragged tails, every rank
+CHUNKED = [
+    # dtype, batch, T, heads, R, with dh_final
+    ("f32", 1, 1, 2, 1, True),
+    ("bf16", 2, 63, 1, 1, True),
+    ("f32", 1, 64, 2, 1, False),
+    ("bf16", 1, 300, 2, 1, True),
+    ("f32", 2, 97, 1, 2, True),
+    ("bf16", 1, 128, 2, 2, False),
+    ("f32", 1, 16, 1, 4, True),
+    ("bf16", 2, 71, 2, 4, True),
+]
+
+
+def grad_errors(got, ref):
+    """rel-L2 of every gradient; one that is zero in exact arithmetic (dtheta
+    of a one-token sequence: the first token's rotation acts on a zero state,
+    and the chunked form gets that zero as terms that cancel to rounding) is
+    measured against the norm of dB instead."""
+    out = {}
+    for k in NAMES:
+        g = np.asarray(from_gpu(got[k]), dtype=np.float64)
+        r = np.asarray(ref[k], dtype=np.float64)
+        den = np.linalg.norm(r) or np.linalg.norm(np.asarray(ref["B"], dtype=np.float64))
+        out[k] = float(np.linalg.norm(g - r) / den)
+    return out
+
+
+@pytest.mark.parametrize("case", CHUNKED, ids=lambda c: "%s-b%d-t%d-h%d-r%d-dh%d" % c)
+def test_backward_chunked_against_oracle(case):
+    from oracle import backward
+    dtype, nb, T, nh, R, with_dh = case
+    log("backward chunked %s" % (case,))
+    inp = I.prefill_inputs(nb, T, nh, 64, 64, R, dtype, seed=180 + T + R)
+    dy, dy_raw, dhf = upstream(inp, 181 + T, with_dh)
+    got = run(inp, dy_raw, dhf)
+    ref = backward.gradients(inp["x"], inp["dt"], inp["A"], inp["lam"], inp["theta"], inp["B"],
+                             inp["C"], dy, dhf)
+    errs = grad_errors(got, ref)
+    log("   " + " ".join("%s=%.1e" % kv for kv in errs.items()))
+    assert max(errs.values()) <= TOL, errs
+
+
+@pytest.mark.parametrize("lam_value", [0.0, 1.0])
+def test_backward_chunked_lambda_extremes(lam_value):
+    """lam = 0 (the input enters only through the next token's trapezoid
+    term, which crosses every chunk boundary) and lam = 1 (no such term)."""
+    from oracle import backward
+    inp = I.prefill_inputs(1, 150, 2, 64, 64, 1, "f32", seed=190)
+    inp["lam"][:] = lam_value
+    dy, dy_raw, dhf = upstream(inp, 191, True)
+    got = run(inp, dy_raw, dhf)
+    ref = backward.gradients(inp["x"], inp["dt"], inp["A"], inp["lam"], inp["theta"], inp["B"],
+                             inp["C"], dy, dhf)
+    errs = grad_errors(got, ref)
+    log("   lam=%g " % lam_value + " ".join("%s=%.1e" % kv for kv in errs.items()))
+    assert max(errs.values()) <= TOL, errs
+
+
+def test_backward_chunked_large_angles():
+    """Angles of several turns per chunk (theta up to 40, dt up to 0.5): the
+    running angles and the chunk's total rotation."""
+    from oracle import backward
+    inp = I.prefill_inputs(1, 200, 1, 64, 64, 2, "f32", seed=195)
+    rng = np.random.default_rng(196)
+    inp["theta"][:] = rng.uniform(-40.0, 40.0, inp["theta"].shape).astype(np.float32)
+    inp["dt"][:] = rng.uniform(0.05, 0.5, inp["dt"].shape).astype(np.float32)
+    dy, dy_raw, dhf = upstream(inp, 197, True)
+    got = run(inp, dy_raw, dhf)
+    ref = backward.gradients(inp["x"], inp["dt"], inp["A"], inp["lam"], inp["theta"], inp["B"],
+                             inp["C"], dy, dhf)
+    errs = {k: rel_l2(from_gpu(got[k]), ref[k]) for k in NAMES}
+    log("   " + " ".join("%s=%.1e" % kv for kv in errs.items()))
+    assert max(errs.values()) <= TOL, errs
+
+
+def test_backward_chunked_repeatable():
+    import torch
+    inp = I.prefill_inputs(2, 200, 2, 64, 64, 1, "bf16", seed=198)
+    _, dy_raw, dhf = upstream(inp, 199, True)
+    a, b = run(inp, dy_raw, dhf), run(inp, dy_raw, dhf)
+    torch.cuda.synchronize()
+    for k in NAMES:
+        assert torch.equal(a[k], b[k]), k
+
+
 def test_backward_repeatable_and_empty():
     import torch
     import state_space_sequence_exp_amd as m3
