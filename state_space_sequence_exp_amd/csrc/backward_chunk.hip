@@ -36,9 +36,10 @@
 //   bwc_grads_kernel   per chunk: the six products above and their
 //                      epilogues (MFMA), every per-element gradient, and per
 //                      token the partial scalar gradients;
-//   bwc_final_kernel   per head: dt and lam from the partials (the omega
+//   bwc_final_kernel   per token: dt and lam from the partials (the omega
 //                      term of a token comes from the chunk of the token
-//                      before it), dA summed in a fixed order.
+//                      before it); per head: dA from the chunks' partials, in
+//                      a fixed order.
 // Every sum runs in a fixed order, so results repeat bit for bit.
 //
 // Products use v_mfma_f32_16x16x4_f32 (float32 throughout, the gradients'
@@ -55,11 +56,59 @@ namespace {
 
 constexpr int kBT = 512;  // threads of a chunk workgroup (8 waves)
 
+// The thread index, opaque to the compiler at each use, so that the gradient
+// kernel's loop over chunks does not hoist lane-dependent LDS addresses out
+// of the loop and hold them in registers across it.
+__device__ __forceinline__ int ltid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 __device__ __forceinline__ int tix(int r, int c) {
   return r * 64 + (c ^ (((r & 3) << 4) | (((r >> 2) & 3) << 2)));
 }
 __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Two products over k in [kb, ke) (multiples of 16, uniform over the wave):
+// acc0 += A0 B0 and acc1 += A1 B1, where op(k, a0, b0, a1, b1) reads this
+// lane's four operands of the k-step at k (rows / columns k + g).  The
+// operands of the next 16 k (four steps) are requested before the current
+// four steps are multiplied, so the LDS latency hides behind eight MFMAs.
+template <class F>
+__device__ __forceinline__ void mma_pipe2(f32x4& acc0, f32x4& acc1, int kb, int ke, F op) {
+  if (kb >= ke) return;
+  float a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) op(kb + 4 * s, a0[s], b0[s], a1[s], b1[s]);
+  for (int k = kb; k < ke; k += 16) {
+    float na0[4], nb0[4], na1[4], nb1[4];
+    const bool more = k + 16 < ke;
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) op(k + 16 + 4 * s, na0[s], nb0[s], na1[s], nb1[s]);
+    }
+    // keep those reads ahead of the products (the scheduler would otherwise
+    // sink each read next to its MFMA and wait on it there)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      acc0 = mma4(a0[s], b0[s], acc0);
+      acc1 = mma4(a1[s], b1[s], acc1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        a0[s] = na0[s];
+        b0[s] = nb0[s];
+        a1[s] = na1[s];
+        b1[s] = nb1[s];
+      }
+    }
+  }
 }
 
 // LDS (float offsets).  The four input tiles come first in both kernels.
@@ -98,7 +147,7 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
 template <typename T, int R>
 __device__ __forceinline__ void load_tile(const void* src, float* tile, const BackwardArgs& a,
                                           int b, int hh, int t0) {
-  const int tid = threadIdx.x, row = tid >> 3, c0 = (tid & 7) * 8;
+  const int tid = ltid(), row = tid >> 3, c0 = (tid & 7) * 8;
   const int t = t0 + row / R, r = row % R;
   float v[8];
   if (t < a.T) {
@@ -127,7 +176,7 @@ template <typename T, int R>
 __device__ __forceinline__ void stage_loads(const BackwardArgs& a, int b, int hh, int c,
                                             float* sm, float* sc, float (&th)[4]) {
   constexpr int L = ChunkGeo<R>::L, TPG = ChunkGeo<R>::TPG;
-  const int tid = threadIdx.x, t0 = c * L;
+  const int tid = ltid(), t0 = c * L;
   load_tile<T, R>(a.C, sm + oC, a, b, hh, t0);
   load_tile<T, R>(a.B, sm + oB, a, b, hh, t0);
   load_tile<T, R>(a.x, sm + oX, a, b, hh, t0);
@@ -150,7 +199,7 @@ __device__ __forceinline__ void stage_loads(const BackwardArgs& a, int b, int hh
 template <int R>
 __device__ __forceinline__ void stage_angle_parts(const float* sc, const float (&th)[4], double* part) {
   constexpr int TPG = ChunkGeo<R>::TPG;
-  const int tid = threadIdx.x, k = tid & 31, grp = tid >> 5;
+  const int tid = ltid(), k = tid & 31, grp = tid >> 5;
   double s = 0.0;
 #pragma unroll
   for (int j = 0; j < TPG; ++j) s += (double)sc[sDt + grp * TPG + j] * (double)th[j];
@@ -165,7 +214,7 @@ template <int R>
 __device__ __forceinline__ void stage_angles_scalars(const BackwardArgs& a, int hh, const float (&th)[4],
                                                      const double* part, float* rev, float* sc) {
   constexpr int L = ChunkGeo<R>::L, TPG = ChunkGeo<R>::TPG;
-  const int tid = threadIdx.x, k = tid & 31, grp = tid >> 5;
+  const int tid = ltid(), k = tid & 31, grp = tid >> 5;
   double phi = 0.0;
   for (int g2 = 0; g2 < grp; ++g2) phi += part[g2 * 32 + k];
 #pragma unroll
@@ -209,7 +258,7 @@ template <int R>
 __device__ __forceinline__ void stage_rotate(float* sm, const float* rev) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int idx = threadIdx.x + kBT * q, row = idx >> 5, k = idx & 31;
+    const int idx = ltid() + kBT * q, row = idx >> 5, k = idx & 31;
     const float rv = rev[(row / R) * 32 + k];
     const float cn = __builtin_amdgcn_cosf(rv), sn = __builtin_amdgcn_sinf(rv);
     float2* pb = reinterpret_cast<float2*>(sm + oB + tix(row, 2 * k));
@@ -218,6 +267,95 @@ __device__ __forceinline__ void stage_rotate(float* sm, const float* rev) {
     *pb = make_float2(cn * b.x + sn * b.y, cn * b.y - sn * b.x);
     *pc = make_float2(cn * cc.x + sn * cc.y, cn * cc.y - sn * cc.x);
   }
+}
+
+// ---- a chunk's inputs as raw registers (the gradient pass fetches the next
+// chunk's while it works on the current one) --------------------------------
+typedef __amdgpu_buffer_rsrc_t brsrc;
+__device__ __forceinline__ brsrc mkr(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// This thread's share of one chunk's inputs: 8 storage elements of each of
+// the C, B, x and dy tiles (row tid / 8, columns 8 (tid % 8) ..), dt and lam
+// of token tid (tid <= L), theta of pair tid % 32 for its TPG tokens.  Every
+// load is a range-checked buffer load (rows past the sequence read as
+// zeros), so nothing waits on a value before it is used.
+template <typename T>
+struct ChunkIn {
+  static constexpr int kV = sizeof(T) / 2;  // 16-byte vectors per 8 elements
+  u32x4 t[4][kV];
+  uint32_t dt, lam, th[4];
+};
+
+template <typename T, int R>
+__device__ __forceinline__ void chunk_fetch(const BackwardArgs& a, int ci, int nC, ChunkIn<T>& in) {
+  constexpr int L = ChunkGeo<R>::L, TPG = ChunkGeo<R>::TPG;
+  constexpr uint32_t es = sizeof(T);
+  const int tid = ltid(), row = tid >> 3, c0 = (tid & 7) * 8;
+  const int unit = ci / nC, c = ci - unit * nC, b = unit / a.H, hh = unit - b * a.H;
+  const int t0 = c * L, len = min(L, a.T - t0);
+  const size_t tok0 = ((size_t)b * a.T + t0) * a.H + hh;
+  const uint32_t stride = (uint32_t)a.H * R * 64 * es;  // bytes from one token's rows to the next
+  const uint32_t range = (uint32_t)(len - 1) * stride + R * 64 * es;
+  const uint32_t off = (uint32_t)(row / R) * stride + (uint32_t)((row % R) * 64 + c0) * es;
+  const void* src[4] = {a.C, a.B, a.x, a.dy};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const brsrc r = mkr(static_cast<const unsigned char*>(src[q]) + tok0 * R * 64 * es, range);
+#pragma unroll
+    for (int v = 0; v < ChunkIn<T>::kV; ++v)
+      in.t[q][v] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16 * v), 0, 0);
+  }
+  const int nsc = min(L + 1, a.T - t0);  // dt, lam of tokens t0 .. t0 + L
+  const brsrc rd = mkr(a.dt + tok0, (uint32_t)(nsc - 1) * a.H * 4 + 4);
+  const brsrc rl = mkr(a.lam + tok0, (uint32_t)(nsc - 1) * a.H * 4 + 4);
+  const uint32_t so = (uint32_t)min(tid, L + 1) * a.H * 4;
+  in.dt = __builtin_amdgcn_raw_buffer_load_b32(rd, (int)so, 0, 0);
+  in.lam = __builtin_amdgcn_raw_buffer_load_b32(rl, (int)so, 0, 0);
+  const uint32_t tstride = (uint32_t)a.H * 32 * 4;
+  const brsrc rt = mkr(a.theta + tok0 * 32, (uint32_t)(len - 1) * tstride + 128);
+  const int k = tid & 31, grp = tid >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    in.th[j] = j < TPG ? __builtin_amdgcn_raw_buffer_load_b32(
+                             rt, (int)((uint32_t)(grp * TPG + j) * tstride + k * 4), 0, 0)
+                       : 0u;
+}
+
+// The fetched tiles into LDS as float, dt and lam into the scalar block,
+// theta into th[].
+template <typename T, int R>
+__device__ __forceinline__ void chunk_commit(const ChunkIn<T>& in, float* sm, float* sc,
+                                             float (&th)[4]) {
+  constexpr int L = ChunkGeo<R>::L;
+  const int tid = ltid(), row = tid >> 3, c0 = (tid & 7) * 8;
+  const int toff[4] = {oC, oB, oX, oDY};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float v[8];
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(in.t[q][0][e] << 16);
+        v[2 * e + 1] = __uint_as_float(in.t[q][0][e] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = __uint_as_float(in.t[q][0][e]);
+        v[4 + e] = __uint_as_float(in.t[q][1][e]);
+      }
+    }
+    *reinterpret_cast<float4*>(sm + toff[q] + tix(row, c0)) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(sm + toff[q] + tix(row, c0 + 4)) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  if (tid <= L) {
+    sc[sDt + tid] = __uint_as_float(in.dt);
+    sc[sLam + tid] = __uint_as_float(in.lam);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) th[j] = __uint_as_float(in.th[j]);
 }
 
 // ---- local pass ---------------------------------------------------------------
@@ -242,7 +380,7 @@ __global__ void __launch_bounds__(kBT) bwc_local_kernel(BackwardArgs a, int nC) 
   stage_rotate<R>(sm, rev);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, i = lane & 15, g = lane >> 4;
+  const int tl = ltid(), lane = tl & 63, w = tl >> 6, i = lane & 15, g = lane >> 4;
   const int m0 = (w >> 1) * 16;
   constexpr int NP = 64 * 64;
   float* Sout = a.hs + ((size_t)unit * (nC + 1) + c + 1) * NP;
@@ -251,12 +389,13 @@ __global__ void __launch_bounds__(kBT) bwc_local_kernel(BackwardArgs a, int nC) 
   for (int q = 0; q < 2; ++q) {
     const int n0 = (2 * (w & 1) + q) * 16;
     f32x4 s = {0.f, 0.f, 0.f, 0.f}, d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k = 0; k < 64; k += 4) {
+    mma_pipe2(s, d, 0, 64, [&](int k, float& a0, float& b0, float& a1, float& b1) {
       const int kr = k + g, tk = kr / R;
-      s = mma4(sm[oB + tix(kr, m0 + i)], sc[sV + tk] * sm[oX + tix(kr, n0 + i)], s);
-      d = mma4(sm[oC + tix(kr, m0 + i)], sc[sEcs + tk] * sm[oDY + tix(kr, n0 + i)], d);
-    }
+      a0 = sm[oB + tix(kr, m0 + i)];
+      b0 = sc[sV + tk] * sm[oX + tix(kr, n0 + i)];
+      a1 = sm[oC + tix(kr, m0 + i)];
+      b1 = sc[sEcs + tk] * sm[oDY + tix(kr, n0 + i)];
+    });
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = m0 + 4 * g + j;
@@ -378,7 +517,7 @@ __device__ __forceinline__ void rot_epilogue(const f32x4& acc, const float* vt, 
                                              float* dphi, bool first, float* out,
                                              const BackwardArgs& a, int b, int hh, int t0, int m0,
                                              int n0) {
-  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+  const int lane = ltid() & 63, i = lane & 15, g = lane >> 4;
   const int n = n0 + i, k = n >> 1;
   const bool even = (n & 1) == 0;
 #pragma unroll
@@ -401,21 +540,38 @@ __device__ __forceinline__ void rot_epilogue(const f32x4& acc, const float* vt, 
   }
 }
 
+// Persistent: workgroup j takes chunks j, j + grid, ...  With bfloat16 inputs
+// the next chunk's inputs are fetched into registers once the current
+// chunk's states are consumed, so they arrive during its products; float
+// inputs (twice the registers) are fetched at the top of each chunk.
 template <typename T, int R>
 __global__ void __launch_bounds__(kBT) bwc_grads_kernel(BackwardArgs a, int nC) {
   extern __shared__ __align__(16) float sm[];
-  constexpr int L = ChunkGeo<R>::L, TPG = ChunkGeo<R>::TPG, NP = 64 * 64;
+  constexpr int L = ChunkGeo<R>::L, TPG = ChunkGeo<R>::TPG;
+  constexpr bool kAhead = sizeof(T) == 2;
   float* sc = sm + oScG;
   float* rev = sm + oRevG;
   float* dphi = sm + oDphi;
-  const int unit = blockIdx.x / nC, c = blockIdx.x - unit * nC;
+  const int nchunk = a.nb * a.H * nC;
+  ChunkIn<T> in;
+  if (kAhead) chunk_fetch<T, R>(a, blockIdx.x, nC, in);
+  for (int ci = blockIdx.x; ci < nchunk; ci += gridDim.x) {
+  // the thread index, opaque to the compiler in each chunk: otherwise every
+  // lane-dependent LDS address of the body is hoisted out of the loop and
+  // held in registers across it
+  const int tid = ltid();
+  const int lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
+  const int unit = ci / nC, c = ci - unit * nC;
   const int b = unit / a.H, hh = unit - b * a.H, t0 = c * L;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
 
   // ---- staging: inputs, and the states: entry G, exit G_next, its adjoint E
+  if (!kAhead) chunk_fetch<T, R>(a, ci, nC, in);
   float th[4];
-  stage_loads<T, R>(a, b, hh, c, sm, sc, th);
-  const int sk = tid >> 4, sp = (tid & 15) * 4;  // rows 2 sk, 2 sk + 1, columns sp .. sp + 3
+  chunk_commit<T, R>(in, sm, sc, th);
+  // the states (written by the chain pass just before; mostly last-level
+  // cache hits): rows 2 sk, 2 sk + 1, columns sp .. sp + 3
+  const int sk = tid >> 4, sp = (tid & 15) * 4;
+  constexpr int NP = 64 * 64;
   const float* Gp = a.hs + ((size_t)unit * (nC + 1) + c) * NP;
   const float* Ep = a.gs + ((size_t)unit * nC + c) * NP;
   const float4 G0 = *reinterpret_cast<const float4*>(Gp + (2 * sk) * 64 + sp);
@@ -453,6 +609,8 @@ __global__ void __launch_bounds__(kBT) bwc_grads_kernel(BackwardArgs a, int nC) 
     if (lane == 0) sc[sMisc + w] = eg;
   }
   __syncthreads();
+  // the next chunk's inputs, in flight through this chunk's products
+  if (kAhead && ci + (int)gridDim.x < nchunk) chunk_fetch<T, R>(a, ci + gridDim.x, nC, in);
 
   const int m0 = (w >> 1) * 16;          // this wave's row tile
   const int tmax = (m0 + 15) / R;        // last token of its rows
@@ -475,11 +633,12 @@ __global__ void __launch_bounds__(kBT) bwc_grads_kernel(BackwardArgs a, int nC) 
         }
       } else {
         f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int k = 0; k < 64; k += 4) {
-          s1 = mma4(sm[oC + tix(m0 + i, k + g)], sm[oB + tix(n0 + i, k + g)], s1);
-          s2 = mma4(sm[oDY + tix(m0 + i, k + g)], sm[oX + tix(n0 + i, k + g)], s2);
-        }
+        mma_pipe2(s1, s2, 0, 64, [&](int k, float& a0, float& b0, float& a1, float& b1) {
+          a0 = sm[oC + tix(m0 + i, k + g)];
+          b0 = sm[oB + tix(n0 + i, k + g)];
+          a1 = sm[oDY + tix(m0 + i, k + g)];
+          b1 = sm[oX + tix(n0 + i, k + g)];
+        });
         const int uu = n0 + i, u = uu / R;
         const float csu = sc[sCs + u], gu = sc[sGam + u], ou = sc[sOm + u];
 #pragma unroll
@@ -516,79 +675,94 @@ __global__ void __launch_bounds__(kBT) bwc_grads_kernel(BackwardArgs a, int nC) 
   __syncthreads();
 
   // ---- dC~ = diag(e^cs) dY G^T + M2 B~ ---------------------------------------------
-  // (the row sums de_t = C~_t . (G dy_t) and dV_u = B~_u . (E~ x_u) come from
-  // the first product of dC~ and of dB~: per row, one partial per wave of
-  // the row tile)
-  float racc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int n0 = (2 * (w & 1) + q) * 16;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k = 0; k < 64; k += 4)
-      acc = mma4(sm[oDY + tix(m0 + i, k + g)], sm[oG + tix(n0 + i, k + g)], acc);
-    float de[4];
+  // The wave's two column tiles n0[0], n0[1] share the A operand.  The row
+  // sums de_t = C~_t . (G dy_t) and dV_u = B~_u . (E~ x_u) come from the first
+  // products of dC~ and of dB~: per row, one partial per wave of the row tile.
+  const int nA = (2 * (w & 1)) * 16, nB = nA + 16;
+  {
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    mma_pipe2(acc0, acc1, 0, 64, [&](int k, float& a0, float& b0, float& a1, float& b1) {
+      a0 = sm[oDY + tix(m0 + i, k + g)];
+      a1 = a0;
+      b0 = sm[oG + tix(nA + i, k + g)];
+      b1 = sm[oG + tix(nB + i, k + g)];
+    });
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rr = m0 + 4 * g + j;
-      de[j] = sm[oC + tix(rr, n0 + i)] * acc[j];
-      acc[j] *= sc[sEcs + rr / R];
+      const float de = sum16(sm[oC + tix(rr, nA + i)] * acc0[j] + sm[oC + tix(rr, nB + i)] * acc1[j]);
+      if (i == 0) sc[sDeP + (w & 1) * 64 + rr] = de;
+      const float e = sc[sEcs + rr / R];
+      acc0[j] *= e;
+      acc1[j] *= e;
     }
-    const int kend = (tmax + 1) * R;
-    for (int k = 0; k < kend; k += 4)
-      acc = mma4(sm[oM2 + tix(m0 + i, k + g)], sm[oB + tix(k + g, n0 + i)], acc);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) racc[j] += sum16(de[j]);
+    mma_pipe2(acc0, acc1, 0, m0 + 16, [&](int k, float& a0, float& b0, float& a1, float& b1) {
+      a0 = sm[oM2 + tix(m0 + i, k + g)];
+      a1 = a0;
+      b0 = sm[oB + tix(k + g, nA + i)];
+      b1 = sm[oB + tix(k + g, nB + i)];
+    });
     // every (row, pair) entry of dphi belongs to one lane of one wave, the
     // same in the dB~ epilogue below: written here, added to there
-    rot_epilogue<R>(acc, sm + oC, rev, dphi, true, a.dC, a, b, hh, t0, m0, n0);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (i == 0) sc[sDeP + (w & 1) * 64 + m0 + 4 * g + j] = racc[j];
-    racc[j] = 0.f;
+    rot_epilogue<R>(acc0, sm + oC, rev, dphi, true, a.dC, a, b, hh, t0, m0, nA);
+    rot_epilogue<R>(acc1, sm + oC, rev, dphi, true, a.dC, a, b, hh, t0, m0, nB);
   }
   // ---- dB~ = diag(V) X E~^T + M2^T C~ -------------------------------------------------
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int n0 = (2 * (w & 1) + q) * 16;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k = 0; k < 64; k += 4)
-      acc = mma4(sm[oX + tix(m0 + i, k + g)], sm[oE + tix(n0 + i, k + g)], acc);
-    float dv[4];
+  {
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    mma_pipe2(acc0, acc1, 0, 64, [&](int k, float& a0, float& b0, float& a1, float& b1) {
+      a0 = sm[oX + tix(m0 + i, k + g)];
+      a1 = a0;
+      b0 = sm[oE + tix(nA + i, k + g)];
+      b1 = sm[oE + tix(nB + i, k + g)];
+    });
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rr = m0 + 4 * g + j;
-      dv[j] = sm[oB + tix(rr, n0 + i)] * acc[j];
-      acc[j] *= sc[sV + rr / R];
+      const float dv = sum16(sm[oB + tix(rr, nA + i)] * acc0[j] + sm[oB + tix(rr, nB + i)] * acc1[j]);
+      if (i == 0) sc[sDvP + (w & 1) * 64 + rr] = dv;
+      const float v = sc[sV + rr / R];
+      acc0[j] *= v;
+      acc1[j] *= v;
     }
-    for (int k = tmin * R; k < 64; k += 4)
-      acc = mma4(sm[oM2 + tix(k + g, m0 + i)], sm[oC + tix(k + g, n0 + i)], acc);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) racc[j] += sum16(dv[j]);
-    rot_epilogue<R>(acc, sm + oB, rev, dphi, false, a.dB, a, b, hh, t0, m0, n0);
+    mma_pipe2(acc0, acc1, m0, 64, [&](int k, float& a0, float& b0, float& a1, float& b1) {
+      a0 = sm[oM2 + tix(k + g, m0 + i)];
+      a1 = a0;
+      b0 = sm[oC + tix(k + g, nA + i)];
+      b1 = sm[oC + tix(k + g, nB + i)];
+    });
+    rot_epilogue<R>(acc0, sm + oB, rev, dphi, false, a.dB, a, b, hh, t0, m0, nA);
+    rot_epilogue<R>(acc1, sm + oB, rev, dphi, false, a.dB, a, b, hh, t0, m0, nB);
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (i == 0) sc[sDvP + (w & 1) * 64 + m0 + 4 * g + j] = racc[j];
   // ---- dx = diag(V) B~ E~ + M1^T dY ------------------------------------------------------
+  {
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    mma_pipe2(acc0, acc1, 0, 64, [&](int k, float& a0, float& b0, float& a1, float& b1) {
+      a0 = sm[oB + tix(m0 + i, k + g)];
+      a1 = a0;
+      b0 = sm[oE + tix(k + g, nA + i)];
+      b1 = sm[oE + tix(k + g, nB + i)];
+    });
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int n0 = (2 * (w & 1) + q) * 16;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k = 0; k < 64; k += 4)
-      acc = mma4(sm[oB + tix(m0 + i, k + g)], sm[oE + tix(k + g, n0 + i)], acc);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] *= sc[sV + (m0 + 4 * g + j) / R];
-    for (int k = tmin * R; k < 64; k += 4)
-      acc = mma4(sm[oM1 + tix(k + g, m0 + i)], sm[oDY + tix(k + g, n0 + i)], acc);
+    for (int j = 0; j < 4; ++j) {
+      const float v = sc[sV + (m0 + 4 * g + j) / R];
+      acc0[j] *= v;
+      acc1[j] *= v;
+    }
+    mma_pipe2(acc0, acc1, m0, 64, [&](int k, float& a0, float& b0, float& a1, float& b1) {
+      a0 = sm[oM1 + tix(k + g, m0 + i)];
+      a1 = a0;
+      b0 = sm[oDY + tix(k + g, nA + i)];
+      b1 = sm[oDY + tix(k + g, nB + i)];
+    });
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rr = m0 + 4 * g + j, t = rr / R;
-      if (t0 + t < a.T)
-        a.dx[((((size_t)b * a.T + t0 + t) * a.H + hh) * R + rr % R) * 64 + n0 + i] = acc[j];
+      if (t0 + t < a.T) {
+        float* o = a.dx + ((((size_t)b * a.T + t0 + t) * a.H + hh) * R + rr % R) * 64;
+        o[nA + i] = acc0[j];
+        o[nB + i] = acc1[j];
+      }
     }
   }
   __syncthreads();
@@ -675,46 +849,61 @@ __global__ void __launch_bounds__(kBT) bwc_grads_kernel(BackwardArgs a, int nC) 
     }
   }
   __syncthreads();
-  if (tid < L) {
+  if (tid < 64) {
     const int t = tid, gt = t0 + t;
     const size_t ntok = (size_t)a.nb * a.T * a.H;
     float* F0 = a.dAc;
     float* F1 = F0 + ntok;
     float* F2 = F1 + ntok;
-    float* F3 = F2 + ntok;
-    if (gt < a.T) {
+    float* dAp = F2 + ntok;  // per chunk: its tokens' share of dA
+    float da = 0.f;
+    if (t < L && gt < a.T) {
       const size_t tok = ((size_t)b * a.T + gt) * a.H + hh;
       const float d = sc[sDt + t], lm = sc[sLam + t], z = sc[sZ + t], dg = sc[sDg + t];
       F0[tok] = a.A[hh] * z + dg * lm + sc[sThp + t];
       F1[tok] = dg * d;
-      F3[tok] = d * z;
+      da = d * z;
       if (gt + 1 < a.T) F2[tok + a.H] = sc[sDo + t];
     }
+    for (int o = 32; o > 0; o >>= 1) da += __shfl_xor(da, o);
+    if (t == 0) dAp[(size_t)unit * nC + c] = da;
+  }
+  __syncthreads();  // the LDS is rewritten by the next chunk
   }
 }
 
-// dt and lam of every token from the chunks' partials, and dA[h] summed over
-// (batch, time) in a fixed order.
-__global__ void __launch_bounds__(1024) bwc_final_kernel(BackwardArgs a) {
-  __shared__ float s[1024];
-  const int hh = blockIdx.x;
-  const size_t n = (size_t)a.nb * a.T, ntok = n * a.H;
+// dt and lam of every token from the chunks' partials (one thread per
+// token), and (the last H workgroups) dA[h], the head's chunk partials
+// summed in a fixed order.
+constexpr int kFinThreads = 256;
+__global__ void __launch_bounds__(kFinThreads) bwc_final_kernel(BackwardArgs a, int nC) {
+  const size_t ntok = (size_t)a.nb * a.T * a.H;
   const float* F0 = a.dAc;
   const float* F1 = F0 + ntok;
   const float* F2 = F1 + ntok;
-  const float* F3 = F2 + ntok;
+  const float* dAp = F2 + ntok;
+  const size_t ntb = (ntok + kFinThreads - 1) / kFinThreads;
+  if (blockIdx.x < ntb) {
+    const size_t tok = (size_t)blockIdx.x * kFinThreads + threadIdx.x;
+    if (tok < ntok) {
+      const bool first = ((tok / a.H) % a.T) == 0;  // no token before it: no omega term
+      const float f2 = first ? 0.f : F2[tok];
+      a.ddt[tok] = F0[tok] + f2 * (1.f - a.lam[tok]);
+      a.dlam[tok] = F1[tok] - f2 * a.dt[tok];
+    }
+    return;
+  }
+  __shared__ float s[kFinThreads];
+  const int hh = (int)(blockIdx.x - ntb);
+  const int n = a.nb * nC;  // (batch, chunk) partials of head hh
   float v = 0.f;
-  for (size_t i = threadIdx.x; i < n; i += 1024) {
-    const size_t tok = i * a.H + hh;
-    const bool first = (i % a.T) == 0;  // no token before it: no omega term
-    const float f2 = first ? 0.f : F2[tok];
-    a.ddt[tok] = F0[tok] + f2 * (1.f - a.lam[tok]);
-    a.dlam[tok] = F1[tok] - f2 * a.dt[tok];
-    v += F3[tok];
+  for (int q = threadIdx.x; q < n; q += kFinThreads) {
+    const int bb = q / nC, cc = q - bb * nC;
+    v += dAp[((size_t)bb * a.H + hh) * nC + cc];
   }
   s[threadIdx.x] = v;
   __syncthreads();
-  for (int w = 512; w > 0; w >>= 1) {
+  for (int w = kFinThreads / 2; w > 0; w >>= 1) {
     if ((int)threadIdx.x < w) s[threadIdx.x] += s[threadIdx.x + w];
     __syncthreads();
   }
@@ -733,9 +922,18 @@ hipError_t launch_r(const BackwardArgs& a, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwc_chain_kernel, dim3(units, 2, 8), dim3(256), 0, stream, a, nC);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwc_grads_kernel<T, R>), dim3(units * nC), dim3(kBT), kLdsGrads, stream, a, nC);
+  // one workgroup per CU (the LDS holds one), each over several chunks
+  int dev = 0, cus = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return e;
+  const unsigned nchunk = units * nC;
+  const unsigned ngrid = nchunk < (unsigned)cus ? nchunk : (unsigned)cus;
+  hipLaunchKernelGGL((bwc_grads_kernel<T, R>), dim3(ngrid), dim3(kBT), kLdsGrads, stream, a, nC);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwc_final_kernel, dim3(a.H), dim3(1024), 0, stream, a);
+  const size_t ntb = ((size_t)a.nb * a.T * a.H + kFinThreads - 1) / kFinThreads;
+  hipLaunchKernelGGL(bwc_final_kernel, dim3((unsigned)(ntb + a.H)), dim3(kFinThreads), 0, stream, a,
+                     nC);
   return hipGetLastError();
 }
 
