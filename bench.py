@@ -628,6 +628,24 @@ def counter_sequence():
                        g["dt"][cur], g["A"], g["lam"][cur], g["theta"][cur])
     torch.cuda.synchronize()
     del g, h
+    # the backward at the SISO shape, then the MIMO block passes (B4 T4096 H16
+    # N = P = 64, R = 4), once each
+    cfg = I.WORKLOADS[1]
+    g = upload(I.config_inputs(1))
+    dy = torch.randn(g["x"].shape, device="cuda:0").to(g["x"].dtype)
+    m3.backward(g["x"], g["dt"], g["A"], g["lam"], g["theta"], g["B"], g["C"], dy)
+    torch.cuda.synchronize()
+    del g, dy
+    nb, T, H, N, P, R = 4, 4096, 16, 64, 64, 4
+    inp = I.block_inputs(nb, T, H, N, P, R, "bf16", seed=144)
+    g = upload(dict(x_raw=inp["x_raw"], B_raw=inp["B_raw"], C_raw=inp["C_raw"], dtype="bf16"))
+    w = {k: torch.from_numpy(inp[k]).to("cuda:0")
+         for k in ("norm_B", "norm_C", "bias_B", "bias_C", "up", "down")}
+    X, _, _ = m3.block_prepass(g["x"], g["B"], g["C"], w["norm_B"], w["norm_C"], w["bias_B"],
+                               w["bias_C"], w["up"], 1e-6)
+    m3.block_postpass(X, w["down"])
+    torch.cuda.synchronize()
+    del g, w, X, inp
     src = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -651,7 +669,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="short untimed sequence for rocprofv3 counter runs: SISO prefill x3, "
-                         "long SISO prefill x1, 10 decode steps, and a 512 MiB device copy x3 "
+                         "long SISO prefill x1, MIMO prefill x1, 10 decode steps, the SISO "
+                         "backward x1, the MIMO block passes x1, and a 512 MiB device copy x3 "
                          "(the copy calibrates the byte counters)")
     args = ap.parse_args()
 
