@@ -505,7 +505,7 @@ def cpu_baseline(cfg, inp, budget_s=20.0):
             "kind": "oracle", "cores_available": avail, "cores_capped_at": 16,
             "cpu_model": model,
             "sample": "%d of %d (batch, head) units over all %d tokens, fp64 C oracle, "
-                      "%d run(s) of %.3f s" % (n, nunits, cfg.seqlen, reps, dt)}
+                      "%d run(s) of %.3g s" % (n, nunits, cfg.seqlen, reps, dt)}
 
 
 def cpu_baseline_decode(cfg, inp, steps=10):
