@@ -1481,12 +1481,21 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
 // (the ticket word was not zero at entry) or a nonzero status word of its
 // own means dirty counters: the caller reports it (bad_ticket) and touches
 // nothing else.  s_misc: two ints of LDS.
+// The status word of ticket blockIdx.x is read together with the ticket,
+// before knowing it: workgroups mostly draw the ticket of their own index,
+// and then the check costs no second round trip to the device-coherent
+// level (reading it early is harmless: only the ticket's holder writes it).
 __device__ __forceinline__ int take_ticket(const PrefillArgs& a, int* s_misc) {
   if (threadIdx.x == 0) {
+    const int guess = (int)blockIdx.x;
+    const int st_guess = __hip_atomic_load(a.status + guess, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int t = atomicAdd(a.ticket, 1);
-    if (t >= 0 && t < (int)gridDim.x &&
-        __hip_atomic_load(a.status + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
-      t = -1;
+    if (t >= 0 && t < (int)gridDim.x) {
+      const int st = t == guess ? st_guess
+                                : __hip_atomic_load(a.status + t, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+      if (st != 0) t = -1;
+    }
     s_misc[0] = t;
   }
   __syncthreads();
@@ -1497,19 +1506,21 @@ __device__ __forceinline__ void bad_ticket(const PrefillArgs& a) {
 }
 
 // The last workgroup to finish zeroes the chain counters, so the next call
-// on this workspace starts from zeros without a reset launch (every other
+// on this workspace starts from zeros without a reset launch.  Every other
 // workgroup has published and read every status word it touches before
-// counting itself done).
+// counting itself done: its reads returned their values (the waits used
+// them) and its own stores are complete (s_waitcnt before the count), so the
+// count needs no fence; the zeroing follows the count's returned value, and
+// the next call sees it across the kernel boundary.
 __device__ __forceinline__ void finish_workgroup(const PrefillArgs& a, int* s_misc) {
   const int tid = threadIdx.x;
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);
     s_misc[1] = atomicAdd(a.done, 1) == (int)gridDim.x - 1;
   }
   __syncthreads();
   if (s_misc[1]) {
-    __threadfence();
     for (int i = tid; i < (int)gridDim.x; i += kT) a.status[i] = 0;
     if (tid == 0) {
       *a.ticket = 0;
