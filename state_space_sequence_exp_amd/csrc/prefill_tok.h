@@ -39,10 +39,10 @@
 // three (B, rotated in place into B~; C, rotated in place into C~; the
 // weighted B~; x; theta; dt and lam; the per-token scalars; the chunk's
 // rotation; the entry state).  A step is [rotate chunk c: read and write
-// buffer c] -- barrier -- [issue the loads of chunk c + 2; MFMA: read buffer
-// c], so one barrier per chunk suffices, waves that finish their MFMA work go
-// on to rotate the next chunk while others still multiply, and the loads
-// have a whole step to arrive.
+// buffer c] -- barrier -- [MFMA: read buffer c; then issue the loads of chunk
+// c + 2], so one barrier per chunk suffices, waves that finish their MFMA
+// work go on to rotate the next chunk while others still multiply, and the
+// loads have the next step to arrive.
 #pragma once
 
 #include "prefill_impl.h"
@@ -598,11 +598,15 @@ __device__ __forceinline__ void tok_segment(const PrefillArgs& a, int ticket,
     // the next item's loads (issued a step ago) have landed
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // the buffer of item i + NB - 1 was last read in the previous step's
-    // MFMA phase, which every wave has finished
-    issue(i + NB - 1);
     if (!local) tok_outputs<C>(a, s, c, t);
     tok_state_update<C>(t, __expf(cse), stt);
+    // the buffer of item i + NB - 1 was last read in the previous step's
+    // MFMA phase, which every wave finished before this step's barrier.  Its
+    // loads go out after this step's own LDS-heavy MFMA work (issued at the
+    // barrier they competed with it: 58.7 against 55.0 us on the SISO bench
+    // shape) and still have the next step to land; at the end of the local
+    // pass they fly during the chain (issued after it: 58.8 us)
+    issue(i + NB - 1);
     if (local) seg_logdecay += cse;
     if (i == K - 1) {
       // ---- between the passes: the chain (chain_phase) -------------------
