@@ -305,8 +305,18 @@ m3_status m3_decode_step_mfma(const m3_dims* dims, m3_dtype dtype, const float* 
  * with G_t = dL/dh_t, G_t = C_t dy_t^T + alpha_{t+1} R_{t+1}^T G_{t+1}, and
  * each token's gradients follow from h_t, h_{t-1} and G_t.
  *
- * With N * P <= 4096 the sequence is cut into segments of S tokens (32,
- * or 16 or 8 where the segment's staged inputs would not fit the LDS): a
+ * With N = P = 64 (R of 1, 2 or 4) the gradients are taken by chunks of
+ * L = 64 / R tokens with the contractions on the matrix cores (float32): a
+ * local pass forms each chunk's state and adjoint contributions, a chain
+ * pass composes them into every chunk's entry state and exit adjoint, a
+ * gradient pass forms every token's gradients from its chunk's products,
+ * and a final pass combines the per-token scalar partials.  The workspace
+ * holds, per (batch, head), nC + 1 entry states and nC exit adjoints
+ * (N x P float each, nC = ceil(T / L)), 65 floats per chunk and 16 bytes
+ * per token (each area rounded up to 256 bytes).  Four kernel launches.
+ * Other shapes with N * P <= 4096: the sequence is cut into segments of S
+ * tokens (32, or 16 or 8 where the segment's staged inputs would not fit the
+ * LDS): a
  * local pass walks every segment from a zero state both ways, a chain pass
  * composes the segments into each one's entry state and exit adjoint, and
  * a gradient pass recomputes each segment's states in blocks of 8 tokens
@@ -318,7 +328,7 @@ m3_status m3_decode_step_mfma(const m3_dims* dims, m3_dtype dtype, const float* 
  * in the workspace instead (8 N P bytes per token-head plus 4), so the call
  * moves about 5 x 4 N P bytes per token-head through HBM.  Four kernel
  * launches.
- * m3_backward_workspace_size gives the bytes for either case.  dy has x's
+ * m3_backward_workspace_size gives the bytes for each case.  dy has x's
  * layout and storage type; dh_final, if given, is [batch, H, N, P] float.
  * lam and theta are required.  N must be 16, 32, 64, 128 or 256 with
  * N * P <= 8192; P and R as for m3_prefill.  x and dy need 16-byte
