@@ -1334,7 +1334,9 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
   s.rowTh = (uint32_t)(a.H * (a.N / 2) * 4);
   s.rowDt = (uint32_t)(a.H * 4);
   s.rowX = (uint32_t)(a.H * C::R * P * C::es);
-  s.Ah = a.A[s.h];
+  // a uniform value, taken into a scalar register here so that its load is
+  // complete before the chunk loops
+  s.Ah = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.A[s.h])));
 
   Map m;
   m.act = tid < lay.items;
@@ -1425,6 +1427,10 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
   f32x4 ent[kMaxStTiles];
   __syncthreads();  // s_srot
   chain_phase<C>(a, wr, s.seg, s.bh, ticket, segD, s_srot, s_misc, stt, ent);
+  // every load of the chain has returned (a load whose value the chain did
+  // not need would otherwise leave the compiler a pending write to its
+  // register, waited for inside the output pass)
+  __builtin_amdgcn_s_waitcnt(0);
   // the output pass's state distribution (see Cfg::kSplit3): the entry
   // state moves to its waves through LDS
   WaveRoles wr3 = wr;

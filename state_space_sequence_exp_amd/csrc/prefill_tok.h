@@ -143,20 +143,60 @@ struct TCtx {
 };
 
 typedef void __attribute__((address_space(3))) lds_void;
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+
+// Words of a raw buffer resource: base, no stride, `bytes` in range.
+__device__ __forceinline__ u32x4v rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return u32x4v{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, (uint32_t)pf::kRsrcWord3};
+}
+
+// LDS byte address of a pointer into the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p);
+}
+
+// One direct global-to-LDS load: lane l's kBytes (4 or 16) at byte `voff` of
+// the range land at LDS byte lds + kBytes l (zeros past the range).  Written
+// as assembly because the compiler, which cannot tell which LDS bytes such a
+// load writes, would otherwise make this wave's next LDS access wait for all
+// of them; the caller orders the LDS instead: a barrier between the last
+// read of a buffer and the loads into it, and s_waitcnt vmcnt, then a
+// barrier, before the first read of what they bring.  M0 carries the LDS
+// base (one wait state after its write) and is restored afterwards.
+template <int kBytes>
+__device__ __forceinline__ void dma_lds(u32x4v r, uint32_t lds, uint32_t voff) {
+  uint32_t saved;
+  if constexpr (kBytes == 16) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory");
+  } else {
+    static_assert(kBytes == 4, "4 or 16 bytes a lane");
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory");
+  }
+}
 
 // One 1 KB block of a row-major tile of `rowb`-byte rows (128 or 256) by a
 // direct load: lane l fills slot l, i.e. row (row0 + l / cpr) and physical
 // 16-byte column l % cpr, with the logical column that the tile's swizzle
 // puts there; `gbyte(row)` is the row's byte offset in the buffer range.
 template <uint32_t kRowb, class F>
-__device__ __forceinline__ void lds_block(rsrc r, unsigned char* tile, uint32_t row0, F gbyte) {
+__device__ __forceinline__ void lds_block(u32x4v r, unsigned char* tile, uint32_t row0, F gbyte) {
   constexpr uint32_t cpr = kRowb / 16;  // 16-byte columns per row
   constexpr uint32_t mask = (cpr < 8u ? cpr : 8u) - 1u;
   const uint32_t l = threadIdx.x & 63;
   const uint32_t row = row0 + l / cpr, pc = l % cpr;
   const uint32_t lc = pc ^ (row & mask);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + row0 * kRowb), 16,
-                                           gbyte(row) + lc * 16, 0, 0, 0);
+  dma_lds<16>(r, lds_addr(tile + row0 * kRowb), gbyte(row) + lc * 16);
 }
 
 // Issue this wave's share of the direct loads of chunk c into ring buffer
@@ -175,10 +215,11 @@ __device__ __forceinline__ void tok_issue(const PrefillArgs& a, const TCtx& s, i
   const uint32_t last = (uint32_t)(len - 1);
   constexpr uint32_t bcb = R * N * 2, xb = R * P * 2;
   // ranges end at the chunk's last valid byte: rows past the sequence land as 0
-  const rsrc rB = make_rsrc(static_cast<const unsigned char*>(a.B) + hrow * bcb, last * s.rowB + bcb);
-  const rsrc rX = make_rsrc(static_cast<const unsigned char*>(a.x) + hrow * xb, last * s.rowX + xb);
-  const rsrc rTh = a.theta ? make_rsrc(a.theta + hrow * (N / 2), last * s.rowTh + (N / 2) * 4)
-                           : make_rsrc(nullptr, 0);
+  const u32x4v rB =
+      rsrc_words(static_cast<const unsigned char*>(a.B) + hrow * bcb, last * s.rowB + bcb);
+  const u32x4v rX = rsrc_words(static_cast<const unsigned char*>(a.x) + hrow * xb, last * s.rowX + xb);
+  const u32x4v rTh = a.theta ? rsrc_words(a.theta + hrow * (N / 2), last * s.rowTh + (N / 2) * 4)
+                             : rsrc_words(nullptr, 0);
   const uint32_t rowB = s.rowB, rowX = s.rowX, rowTh = s.rowTh;
   // B and C rows are (token, rank): token u = row / R, rank row % R
   auto gB = [rowB](uint32_t row) { return (row / R) * rowB + (row % R) * (N * 2); };
@@ -190,8 +231,8 @@ __device__ __forceinline__ void tok_issue(const PrefillArgs& a, const TCtx& s, i
   for (uint32_t j = w; j < kBlkN; j += kW)
     lds_block<C::kRowN>(rB, buf + C::oB, j * kRowsN, gB);
   if constexpr (kWithC) {
-    const rsrc rC =
-        make_rsrc(static_cast<const unsigned char*>(a.C) + hrow * bcb, last * s.rowB + bcb);
+    const u32x4v rC =
+        rsrc_words(static_cast<const unsigned char*>(a.C) + hrow * bcb, last * s.rowB + bcb);
     for (uint32_t j = w; j < kBlkN; j += kW)
       lds_block<C::kRowN>(rC, buf + C::oC, j * kRowsN, gB);
   }
@@ -205,17 +246,14 @@ __device__ __forceinline__ void tok_issue(const PrefillArgs& a, const TCtx& s, i
     const uint32_t u = threadIdx.x & 63;
     const int nsc = min(kL + 1, a.T - t0);
     const uint32_t scb = (uint32_t)(nsc - 1) * s.rowDt + 4;
-    const rsrc rD = make_rsrc(a.dt + hrow, scb);
-    lds_void* raw = (lds_void*)(buf + C::oRaw);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, raw, 4, u * s.rowDt, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (lds_void*)(buf + C::oRaw + 256), 4,
-                                             (u + 1) * s.rowDt, 0, 0, 0);
+    const u32x4v rD = rsrc_words(a.dt + hrow, scb);
+    const uint32_t raw = lds_addr(buf + C::oRaw);
+    dma_lds<4>(rD, raw, u * s.rowDt);
+    dma_lds<4>(rD, raw + 256, (u + 1) * s.rowDt);
     if (a.lam) {
-      const rsrc rL = make_rsrc(a.lam + hrow, scb);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (lds_void*)(buf + C::oRaw + 512), 4,
-                                               u * s.rowDt, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (lds_void*)(buf + C::oRaw + 768), 4,
-                                               (u + 1) * s.rowDt, 0, 0, 0);
+      const u32x4v rL = rsrc_words(a.lam + hrow, scb);
+      dma_lds<4>(rL, raw + 512, u * s.rowDt);
+      dma_lds<4>(rL, raw + 768, (u + 1) * s.rowDt);
     }
   }
 }
@@ -553,7 +591,9 @@ __device__ __forceinline__ void tok_segment(const PrefillArgs& a, int ticket,
   s.rowTh = (uint32_t)(a.H * (C::N / 2) * 4);
   s.rowDt = (uint32_t)(a.H * 4);
   s.rowX = (uint32_t)(a.H * C::R * C::P * 2);
-  s.Ah = a.A[s.h];
+  // a uniform value, taken into a scalar register here so that its load is
+  // complete before the chunk loop
+  s.Ah = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.A[s.h])));
   const bool has_lam = a.lam != nullptr;
   int* s_misc = reinterpret_cast<int*>(smem + C::oMisc);
   float2* s_srot = reinterpret_cast<float2*>(smem + C::oSrot);
@@ -622,6 +662,10 @@ __device__ __forceinline__ void tok_segment(const PrefillArgs& a, int ticket,
                          ent);
 #pragma unroll
       for (int q = 0; q < kMaxStTiles; ++q) stt[q] = ent[q];
+      // every load of the chain has returned: otherwise a load whose value
+      // the chain did not need leaves the compiler a pending write to its
+      // register, and it would wait for all memory at the top of every step
+      __builtin_amdgcn_s_waitcnt(0);
     }
   }
 }
