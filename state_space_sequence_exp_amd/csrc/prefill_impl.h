@@ -287,21 +287,31 @@ __device__ __forceinline__ void issue_loads(const PrefillArgs& a, const Ctx& s, 
 
 // dt and lam of tokens lane, lane + 64, lane + 128 of chunk c, up to the end
 // of the sequence (the token after the chunk feeds omega of its last token).
+// With NJ = 2 (chunks of at most 64 tokens) the third group is not loaded
+// and reads as zero.
+// With `real` false the range is empty: the loads read zeros and touch no
+// memory.
+template <int NJ = 3>
 __device__ __forceinline__ void scalar_loads(const PrefillArgs& a, const Ctx& s, int c,
-                                             float (&wd)[3], float (&wl)[3]) {
+                                             float (&wd)[3], float (&wl)[3], bool real) {
   const int t0 = c * a.L;
   const size_t hrow = ((size_t)s.b * a.T + t0) * a.H + s.h;
   // the range covers the 3 * 64 tokens read at most (a range over the rest of
   // the sequence could wrap 32 bits on long sequences with many heads)
-  const uint32_t bytes = (uint32_t)(min(a.T - t0, 3 * kWave) - 1) * s.rowDt + 4;
+  const uint32_t bytes = real ? (uint32_t)(min(a.T - t0, 3 * kWave) - 1) * s.rowDt + 4 : 0u;
   const rsrc rw = make_rsrc(a.dt + hrow, bytes);
   const rsrc rl = a.lam ? make_rsrc(a.lam + hrow, bytes) : make_rsrc(nullptr, 0);
 #pragma unroll
   for (int jj = 0; jj < 3; ++jj) {
     const uint32_t o = (uint32_t)((threadIdx.x & 63) + jj * 64) * s.rowDt;
-    wd[jj] = __uint_as_float(ld32(rw, o));
-    // without lam the weight is 1 (the exponential-Euler rule)
-    wl[jj] = a.lam ? __uint_as_float(ld32(rl, o)) : 1.f;
+    if (jj < NJ) {
+      wd[jj] = __uint_as_float(ld32(rw, o));
+      // without lam the weight is 1 (the exponential-Euler rule)
+      wl[jj] = a.lam ? __uint_as_float(ld32(rl, o)) : 1.f;
+    } else {
+      wd[jj] = 0.f;
+      wl[jj] = 0.f;
+    }
   }
 }
 
@@ -1379,9 +1389,10 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
   Stage<C> stg;
   issue_loads<C, false>(a, s, m, s.c0, stg);
   const bool scal_wave = __builtin_amdgcn_readfirstlane(tid >> 6) == kScalarWave;
+  constexpr int NJ = C::NC != 0 ? 2 : 3;  // N fixed: chunks of at most 64 tokens
   if (scal_wave) {
     float wd[3], wl[3];
-    scalar_loads(a, s, s.c0, wd, wl);
+    scalar_loads<NJ>(a, s, s.c0, wd, wl, true);
     const int t0c = s.c0 * a.L;
     chunk_scalars(a, t0c, min(a.L, a.T - t0c), s.Ah, wd, wl, s_scal);
   }
@@ -1392,6 +1403,16 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     const Ctx s = step_ctx(s0);
     const Tiles t = step_tiles<C>(tiles0, smem);
     const double inw = step_partials<C>(a, lay, s, m, c, stg, sc, smem);
+    // the next chunk's dt and lam (the first chunk's again after the last,
+    // for phase 3), for the scalar wave, requested once the staged angles
+    // are summed: they have the rest of the step to arrive, and are not
+    // queued behind the next chunk's staging loads.  Every wave issues these
+    // loads (the others over an empty range, which reads zeros without a
+    // memory access), so that each wave has the same loads in flight where
+    // it waits for its staged registers
+    const int nc = c + 1 < s.c1 ? c + 1 : s.c0;
+    float wd[3], wl[3];
+    scalar_loads<NJ>(a, s, nc, wd, wl, scal_wave);
     __syncthreads();
     step_rotate<C, false, true>(a, lay, s, m, c, stg, sc, t, inw, smem);
     // prefetch the next chunk; the last step prefetches the first chunk
@@ -1400,15 +1421,11 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
       issue_loads<C, false>(a, s, m, c + 1, stg);
     else
       issue_loads<C, true>(a, s, m, s.c0, stg);
-    // the scalar wave prepares the next chunk's scalars (the first chunk's
-    // again after the last, for phase 3) in the other buffer
-    const int nc = c + 1 < s.c1 ? c + 1 : s.c0;
-    float wd[3], wl[3];
-    if (scal_wave) scalar_loads(a, s, nc, wd, wl);
     __syncthreads();
     const float lc = sc[4 * kLMax];
     seg_logdecay += lc;
     state_update<C>(a, lay, wr, __expf(lc), stt, t.W, t.X, smem);
+    // the scalar wave prepares the next chunk's scalars in the other buffer
     if (scal_wave)
       chunk_scalars(a, nc * a.L, min(a.L, a.T - nc * a.L), s.Ah, wd, wl,
                     s_scal + (buf ^ 1) * (kScalBytes / 4));
@@ -1463,6 +1480,8 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     const Ctx s = step_ctx(s0);
     const Tiles t = step_tiles<C>(tiles0, smem);
     const double inw = step_partials<C>(a, lay, s, m, c, stg, sc, smem);
+    float wd[3], wl[3];
+    scalar_loads<NJ>(a, s, more ? c + 1 : c, wd, wl, more && scal_wave);
     __syncthreads();
     step_rotate<C, true, false>(a, lay, s, m, c, stg, sc, t, inw, smem);
     state_to_lds<C>(a, wr3, stt, t.G);
@@ -1470,8 +1489,6 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     __syncthreads();
     chunk_output<C>(a, lay, wr, s, chunk_res<C>(a, s, c), sc, t.C, t.B, t.X, t.G);
     if (more) {
-      float wd[3], wl[3];
-      if (scal_wave) scalar_loads(a, s, c + 1, wd, wl);
       state_update<C, NSW3>(a, lay, wr3, __expf(sc[4 * kLMax]), stt, t.W, t.X, smem);
       if (scal_wave)
         chunk_scalars(a, (c + 1) * a.L, min(a.L, a.T - (c + 1) * a.L), s.Ah, wd, wl,
