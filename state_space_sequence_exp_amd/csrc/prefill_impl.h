@@ -166,12 +166,39 @@ struct Cfg {
   static constexpr bool kWaveSums = N_ != 0 && 64 % (N_ / 2) == 0 && 64 / (N_ / 2) <= 2;
 };
 
-// Raw inputs of one chunk for this thread, staged in registers.
+// Raw inputs of one chunk for this thread, staged in registers.  With wave
+// sums every lane of a wave has its tokens among the wave's 64 / (N / 2)
+// blocks, so the wave loads those tokens' dt once (lane j: the wave's token
+// j, in dtw) and each lane takes its own when they are used (stage_dt).
 template <class C>
 struct Stage {
   float th[C::S], dt[C::S];                                  // rotation item
+  uint32_t dtw;
   uint32_t b[C::KR * C::PW], c[C::KR * C::PW], x[C::KR * C::PW];
 };
+
+// This thread's dt of its rotation item's tokens.
+template <class C>
+__device__ __forceinline__ void stage_dt(const Stage<C>& st, float (&dt)[C::S]) {
+  if constexpr (C::kWaveSums) {
+    // lanes 32..63 hold the wave's second block when there are two
+    constexpr int kBlocks = 64 / (C::NC / 2);
+    const bool upper = kBlocks == 2 && (threadIdx.x & 32) != 0;
+#pragma unroll
+    for (int j = 0; j < C::S; ++j) {
+      const float lo = __uint_as_float(__builtin_amdgcn_readlane(st.dtw, j));
+      if constexpr (kBlocks == 2) {
+        const float hi = __uint_as_float(__builtin_amdgcn_readlane(st.dtw, C::S + j));
+        dt[j] = upper ? hi : lo;
+      } else {
+        dt[j] = lo;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < C::S; ++j) dt[j] = st.dt[j];
+  }
+}
 
 // The wave that computes the per-token scalars of the next chunk during the
 // MFMA phase (it holds no output unit when the outputs fit in few waves).
@@ -189,6 +216,8 @@ struct Ctx {
 struct Map {
   int kp, blk, jp, xblk;
   bool act, xact;
+  bool xwave;  // some lane of this wave has an x item (uniform)
+  int wblk;    // block of the wave's lane 0 (uniform)
 };
 
 struct ChunkRes {
@@ -218,14 +247,17 @@ __device__ __forceinline__ ChunkRes chunk_res(const PrefillArgs& a, const Ctx& s
 // Rotation-item inputs (theta, dt, B and optionally C) of item (kp, blk).
 template <class C, bool kWithC>
 __device__ __forceinline__ void load_item(const PrefillArgs& a, const Ctx& s, const ChunkRes& r,
-                                          uint32_t vB, uint32_t vTh, uint32_t vDt,
-                                          float (&th)[C::S], float (&dt)[C::S],
+                                          uint32_t vB, uint32_t vTh, uint32_t vDt, uint32_t vDw,
+                                          float (&th)[C::S], float (&dt)[C::S], uint32_t& dtw,
                                           uint32_t (&bv)[C::KR * C::PW],
                                           uint32_t (&cv)[C::KR * C::PW]) {
 #pragma unroll
-  for (int j = 0; j < C::S; ++j) {
-    th[j] = __uint_as_float(ld32(r.th, vTh + j * s.rowTh));
-    dt[j] = __uint_as_float(ld32(r.dt, vDt + j * s.rowDt));
+  for (int j = 0; j < C::S; ++j) th[j] = __uint_as_float(ld32(r.th, vTh + j * s.rowTh));
+  if constexpr (C::kWaveSums) {
+    dtw = ld32(r.dt, vDw);
+  } else {
+#pragma unroll
+    for (int j = 0; j < C::S; ++j) dt[j] = __uint_as_float(ld32(r.dt, vDt + j * s.rowDt));
   }
 #pragma unroll
   for (int j = 0; j < C::S; ++j)
@@ -281,8 +313,16 @@ __device__ __forceinline__ void issue_loads(const PrefillArgs& a, const Ctx& s, 
   const uint32_t vDt = m.act ? tb * s.rowDt : kOOB;
   const uint32_t vX = m.xact ? (uint32_t)(m.xblk * C::S) * s.rowX + (uint32_t)(2 * m.jp * C::es)
                              : kOOB;
-  load_item<C, kWithC>(a, s, r, vB, vTh, vDt, st.th, st.dt, st.b, st.c);
-  load_x_item<C>(s, r, vX, st.x);
+  // wave sums: lane j loads the dt of the wave's token j (its first block's
+  // first token on), for the wave's 64 / (N / 2) blocks of S tokens
+  uint32_t vDw = kOOB;
+  if constexpr (C::kWaveSums) {
+    const uint32_t lane = threadIdx.x & 63;
+    vDw = lane < (uint32_t)(64 / (C::NC / 2) * C::S) ? (m.wblk * C::S + lane) * s.rowDt : kOOB;
+  }
+  load_item<C, kWithC>(a, s, r, vB, vTh, vDt, vDw, st.th, st.dt, st.dtw, st.b, st.c);
+  // x items are dealt from thread 0: waves past them issue no x loads
+  if (m.xwave) load_x_item<C>(s, r, vX, st.x);
 }
 
 // dt and lam of tokens lane, lane + 64, lane + 128 of chunk c, up to the end
@@ -1004,7 +1044,9 @@ __device__ __forceinline__ double step_partials(const PrefillArgs& a, const Pref
   double* s_part = reinterpret_cast<double*>(smem + lay.off_part);
   if constexpr (C::kWaveSums) {
     if (!m.act) return 0.0;
-    const double own = item_angle_sum<C::S>(st.th, st.dt);
+    float dt[C::S];
+    stage_dt<C>(st, dt);
+    const double own = item_angle_sum<C::S>(st.th, dt);
     const int wave = threadIdx.x >> 6;
     if constexpr (C::NC / 2 == 32) {
       // lanes l and l + 32 hold blocks 2w and 2w + 1 of pair l % 32:
@@ -1025,7 +1067,9 @@ __device__ __forceinline__ double step_partials(const PrefillArgs& a, const Pref
       return 0.0;
     }
   } else {
-    if (m.act) s_part[m.blk * lay.npair + m.kp] = item_angle_sum<C::S>(st.th, st.dt);
+    float dt[C::S];
+    stage_dt<C>(st, dt);
+    if (m.act) s_part[m.blk * lay.npair + m.kp] = item_angle_sum<C::S>(st.th, dt);
     return 0.0;
   }
 }
@@ -1038,9 +1082,11 @@ __device__ __forceinline__ void step_rotate(const PrefillArgs& a, const PrefillL
                                             unsigned char* smem) {
   const float* s_w = sc + 3 * kLMax;
   if (m.xact) write_x_item<C>(m.jp, m.xblk, st.x, t.X);
+  float dt[C::S];
+  stage_dt<C>(st, dt);
   if (m.act)
     rotate_item<C, kWithC, kAccumSeg>(
-        lay.npair, lay.nblk, m.kp, m.blk, st.th, st.dt, st.b, st.c, s_w, t.B, t.C, t.W,
+        lay.npair, lay.nblk, m.kp, m.blk, st.th, dt, st.b, st.c, s_w, t.B, t.C, t.W,
         reinterpret_cast<const double*>(smem + lay.off_part), inw,
         reinterpret_cast<float2*>(smem + lay.off_crot), reinterpret_cast<double*>(smem + lay.off_sang));
 }
@@ -1355,6 +1401,8 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
   m.xact = tid < lay.xitems;
   m.jp = tid % (P / 2);
   m.xblk = tid / (P / 2);
+  m.xwave = __builtin_amdgcn_readfirstlane(wave) * kWave < lay.xitems;
+  m.wblk = __builtin_amdgcn_readfirstlane(wave * kWave / lay.npair);
 
   const Tiles tiles0 = make_tiles<C>(a, lay, smem);
   const Tiles& t = tiles0;
