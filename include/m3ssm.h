@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define M3SSM_VERSION 140 /* 1.4.0 */
+#define M3SSM_VERSION 150 /* 1.5.0 */
 
 typedef enum {
   M3_SUCCESS = 0,
@@ -123,18 +123,19 @@ size_t m3_prefill_workspace_size(const m3_dims* dims, int chunk, m3_dtype dtype)
  * segment: with units = batch * nheads and nC = ceil(seqlen / chunk), a
  * segment is K = min(nC, max(1, ceil(nC * units / 256))) chunks and there are
  * G = units * ceil(nC / K) of them (G < 256 + units, and G = units when
- * units >= 256).  The workspace starts with the chain's int32 counters --
- * word 0 the work ticket, word 1 the error word, word 2 the
- * finished-workgroup count, word 3 unused, then one status word per
- * segment: 16 + 4 G bytes -- and holds, from byte 4096 or from the first
- * 256-byte boundary past the counters (whichever is later), one slot per
- * segment (the map from its entry to its exit state, then its exit state)
- * and the entry state of each sequence.  A call needs its counters zero on
- * entry and leaves them zero (its last workgroup resets them), so a buffer
- * zero-filled once serves every later call as long as batch * nheads <=
- * 1020 (then 4 + G <= 1024 words), or as long as no call has more segments
- * than the call before it on this buffer; otherwise zero the counter bytes
- * before the call.
+ * units >= 256).  The workspace starts with the chain's int32 counters:
+ * the work-ticket counters of up to 8 classes of workgroups (class c's at
+ * word 32 c, so word 0 is class 0's), word 1 the error word, word 2 the
+ * finished-workgroup count, the other words below 256 unused, then from
+ * word 256 one status word per segment: 1024 + 4 G bytes.  From byte 8192
+ * or from the first 256-byte boundary past the counters (whichever is
+ * later) it holds one slot per segment (the map from its entry to its exit
+ * state, then its exit state) and the entry state of each sequence.  A call
+ * needs its counters zero on entry and leaves them zero (its last workgroup
+ * resets them), so a buffer zero-filled once serves every later call as
+ * long as batch * nheads <= 1792 (then 256 + G <= 2048 words), or as long
+ * as no call has more segments than the call before it on this buffer;
+ * otherwise zero the counter bytes before the call.
  *
  * Chain errors.  The error word is left nonzero, and stays so until cleared
  * (m3_prefill_workspace_error), when:
@@ -143,9 +144,9 @@ size_t m3_prefill_workspace_size(const m3_dims* dims, int chunk, m3_dtype dtype)
  *     NaN, so its y, every state it hands on (hence the rest of that
  *     sequence's y) and h_final are NaN.
  *  2  the counters were not zero on entry, as seen by a workgroup whose
- *     ticket lies past the grid (the ticket word was not zero) or whose own
- *     status word was not zero.  That workgroup computes nothing; others may
- *     then time out (1).  A nonzero finished-workgroup word (word 2) is not
+ *     ticket lies past the grid (its class's ticket word was not zero) or
+ *     whose own status word was not zero.  That workgroup computes nothing;
+ *     others may then time out (1).  A nonzero finished-workgroup word (word 2) is not
  *     detected: it makes the reset at the end of the call happen early or
  *     not at all, so zero-fill the counter bytes after any call that did not
  *     finish normally.

@@ -49,10 +49,32 @@ struct PrefillArgs {
                       //        rotation (cos, sin) per pair [N/2][2], decay, 3 unused
   float* cont_entry;  // [B*H][N][P] entry state of each sequence's first segment (cont)
   int* status;        // [grid] per ticket: 0 nothing, 1 aggregate, 2 exit state published
-  int* ticket;        // [1]   next segment ticket (work order)
+  int* ticket;        // ticket counters: class c's at ticket[kTicketStride c] (work order)
   int* err;           // [1]   1: a wait for a predecessor timed out; 2: counters not zero at entry
-  int* done;          // [1]   finished workgroups; the last one zeroes status, ticket, done
+  int* done;          // [1]   finished workgroups; the last one zeroes status, tickets, done
+  int ncls;           // ticket classes in use (a power of two dividing nb * H, at most 8)
 };
+
+// The prefill workspace's chain counters (int32 words).  Workgroups take
+// their tickets from one counter per class: workgroup b is in class b %
+// ncls and draws ticket c + ncls k from class c's counter, so a segment's
+// predecessors in its sequence (tickets t - j nb H, the same class when
+// ncls divides nb H) are drawn from its own counter, before its own.  Each
+// counter has a 128-byte line of its own, so the workgroups of a launch do
+// not all queue on one address.  Class 0's counter is word 0, the error word
+// 1 and the finished-workgroup count 2; class c's counter is word
+// kTicketStride c; the status words start at kStatusWord; the segments'
+// slots start at kSlotsMinBytes or past the status words.
+constexpr int kTicketClasses = 8;
+constexpr int kTicketStride = 32;
+constexpr int kStatusWord = kTicketClasses * kTicketStride;
+constexpr size_t kSlotsMinBytes = 8192;
+
+// Ticket classes for nb * H sequences: the largest power of two up to
+// kTicketClasses that divides it.
+__host__ __device__ constexpr int prefill_ticket_classes(long long units) {
+  return units % 8 == 0 ? 8 : (units % 4 == 0 ? 4 : (units % 2 == 0 ? 2 : 1));
+}
 
 // Floats of one segment's slot in the prefill workspace.
 __host__ __device__ constexpr size_t prefill_slot_floats(int N, int P) {

@@ -69,13 +69,14 @@ struct WsCarve {
   size_t grid, off_slots, off_cont, total;
 };
 
-// The counters come first, at offsets that do not depend on the shape:
-// int32 words ticket, error, finished workgroups, (unused), then one status
-// word per workgroup (segment).  The segments' slots (aggregate, exit state,
-// rotation and decay) start at 4 KiB or past the counters, whichever is
+// The counters come first, at offsets that do not depend on the shape (see
+// kStatusWord): the ticket counters, the error word and the
+// finished-workgroup count, then from word kStatusWord one status word per
+// workgroup (segment).  The segments' slots (aggregate, exit state, rotation
+// and decay) start at kSlotsMinBytes or past the counters, whichever is
 // later, then the continuation entry states.  A call has at most 256 + units
 // workgroups when units < 256 and exactly units otherwise, so calls with at
-// most 1020 units keep their counters below 4 KiB and never store states
+// most 1792 units keep their counters below 8 KiB and never store states
 // where any call keeps counters.
 WsCarve carve(const m3_dims* d, int chunk, m3_dtype /*dtype*/) {
   WsCarve w;
@@ -83,8 +84,8 @@ WsCarve carve(const m3_dims* d, int chunk, m3_dtype /*dtype*/) {
   const int nC = (int)((d->seqlen + chunk - 1) / chunk);
   const int K = m3::prefill_segment_chunks((int)d->batch, (int)d->nheads, nC > 0 ? nC : 1);
   w.grid = units * (size_t)((nC + K - 1) / K);
-  const size_t counters = round256((4 + w.grid) * sizeof(int));
-  w.off_slots = counters > 4096 ? counters : 4096;
+  const size_t counters = round256((m3::kStatusWord + w.grid) * sizeof(int));
+  w.off_slots = counters > m3::kSlotsMinBytes ? counters : m3::kSlotsMinBytes;
   const size_t np = (size_t)d->dstate_n * d->headdim_p;
   w.off_cont = w.off_slots + round256(w.grid * m3::prefill_slot_floats((int)d->dstate_n,
                                                                        (int)d->headdim_p) *
@@ -289,10 +290,11 @@ m3_status prefill_impl(const m3_dims* dims, m3_dtype dtype, int chunk, const flo
     a.ticket = reinterpret_cast<int*>(ws);
     a.err = a.ticket + 1;
     a.done = a.ticket + 2;
-    a.status = a.ticket + 4;
+    a.status = a.ticket + m3::kStatusWord;
+    a.ncls = m3::prefill_ticket_classes((long long)a.nb * a.H);
   }
   if (noalloc && work) {
-    const int nwords = (int)(4 + w.grid);
+    const int nwords = (int)(m3::kStatusWord + w.grid);
     const int blocks = (nwords + 255) / 256;
     hipLaunchKernelGGL(zero_words_kernel, dim3(blocks < 1024 ? blocks : 1024), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a.ticket, nwords);

@@ -1560,7 +1560,10 @@ __device__ __forceinline__ int take_ticket(const PrefillArgs& a, int* s_misc) {
   if (threadIdx.x == 0) {
     const int guess = (int)blockIdx.x;
     const int st_guess = __hip_atomic_load(a.status + guess, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int t = atomicAdd(a.ticket, 1);
+    // the class's counter (see kTicketStride): its workgroups, in the order
+    // they come, take the class's tickets in increasing order
+    const int cls = guess & (a.ncls - 1);
+    int t = cls + a.ncls * atomicAdd(a.ticket + kTicketStride * cls, 1);
     if (t >= 0 && t < (int)gridDim.x) {
       const int st = t == guess ? st_guess
                                 : __hip_atomic_load(a.status + t, __ATOMIC_RELAXED,
@@ -1593,10 +1596,8 @@ __device__ __forceinline__ void finish_workgroup(const PrefillArgs& a, int* s_mi
   __syncthreads();
   if (s_misc[1]) {
     for (int i = tid; i < (int)gridDim.x; i += kT) a.status[i] = 0;
-    if (tid == 0) {
-      *a.ticket = 0;
-      *a.done = 0;
-    }
+    if (tid < a.ncls) a.ticket[kTicketStride * tid] = 0;
+    if (tid == 0) *a.done = 0;
   }
 }
 

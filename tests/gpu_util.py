@@ -55,9 +55,10 @@ def prefill_grid(nb, nt, nh, chunk):
 
 
 def counter_words(nb, nt, nh, chunk):
-    """int32 words of the workspace's chain counters: four, then one status
-    word per workgroup."""
-    return 4 + prefill_grid(nb, nt, nh, chunk)
+    """int32 words of the workspace's chain counters: 256 (the ticket
+    counters, the error word and the finished-workgroup count), then one
+    status word per workgroup."""
+    return 256 + prefill_grid(nb, nt, nh, chunk)
 
 
 def gpu_prefill(inp, chunk, dev_inp=None, calls=1):

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.m3_version() == 140
+    assert lib.m3_version() == 150
     for code in range(6):
         s = m3.status_string(code)
         assert s.startswith("M3_")
@@ -70,8 +70,9 @@ def ws(d, chunk=32, dtype=m3.M3_F32):
 
 
 def test_workspace_size(lib):
-    """The chain counters (four words, then one status word per workgroup),
-    from 4 KiB or past the counters one slot per workgroup (two states, the
+    """The chain counters (256 words: the ticket counters, the error word,
+    the finished-workgroup count; then one status word per workgroup), from
+    8 KiB or past the counters one slot per workgroup (two states, the
     rotation per pair, the decay and three unused floats), then one
     continuation entry state per (batch, head) unit."""
     r256 = lambda v: (v + 255) // 256 * 256
@@ -81,17 +82,17 @@ def test_workspace_size(lib):
         nc = max(1, -(-nt // chunk))
         k = min(nc, max(1, -(-(nc * units) // 256)))
         grid = units * (-(-nc // k))
-        slots = max(4096, r256((4 + grid) * 4))
+        slots = max(8192, r256((256 + grid) * 4))
         return r256(slots + r256(grid * (2 * n * p + n + 4) * 4) + units * n * p * 4)
 
     d = dims(2, 100, 3, 16, 32, 2)     # 6 units, 4 chunks of 32: 24 segments
     assert ws(d, 32, m3.M3_F32) == expect(2, 100, 3, 16, 32, 32)
     assert ws(d, 32, m3.M3_BF16) == expect(2, 100, 3, 16, 32, 32)
-    # 4 KiB of counters, 24 slots of 1060 floats (101888 bytes), 6 entry states
-    assert expect(2, 100, 3, 16, 32, 32) == 4096 + 101888 + 6 * 512 * 4
-    d = dims(64, 100, 20, 16, 32, 1)   # 1280 units, one segment each: counters past 4 KiB
-    assert ws(d, 32, m3.M3_BF16) == expect(64, 100, 20, 16, 32, 32)
-    assert expect(64, 100, 20, 16, 32, 32) == r256(1284 * 4) + r256(1280 * 1060 * 4) + 1280 * 2048
+    # 8 KiB of counters, 24 slots of 1060 floats (101888 bytes), 6 entry states
+    assert expect(2, 100, 3, 16, 32, 32) == 8192 + 101888 + 6 * 512 * 4
+    d = dims(64, 100, 40, 16, 32, 1)   # 2560 units, one segment each: counters past 8 KiB
+    assert ws(d, 32, m3.M3_BF16) == expect(64, 100, 40, 16, 32, 32)
+    assert expect(64, 100, 40, 16, 32, 32) == r256(2816 * 4) + r256(2560 * 1060 * 4) + 2560 * 2048
     assert ws(dims(0, 100), 32) == 0
     assert ws(dims(1, 0), 32) == 0
 

@@ -193,9 +193,10 @@ def test_workspace_reused_across_shapes():
 
 
 def test_dirty_counters_reported():
-    """A workspace whose ticket word is not zero on entry makes every
-    workgroup skip its segment and raise the error word (2); the counters are
-    still returned to zero, so the next call (error word cleared) is correct."""
+    """A workspace whose class-0 ticket word is not zero on entry makes every
+    workgroup of that class skip its segment and raise the error word (2);
+    the counters are still returned to zero, so the next call (error word
+    cleared) is correct."""
     import torch
     import state_space_sequence_exp_amd as m3
     inp = I.prefill_inputs(1, 200, 2, 32, 64, 1, "bf16", seed=63)
