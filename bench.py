@@ -655,6 +655,41 @@ def counter_sequence():
 
 
 # ---------------------------------------------------------------------------
+# The goals set for these kernels: prefill at half the dense bf16 MFMA peak,
+# the decode step at 70% of the HBM peak.
+PREFILL_MFMA_GOAL = 0.5
+DECODE_HBM_GOAL = 0.7
+
+
+def goals_report(line):
+    """Each goal beside what was measured.  For prefill also the MFMA
+    fraction its useful flops would reach if the call ran at the HBM
+    roofline (its algorithmic bytes at 8 TB/s): the most the shape allows
+    while it stays bound by its bytes."""
+    from state_space_sequence_exp_amd import inputs as I
+
+    def ceiling(c):
+        t_s = prefill_bytes(c) / (HBM_PEAK_GBS * 1e9)
+        return prefill_flops(c) / t_s / 1e12 / BF16_PEAK_TFLOPS
+
+    pre = {"goal": PREFILL_MFMA_GOAL, "measured": {}, "ceiling_at_hbm_roofline": {}}
+    c1 = I.WORKLOADS[1]
+    pre["measured"][c1.name] = line["roofline"]["mfma_frac"]
+    pre["ceiling_at_hbm_roofline"][c1.name] = ceiling(c1)
+    sec = line.get("secondary", {})
+    for idx in (2, 3):
+        c = I.WORKLOADS[idx]
+        if c.name in sec:
+            pre["measured"][c.name] = sec[c.name]["mfma_frac"]
+            pre["ceiling_at_hbm_roofline"][c.name] = ceiling(c)
+    out = {"prefill_bf16_mfma_frac": pre}
+    c4 = I.WORKLOADS[4]
+    if c4.name in sec:
+        out["decode_hbm_frac"] = {"goal": DECODE_HBM_GOAL,
+                                  "measured": sec[c4.name]["roofline"]["frac"]}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -818,6 +853,7 @@ def main():
         if not args.no_backward:
             sec["backward_siso_b4_t2048_h16_n64_p64"] = backward_bench(10, log)
         line["secondary"] = sec
+    line["goals"] = goals_report(line)
     print(json.dumps(line))
 
 
