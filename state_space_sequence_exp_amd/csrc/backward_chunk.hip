@@ -127,40 +127,6 @@ constexpr size_t kLdsGrads = (size_t)(oScG + kScGrad) * 4;
 // local: its scalars, then 16 x 32 doubles of angle partial sums
 constexpr size_t kLdsLocal = (size_t)(oScL + kScLocal) * 4 + 16 * 32 * 8;
 
-__device__ __forceinline__ void load8(const bf16* p, float (&v)[8]) {
-  const uint4 w = *reinterpret_cast<const uint4*>(p);
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(ws[i] << 16);
-    v[2 * i + 1] = __uint_as_float(ws[i] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-// One 64 x 64 tile of rows (token t0 + row / R, rank row % R) of a [B, T, H,
-// R, 64] tensor into LDS as float (rows past the sequence: zeros).
-template <typename T, int R>
-__device__ __forceinline__ void load_tile(const void* src, float* tile, const BackwardArgs& a,
-                                          int b, int hh, int t0) {
-  const int tid = ltid(), row = tid >> 3, c0 = (tid & 7) * 8;
-  const int t = t0 + row / R, r = row % R;
-  float v[8];
-  if (t < a.T) {
-    const T* p = static_cast<const T*>(src) + ((((size_t)b * a.T + t) * a.H + hh) * R + r) * 64 + c0;
-    load8(p, v);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = 0.f;
-  }
-  *reinterpret_cast<float4*>(tile + tix(row, c0)) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4*>(tile + tix(row, c0 + 4)) = make_float4(v[4], v[5], v[6], v[7]);
-}
-
 // What both chunk kernels stage: the B, C, x, dy tiles, the per-token
 // scalars and the chunk's angles.  Thread (k = tid & 31, grp = tid >> 5)
 // owns pair k of tokens grp * TPG .. + TPG - 1 for the angle scans and keeps
@@ -170,30 +136,6 @@ struct ChunkGeo {
   static constexpr int L = 64 / R;     // tokens of a chunk
   static constexpr int TPG = L / 16;   // tokens per angle group
 };
-
-// Phase 1 of staging: global loads (tiles, dt / lam into LDS, theta into th).
-template <typename T, int R>
-__device__ __forceinline__ void stage_loads(const BackwardArgs& a, int b, int hh, int c,
-                                            float* sm, float* sc, float (&th)[4]) {
-  constexpr int L = ChunkGeo<R>::L, TPG = ChunkGeo<R>::TPG;
-  const int tid = ltid(), t0 = c * L;
-  load_tile<T, R>(a.C, sm + oC, a, b, hh, t0);
-  load_tile<T, R>(a.B, sm + oB, a, b, hh, t0);
-  load_tile<T, R>(a.x, sm + oX, a, b, hh, t0);
-  load_tile<T, R>(a.dy, sm + oDY, a, b, hh, t0);
-  if (tid <= L) {
-    const int t = t0 + tid;
-    const size_t tok = ((size_t)b * a.T + t) * a.H + hh;
-    sc[sDt + tid] = t < a.T ? a.dt[tok] : 0.f;
-    sc[sLam + tid] = t < a.T ? a.lam[tok] : 0.f;
-  }
-  const int k = tid & 31, grp = tid >> 5;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t0 + grp * TPG + j;
-    th[j] = (j < TPG && t < a.T) ? a.theta[(((size_t)b * a.T + t) * a.H + hh) * 32 + k] : 0.f;
-  }
-}
 
 // Phase 2 (after a barrier): each thread's angle partial sum, in double.
 template <int R>
@@ -359,54 +301,67 @@ __device__ __forceinline__ void chunk_commit(const ChunkIn<T>& in, float* sm, fl
 }
 
 // ---- local pass ---------------------------------------------------------------
-// One workgroup per (sequence, head, chunk): S_c into slot c + 1 of the
-// entry states, D_c into slot c of the adjoints, and the chunk's decay and
-// rotation.
+// Per (sequence, head, chunk): S_c into slot c + 1 of the entry states, D_c
+// into slot c of the adjoints, and the chunk's decay and rotation.  The
+// workgroups are persistent over the chunks (chunk ci, ci + gridDim.x, ...),
+// with the next chunk's inputs requested into registers as soon as the
+// current chunk's are in the LDS, so their latency hides behind this
+// chunk's work.  Registers are held to 128 a lane so that two workgroups
+// share a CU (the LDS holds two): 266.5 against 275.7 us for the whole
+// backward at the SISO bench shape with one workgroup per CU, and 277.4 us
+// before, with one workgroup per chunk.
 template <typename T, int R>
-__global__ void __launch_bounds__(kBT) bwc_local_kernel(BackwardArgs a, int nC) {
+__global__ void __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(4)))
+bwc_local_kernel(BackwardArgs a, int nC) {
   extern __shared__ __align__(16) float sm[];
   float* sc = sm + oScL;
   float* rev = sm + oRevL;
   double* part = reinterpret_cast<double*>(sm + oScL + kScLocal);
-  const int unit = blockIdx.x / nC, c = blockIdx.x - unit * nC;
-  const int b = unit / a.H, hh = unit - b * a.H;
-  float th[4];
-  stage_loads<T, R>(a, b, hh, c, sm, sc, th);
-  __syncthreads();
-  stage_angle_parts<R>(sc, th, part);
-  __syncthreads();
-  stage_angles_scalars<R>(a, hh, th, part, rev, sc);
-  __syncthreads();
-  stage_rotate<R>(sm, rev);
-  __syncthreads();
+  const int nchunk = a.nb * a.H * nC;
+  ChunkIn<T> in;
+  chunk_fetch<T, R>(a, blockIdx.x, nC, in);
+  for (int ci = blockIdx.x; ci < nchunk; ci += gridDim.x) {
+    const int unit = ci / nC, c = ci - unit * nC;
+    float th[4];
+    __syncthreads();  // every read of the previous chunk's LDS is done
+    chunk_commit<T, R>(in, sm, sc, th);
+    if (ci + (int)gridDim.x < nchunk) chunk_fetch<T, R>(a, ci + gridDim.x, nC, in);
+    __syncthreads();
+    stage_angle_parts<R>(sc, th, part);
+    __syncthreads();
+    stage_angles_scalars<R>(a, unit % a.H, th, part, rev, sc);
+    __syncthreads();
+    stage_rotate<R>(sm, rev);
+    __syncthreads();
 
-  const int tl = ltid(), lane = tl & 63, w = tl >> 6, i = lane & 15, g = lane >> 4;
-  const int m0 = (w >> 1) * 16;
-  constexpr int NP = 64 * 64;
-  float* Sout = a.hs + ((size_t)unit * (nC + 1) + c + 1) * NP;
-  float* Dout = a.gs + ((size_t)unit * nC + c) * NP;
+    const int tl = ltid(), lane = tl & 63, w = tl >> 6, i = lane & 15, g = lane >> 4;
+    const int m0 = (w >> 1) * 16;
+    constexpr int NP = 64 * 64;
+    float* Sout = a.hs + ((size_t)unit * (nC + 1) + c + 1) * NP;
+    float* Dout = a.gs + ((size_t)unit * nC + c) * NP;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int n0 = (2 * (w & 1) + q) * 16;
-    f32x4 s = {0.f, 0.f, 0.f, 0.f}, d = {0.f, 0.f, 0.f, 0.f};
-    mma_pipe2(s, d, 0, 64, [&](int k, float& a0, float& b0, float& a1, float& b1) {
-      const int kr = k + g, tk = kr / R;
-      a0 = sm[oB + tix(kr, m0 + i)];
-      b0 = sc[sV + tk] * sm[oX + tix(kr, n0 + i)];
-      a1 = sm[oC + tix(kr, m0 + i)];
-      b1 = sc[sEcs + tk] * sm[oDY + tix(kr, n0 + i)];
-    });
+    for (int q = 0; q < 2; ++q) {
+      const int n0 = (2 * (w & 1) + q) * 16;
+      f32x4 s = {0.f, 0.f, 0.f, 0.f}, d = {0.f, 0.f, 0.f, 0.f};
+      mma_pipe2(s, d, 0, 64, [&](int k, float& a0, float& b0, float& a1, float& b1) {
+        const int kr = k + g, tk = kr / R;
+        a0 = sm[oB + tix(kr, m0 + i)];
+        b0 = sc[sV + tk] * sm[oX + tix(kr, n0 + i)];
+        a1 = sm[oC + tix(kr, m0 + i)];
+        b1 = sc[sEcs + tk] * sm[oDY + tix(kr, n0 + i)];
+      });
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = m0 + 4 * g + j;
-      Sout[n * 64 + n0 + i] = s[j];
-      Dout[n * 64 + n0 + i] = d[j];
+      for (int j = 0; j < 4; ++j) {
+        const int n = m0 + 4 * g + j;
+        Sout[n * 64 + n0 + i] = s[j];
+        Dout[n * 64 + n0 + i] = d[j];
+      }
     }
+    constexpr int L = ChunkGeo<R>::L;
+    float* cs_out = a.dseg + ((size_t)unit * nC + c) * 65;
+    if (threadIdx.x < 64) cs_out[threadIdx.x] = sc[sExitCS + threadIdx.x];
+    if (threadIdx.x == 64) cs_out[64] = sc[sEcs + L - 1];
   }
-  constexpr int L = ChunkGeo<R>::L;
-  float* cs_out = a.dseg + ((size_t)unit * nC + c) * 65;
-  if (threadIdx.x < 64) cs_out[threadIdx.x] = sc[sExitCS + threadIdx.x];
-  if (threadIdx.x == 64) cs_out[64] = sc[sEcs + L - 1];
 }
 
 // ---- chain ----------------------------------------------------------------------
@@ -918,16 +873,23 @@ hipError_t launch_r(const BackwardArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   e = lds_limit(reinterpret_cast<const void*>(&bwc_grads_kernel<T, R>), kLdsGrads);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwc_local_kernel<T, R>), dim3(units * nC), dim3(kBT), kLdsLocal, stream, a, nC);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwc_chain_kernel, dim3(units, 2, 8), dim3(256), 0, stream, a, nC);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // one workgroup per CU (the LDS holds one), each over several chunks
-  int dev = 0, cus = 0;
+  int dev = 0, cus = 0, per_cu = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
     return e;
   const unsigned nchunk = units * nC;
+  // the local pass: as many persistent workgroups as are resident at once
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+           &per_cu, reinterpret_cast<const void*>(&bwc_local_kernel<T, R>), kBT, kLdsLocal)) !=
+      hipSuccess)
+    return e;
+  const unsigned nlocal = (unsigned)cus * (unsigned)(per_cu > 0 ? per_cu : 1);
+  hipLaunchKernelGGL((bwc_local_kernel<T, R>), dim3(nchunk < nlocal ? nchunk : nlocal), dim3(kBT),
+                     kLdsLocal, stream, a, nC);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwc_chain_kernel, dim3(units, 2, 8), dim3(256), 0, stream, a, nC);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // one workgroup per CU (the LDS holds one), each over several chunks
   const unsigned ngrid = nchunk < (unsigned)cus ? nchunk : (unsigned)cus;
   hipLaunchKernelGGL((bwc_grads_kernel<T, R>), dim3(ngrid), dim3(kBT), kLdsGrads, stream, a, nC);
   if ((e = hipGetLastError()) != hipSuccess) return e;
