@@ -81,6 +81,13 @@ SMALL = [
     ("bf16", 1, 130, 2, 192, 32, 1, 32),
     ("bf16", 1, 90, 1, 160, 16, 4, 16),
     ("bf16", 2, 100, 1, 224, 16, 2, 16),
+    # workgroups draw tickets from one counter per class, the classes the
+    # largest power of two up to 8 dividing batch * heads: 8 (both kernels),
+    # 4 and 1, every sequence cut into several one-chunk segments
+    ("bf16", 2, 300, 4, 64, 64, 1, 64),
+    ("f32", 2, 200, 4, 32, 32, 1, 32),
+    ("bf16", 3, 250, 4, 64, 64, 1, 64),
+    ("bf16", 1, 300, 5, 128, 64, 1, 64),
 ]
 
 
