@@ -157,8 +157,19 @@ __device__ __forceinline__ void stage_angles_scalars(const BackwardArgs& a, int 
                                                      const double* part, float* rev, float* sc) {
   constexpr int L = ChunkGeo<R>::L, TPG = ChunkGeo<R>::TPG;
   const int tid = ltid(), k = tid & 31, grp = tid >> 5;
+  // the sums of the groups before this one, in order, requested five at a
+  // time (one at a time, the later groups waited out fifteen LDS round trips)
+  constexpr int NG = kBT / 32;
   double phi = 0.0;
-  for (int g2 = 0; g2 < grp; ++g2) phi += part[g2 * 32 + k];
+#pragma unroll
+  for (int g0 = 0; g0 < NG - 1; g0 += 5) {
+    double v[5];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) v[q] = g0 + q < NG - 1 ? part[(g0 + q) * 32 + k] : 0.0;
+#pragma unroll
+    for (int q = 0; q < 5; ++q)
+      if (g0 + q < NG - 1 && g0 + q < grp) phi += v[q];
+  }
 #pragma unroll
   for (int j = 0; j < TPG; ++j) {
     const int t = grp * TPG + j;
@@ -177,12 +188,8 @@ __device__ __forceinline__ void stage_angles_scalars(const BackwardArgs& a, int 
     const int t = tid;
     const float Ah = a.A[hh];
     const float d = t < L ? sc[sDt + t] : 0.f;
-    float v = Ah * d;
-    for (int o = 1; o < 64; o <<= 1) {
-      const float n = __shfl_up(v, o);
-      if (t >= o) v += n;
-    }
-    const float cs = v, csl = __shfl(v, L - 1);
+    // inclusive scan over the wave (DPP; the whole of wave 0 runs this)
+    const float cs = wave_incl_scan(Ah * d), csl = wave_read_lane(cs, L - 1);
     if (t < L) {
       const float gam = sc[sLam + t] * d;
       const float om = (1.f - sc[sLam + t + 1]) * sc[sDt + t + 1];
