@@ -88,7 +88,7 @@ typedef struct {
   int64_t rank_r;    /* R: 1, 2 or 4 (MIMO rank) */
 } m3_dims;
 
-/* Library version (M3SSM_VERSION of the build). */
+/* Library version (M3SSM_VERSION of the compiled library). */
 int m3_version(void);
 
 /* Static, NUL-terminated description of a status code. */
