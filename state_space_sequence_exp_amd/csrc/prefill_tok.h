@@ -104,6 +104,36 @@ struct TCfg {
   static constexpr bool kFits = kTotal <= kLdsLimit && NTILES % kW == 0 && TPW >= 1 &&
                                 TPW <= kMaxStTiles && NPW >= 1 && PPG >= 1 &&
                                 (kRowN == 128 || kRowN == 256) && (kRowP == 128 || kRowP == 256);
+  // The single pass (tok1_segment, segments of at most kK1 chunks): a ring
+  // of three staging buffers (B, then B~; x; theta; dt and lam of the
+  // chunk's tokens and the token after it), two buffers of computed values
+  // (the entry state [P][N] the outputs see; gamma, gamma + omega and the
+  // state weight per token), and per chunk of the segment, kept to its end:
+  // C (then C~), the log-decay prefix cs and the chunk's angle per pair.
+  // The correction's entry-state tiles reuse the ring.
+  static constexpr int kK1 = 8;
+  static constexpr uint32_t o1B = 0;
+  static constexpr uint32_t o1X = o1B + LR * kRowN;
+  static constexpr uint32_t o1Th = o1X + LR * kRowP;
+  static constexpr uint32_t o1Raw = o1Th + kL * kRowTh;
+  static constexpr uint32_t k1Sc = (kL + 4) * 4;  // 65 floats, padded
+  static constexpr uint32_t k1Ring = o1Raw + 2 * k1Sc;
+  static constexpr uint32_t o1Dbl = 3 * k1Ring;
+  static constexpr uint32_t o1G = 0;
+  static constexpr uint32_t o1Gs = o1G + P_ * kRowN;
+  static constexpr uint32_t k1Dbl = o1Gs + 3 * kL * 4;
+  static constexpr uint32_t o1Per = o1Dbl + 2 * k1Dbl;
+  static constexpr uint32_t o1C = 0;
+  static constexpr uint32_t o1Cs = o1C + LR * kRowN;
+  static constexpr uint32_t o1Ang = o1Cs + kL * 4;
+  static constexpr uint32_t k1Per = o1Ang + (N_ / 2) * 4;
+  static constexpr uint32_t o1Misc = o1Per + kK1 * k1Per;
+  static constexpr uint32_t o1Srot = o1Misc + 64;
+  static constexpr uint32_t k1Total = o1Misc + kMisc;
+  // one output unit per wave (its partial outputs stay in its registers),
+  // rank 1, and the correction's kK1 entry-state tiles fit the ring
+  static constexpr bool k1Fits = kFits && k1Total <= kLdsLimit && NOUT == kW && R_ == 1 &&
+                                 kK1 * P_ * kRowN <= 3 * k1Ring;
 };
 
 // Whether the layout fits (the ring in the LDS, whole state tiles per wave).
@@ -204,9 +234,15 @@ __device__ __forceinline__ void lds_block(u32x4v r, unsigned char* tile, uint32_
 // robin, and (the last wave) dt and lam of tokens u and u + 1.  Returns nothing to
 // wait for here: the caller waits (vmcnt) before the barrier that publishes
 // the buffer.
-template <class C, bool kWithC>
+// Where one chunk's staged inputs land: the B, C, x and theta tiles and the
+// raw dt / lam words (each may lie in a different LDS area).
+struct TDst {
+  unsigned char *B, *C, *X, *Th, *raw;
+};
+
+template <class C, bool kWithC, bool kCompact = false>
 __device__ __forceinline__ void tok_issue(const PrefillArgs& a, const TCtx& s, int c,
-                                          unsigned char* buf) {
+                                          const TDst& d) {
   constexpr int R = C::R, N = C::N, P = C::P;
   const uint32_t w = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int t0 = c * kL;
@@ -229,17 +265,17 @@ __device__ __forceinline__ void tok_issue(const PrefillArgs& a, const TCtx& s, i
   constexpr uint32_t kBlkX = C::LR * C::kRowP / 1024, kRowsX = 1024 / C::kRowP;
   constexpr uint32_t kBlkT = kL * C::kRowTh / 1024, kRowsT = 1024 / C::kRowTh;
   for (uint32_t j = w; j < kBlkN; j += kW)
-    lds_block<C::kRowN>(rB, buf + C::oB, j * kRowsN, gB);
+    lds_block<C::kRowN>(rB, d.B, j * kRowsN, gB);
   if constexpr (kWithC) {
     const u32x4v rC =
         rsrc_words(static_cast<const unsigned char*>(a.C) + hrow * bcb, last * s.rowB + bcb);
     for (uint32_t j = w; j < kBlkN; j += kW)
-      lds_block<C::kRowN>(rC, buf + C::oC, j * kRowsN, gB);
+      lds_block<C::kRowN>(rC, d.C, j * kRowsN, gB);
   }
   for (uint32_t j = w; j < kBlkX; j += kW)
-    lds_block<C::kRowP>(rX, buf + C::oX, j * kRowsX, gX);
+    lds_block<C::kRowP>(rX, d.X, j * kRowsX, gX);
   for (uint32_t j = w; j < kBlkT; j += kW)
-    lds_block<C::kRowTh>(rTh, buf + C::oTh, j * kRowsT, gT);
+    lds_block<C::kRowTh>(rTh, d.Th, j * kRowsT, gT);
   if (w == kW - 1) {
     // dt and lam of token u, and of token u + 1 (its omega needs the token
     // after the chunk), up to the sequence's end
@@ -247,13 +283,25 @@ __device__ __forceinline__ void tok_issue(const PrefillArgs& a, const TCtx& s, i
     const int nsc = min(kL + 1, a.T - t0);
     const uint32_t scb = (uint32_t)(nsc - 1) * s.rowDt + 4;
     const u32x4v rD = rsrc_words(a.dt + hrow, scb);
-    const uint32_t raw = lds_addr(buf + C::oRaw);
-    dma_lds<4>(rD, raw, u * s.rowDt);
-    dma_lds<4>(rD, raw + 256, (u + 1) * s.rowDt);
-    if (a.lam) {
-      const u32x4v rL = rsrc_words(a.lam + hrow, scb);
-      dma_lds<4>(rL, raw + 512, u * s.rowDt);
-      dma_lds<4>(rL, raw + 768, (u + 1) * s.rowDt);
+    const uint32_t raw = lds_addr(d.raw);
+    if constexpr (kCompact) {
+      // tokens 0..63, then token 64 by lane 0 alone (its word lands at
+      // float 64): 65 floats of dt, then of lam at float 68
+      dma_lds<4>(rD, raw, u * s.rowDt);
+      if (u == 0) dma_lds<4>(rD, raw + 256, 64 * s.rowDt);
+      if (a.lam) {
+        const u32x4v rL = rsrc_words(a.lam + hrow, scb);
+        dma_lds<4>(rL, raw + C::k1Sc, u * s.rowDt);
+        if (u == 0) dma_lds<4>(rL, raw + C::k1Sc + 256, 64 * s.rowDt);
+      }
+    } else {
+      dma_lds<4>(rD, raw, u * s.rowDt);
+      dma_lds<4>(rD, raw + 256, (u + 1) * s.rowDt);
+      if (a.lam) {
+        const u32x4v rL = rsrc_words(a.lam + hrow, scb);
+        dma_lds<4>(rL, raw + 512, u * s.rowDt);
+        dma_lds<4>(rL, raw + 768, (u + 1) * s.rowDt);
+      }
     }
   }
 }
@@ -265,6 +313,10 @@ struct TBuf {
   float* raw;    // dt, dt of the next token, lam, lam of the next token (64 each)
   float* sc;     // cs, gamma, gamma + omega (stride kLMax)
   float2* rot;   // (cos, sin) of the chunk's total angle per pair
+  // the single pass: raw holds 65 floats of dt, then of lam (stride k1Sc);
+  // cs (64 floats), gamma, gamma + omega and the state weight (stride 64),
+  // the chunk's angle per pair in revolutions
+  float *cs, *gs, *ang;
 };
 
 template <class C>
@@ -307,14 +359,20 @@ __device__ __forceinline__ void ld_tile(const Tile& t, uint32_t row, uint32_t by
 // per pair.  Returns the
 // chunk's log-decay cs_e; the lanes below NPW add their pair's chunk angle
 // (revolutions, reduced) to sang.
-template <class C, bool kOut>
+// kSplit (the single pass, with kOut): the raw words are 65 floats of dt and
+// of lam; the scalars go to t.cs and t.gs (with the state weight, which the
+// state update applies to its operand instead of a weighted B~ tile) and
+// the chunk's angle to t.ang.
+template <class C, bool kOut, bool kSplit = false>
 __device__ __forceinline__ float tok_rotate(const TBuf& t, bool has_lam, float Ah,
                                             double& sang) {
   constexpr int R = C::R, NPW = C::NPW;
+  static_assert(!kSplit || kOut, "the single pass rotates B and C");
   const uint32_t u = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const float d = t.raw[u], dn = t.raw[64 + u];
+  constexpr uint32_t kLam = kSplit ? C::k1Sc / 4 : 128, kNext = kSplit ? 1 : 64;
+  const float d = t.raw[u], dn = t.raw[kNext + u];
   // without lam the weight is 1 (the exponential-Euler rule)
-  const float l = has_lam ? t.raw[128 + u] : 1.f, ln = has_lam ? t.raw[192 + u] : 1.f;
+  const float l = has_lam ? t.raw[kLam + u] : 1.f, ln = has_lam ? t.raw[kLam + kNext + u] : 1.f;
   uint32_t th[NPW];
   ld_tile<NPW * 4>(t.Th, u, w * (NPW * 4), th);
   // per-token scalars (exponential-trapezoidal weights; every wave has them)
@@ -323,7 +381,14 @@ __device__ __forceinline__ float tok_rotate(const TBuf& t, bool has_lam, float A
   const float ga = l * d;
   const float gom = ga + (1.f - ln) * dn;
   const float wgt = __expf(cse - cs) * gom;
-  if (kOut && w == 0) {
+  if constexpr (kSplit) {
+    if (w == 0) {
+      t.cs[u] = cs;
+      t.gs[u] = ga;
+      t.gs[kL + u] = gom;
+      t.gs[2 * kL + u] = wgt;
+    }
+  } else if (kOut && w == 0) {
     t.sc[u] = cs;
     t.sc[kLMax + u] = ga;
     t.sc[2 * kLMax + u] = gom;
@@ -375,7 +440,7 @@ __device__ __forceinline__ float tok_rotate(const TBuf& t, bool has_lam, float A
       const bf16x2 bp = __builtin_bit_cast(bf16x2, bv[k]);
       const float rb0 = __builtin_amdgcn_fdot2_f32_bf16(bp, rcs[k], 0.f, false);
       const float rb1 = __builtin_amdgcn_fdot2_f32_bf16(bp, rncs[k], 0.f, false);
-      bw[k] = pack_bf16(wgt * rb0, wgt * rb1);
+      if constexpr (!kSplit) bw[k] = pack_bf16(wgt * rb0, wgt * rb1);
       if constexpr (kOut) {
         bt[k] = pack_bf16(rb0, rb1);
         const bf16x2 cp = __builtin_bit_cast(bf16x2, cv[k]);
@@ -384,7 +449,7 @@ __device__ __forceinline__ float tok_rotate(const TBuf& t, bool has_lam, float A
       }
     }
     // B~ and C~ in place (for the scores), the weighted B~ into its tile
-    st_bytes<NPW * 4>(t.W, row, w * (NPW * 4), bw);
+    if constexpr (!kSplit) st_bytes<NPW * 4>(t.W, row, w * (NPW * 4), bw);
     if constexpr (kOut) {
       st_bytes<NPW * 4>(t.B, row, w * (NPW * 4), bt);
       st_bytes<NPW * 4>(t.C, row, w * (NPW * 4), ct);
@@ -395,7 +460,10 @@ __device__ __forceinline__ float tok_rotate(const TBuf& t, bool has_lam, float A
   // in double
   if (u < (uint32_t)NPW) {
     const float f = mine - __builtin_rintf(mine);
-    t.rot[w * NPW + u] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+    if constexpr (kSplit)
+      t.ang[w * NPW + u] = f;
+    else
+      t.rot[w * NPW + u] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
     sang += static_cast<double>(f);
     sang -= __builtin_rint(sang);
   }
@@ -447,7 +515,10 @@ __device__ __forceinline__ bf16x8 frag_tr(const Tile& t, uint32_t r0, uint32_t r
 // Chunk state of this wave's tiles, S = sum over rows of Bw^T X (A from the
 // weighted B~ tile, B from the x tile, both through transpose reads), folded
 // in: stt <- R(Phi_c)(d stt + S).
-template <class C>
+// kSplit (the single pass): the A operand is B~ with each token's slot
+// scaled by its state weight (t.gs), and the rotation comes from the
+// chunk's angles (t.ang).
+template <class C, bool kSplit = false>
 __device__ __forceinline__ void tok_state_update(const TBuf& t, float d,
                                                  f32x4 (&stt)[kMaxStTiles]) {
   using M = typename C::M;
@@ -462,7 +533,18 @@ __device__ __forceinline__ void tok_state_update(const TBuf& t, float d,
 #pragma unroll
   for (int k0 = 0; k0 < C::LR; k0 += M::K) {
     const uint32_t r0 = (uint32_t)(k0 + 8 * g);
-    const bf16x8 fa = frag_tr(t.W, r0, r0 + 4, nt);
+    bf16x8 fa;
+    if constexpr (kSplit) {
+      // slots 0..7 are tokens r0 .. r0 + 7
+      fa = frag_tr(t.B, r0, r0 + 4, nt);
+      const float4 w0 = *reinterpret_cast<const float4*>(t.gs + 2 * kL + r0);
+      const float4 w1 = *reinterpret_cast<const float4*>(t.gs + 2 * kL + r0 + 4);
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fa[j] = from_f32<bf16>(to_f32(fa[j]) * wv[j]);
+    } else {
+      fa = frag_tr(t.W, r0, r0 + 4, nt);
+    }
 #pragma unroll
     for (int m = 0; m < C::TPW; ++m) {
       const int pt = (wave + kW * m) / C::NNT;
@@ -470,7 +552,15 @@ __device__ __forceinline__ void tok_state_update(const TBuf& t, float d,
     }
   }
   // rows 4g .. 4g + 3 of n-tile nt: pairs 8 nt + 2g and 8 nt + 2g + 1
-  const float2 q0 = t.rot[nt * 8 + 2 * g], q1 = t.rot[nt * 8 + 2 * g + 1];
+  float2 q0, q1;
+  if constexpr (kSplit) {
+    const float2 f = *reinterpret_cast<const float2*>(t.ang + nt * 8 + 2 * g);
+    q0 = make_float2(__builtin_amdgcn_cosf(f.x), __builtin_amdgcn_sinf(f.x));
+    q1 = make_float2(__builtin_amdgcn_cosf(f.y), __builtin_amdgcn_sinf(f.y));
+  } else {
+    q0 = t.rot[nt * 8 + 2 * g];
+    q1 = t.rot[nt * 8 + 2 * g + 1];
+  }
 #pragma unroll
   for (int m = 0; m < C::TPW; ++m) {
     const float v0 = d * stt[m][0] + acc[m][0], v1 = d * stt[m][1] + acc[m][1];
@@ -482,40 +572,52 @@ __device__ __forceinline__ void tok_state_update(const TBuf& t, float d,
   }
 }
 
-// One output unit, computed transposed: y^T rows p (PPG p-tiles from p_lo)
-// by the 16 query rows of block qb.
-//   y_t = exp(cs_t) C~_t^T G + sum_u W[t,u] (C~_t^T B~_u) x_u^T
-// with W the chunk's decay x 2-band trapezoid mask (Mamba-3 paper
-// translation, section 3.1, equation 7): the inter-chunk term is G^T C~^T,
-// the scores S^T = B~ C~^T (keys x queries) are masked in registers, and
-// their accumulator layout is the B operand of the product with x^T.
+// Inter-chunk term of one output unit, computed transposed (y^T rows p:
+// PPG p-tiles from p_lo, by the query row of this lane's column):
+// acc += exp(cs_q) G^T C~_q, G the state a chunk's outputs see (as a [P][N]
+// tile) and C~ the chunk's rotated C.
 template <class C>
-__device__ __forceinline__ void tok_output_unit(const TBuf& t, const rsrc& ry, uint32_t rowX,
-                                                int qb, int p_lo) {
+__device__ __forceinline__ void tok_inter(const Tile& G, const Tile& Cq, uint32_t qrow, int p_lo,
+                                          float eq, f32x4 (&acc)[C::PPG]) {
   using M = typename C::M;
-  constexpr int R = C::R, P = C::P, N = C::N, PPG = C::PPG;
+  constexpr int N = C::N, PPG = C::PPG;
+  const int li = threadIdx.x & 15;
+  f32x4 t[PPG];
+#pragma unroll
+  for (int pp = 0; pp < PPG; ++pp) t[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int n0 = 0; n0 < N; n0 += M::K) {
+    const bf16x8 fq = frag_row(Cq, qrow, n0);
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp)
+      t[pp] = M::mma(frag_row(G, (uint32_t)((p_lo + pp) * 16 + li), n0), fq, t[pp]);
+  }
+#pragma unroll
+  for (int pp = 0; pp < PPG; ++pp)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[pp][j] = __builtin_fmaf(t[pp][j], eq, acc[pp][j]);
+}
+
+// Intra-chunk term of one output unit (query block qb, PPG p-tiles from
+// p_lo), added to acc:
+//   y_t += sum_u W[t,u] (C~_t^T B~_u) x_u^T
+// with W the chunk's decay x 2-band trapezoid mask (Mamba-3 paper
+// translation, section 3.1, equation 7).  The scores S^T = B~ C~^T (keys x
+// queries) are masked in registers, and their accumulator layout is the B
+// operand of the product with x^T.
+// kSplit (the single pass, R = 1): cs from t.cs, gamma and gamma + omega
+// from t.gs.
+template <class C, bool kSplit = false>
+__device__ __forceinline__ void tok_intra(const TBuf& t, int qb, int p_lo, f32x4 (&acc)[C::PPG]) {
+  using M = typename C::M;
+  constexpr int R = C::R, N = C::N, PPG = C::PPG;
+  static_assert(!kSplit || R == 1, "the single pass is rank 1");
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, li = lane & 15;
   const uint32_t qrow = (uint32_t)(qb * 16 + li);
   const int tq = (qb * 16 + li) / R;
-  const float csq = t.sc[tq];
-  f32x4 acc[PPG];
-#pragma unroll
-  for (int pp = 0; pp < PPG; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // inter-chunk term, then every column (query) scaled by exp(cs_q)
-#pragma unroll
-  for (int n0 = 0; n0 < N; n0 += M::K) {
-    const bf16x8 fq = frag_row(t.C, qrow, n0);
-#pragma unroll
-    for (int pp = 0; pp < PPG; ++pp)
-      acc[pp] = M::mma(frag_row(t.G, (uint32_t)((p_lo + pp) * 16 + li), n0), fq, acc[pp]);
-  }
-  const float eq = __expf(csq);
-#pragma unroll
-  for (int pp = 0; pp < PPG; ++pp)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[pp][j] *= eq;
-  // intra-chunk term over pairs of 16-row key blocks up to the diagonal
+  const float csq = kSplit ? t.cs[tq] : t.sc[tq];
+  // over pairs of 16-row key blocks up to the diagonal
   for (int kb = 0; kb <= qb; kb += 2) {
     f32x4 sct[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -527,8 +629,19 @@ __device__ __forceinline__ void tok_output_unit(const TBuf& t, const rsrc& ry, u
     }
     float kcs[2][4], kga[2][4], kgom[2][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      pf::key_scalars4<R>(t.sc, (kb + i) * 16 + 4 * g, kcs[i], kga[i], kgom[i]);
+    for (int i = 0; i < 2; ++i) {
+      const int row0 = (kb + i) * 16 + 4 * g;
+      if constexpr (kSplit) {
+        const float4 c = *reinterpret_cast<const float4*>(t.cs + row0);
+        const float4 ga = *reinterpret_cast<const float4*>(t.gs + row0);
+        const float4 go = *reinterpret_cast<const float4*>(t.gs + kL + row0);
+        kcs[i][0] = c.x; kcs[i][1] = c.y; kcs[i][2] = c.z; kcs[i][3] = c.w;
+        kga[i][0] = ga.x; kga[i][1] = ga.y; kga[i][2] = ga.z; kga[i][3] = ga.w;
+        kgom[i][0] = go.x; kgom[i][1] = go.y; kgom[i][2] = go.z; kgom[i][3] = go.w;
+      } else {
+        pf::key_scalars4<R>(t.sc, row0, kcs[i], kga[i], kgom[i]);
+      }
+    }
     pf::mask_scores<R, 2>(sct, kcs, kga, kgom, kb, g, tq, csq);
     bf16x8 fs;
 #pragma unroll
@@ -542,15 +655,40 @@ __device__ __forceinline__ void tok_output_unit(const TBuf& t, const rsrc& ry, u
 #pragma unroll
     for (int pp = 0; pp < PPG; ++pp) acc[pp] = M::mma(frag_tr(t.X, r0, r1, p_lo + pp), fs, acc[pp]);
   }
-  // lane (g, c): p = 16 (p_lo + pp) + 4g .. + 3 of query row qb * 16 + c
-  const uint32_t q = qrow;
+}
+
+// y of one output unit from its accumulators: lane (g, c) holds p = 16
+// (p_lo + pp) + 4g .. + 3 of query row qb * 16 + c, stored as one 8-byte
+// vector per p-tile (lanes past the sequence's end are dropped by the range).
+template <class C>
+__device__ __forceinline__ void tok_unit_store(const rsrc& ry, uint32_t rowX, int qb, int p_lo,
+                                               const f32x4 (&acc)[C::PPG]) {
+  constexpr int R = C::R, P = C::P;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const uint32_t q = (uint32_t)(qb * 16 + li);
   const uint32_t ob = (q / R) * rowX + (q % R) * (P * 2);
 #pragma unroll
-  for (int pp = 0; pp < PPG; ++pp) {
+  for (int pp = 0; pp < C::PPG; ++pp) {
     const uint32_t o = ob + (uint32_t)(((p_lo + pp) * 16 + 4 * g) * 2);
     const u32x2 v = {pack_bf16(acc[pp][0], acc[pp][1]), pack_bf16(acc[pp][2], acc[pp][3])};
     __builtin_amdgcn_raw_buffer_store_b64(v, ry, (int)o, 0, 0);
   }
+}
+
+// One output unit: y_t = exp(cs_t) C~_t^T G + the intra-chunk term.
+template <class C>
+__device__ __forceinline__ void tok_output_unit(const TBuf& t, const rsrc& ry, uint32_t rowX,
+                                                int qb, int p_lo) {
+  constexpr int R = C::R, PPG = C::PPG;
+  const int li = threadIdx.x & 15;
+  const uint32_t qrow = (uint32_t)(qb * 16 + li);
+  f32x4 acc[PPG];
+#pragma unroll
+  for (int pp = 0; pp < PPG; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+  tok_inter<C>(t.G, t.C, qrow, p_lo, __expf(t.sc[(qb * 16 + li) / R]), acc);
+  tok_intra<C>(t, qb, p_lo, acc);
+  tok_unit_store<C>(ry, rowX, qb, p_lo, acc);
 }
 
 // y of one chunk: units (query block, p-group) dealt to the waves w, 2kW-1-w,
@@ -605,10 +743,11 @@ __device__ __forceinline__ void tok_segment(const PrefillArgs& a, int ticket,
   auto issue = [&](int i) {
     if (i >= nitem) return;
     unsigned char* buf = smem + (uint32_t)(i % NB) * C::kBuf;
+    const TDst d = {buf + C::oB, buf + C::oC, buf + C::oX, buf + C::oTh, buf + C::oRaw};
     if (i < K)
-      tok_issue<C, false>(a, s, s.c0 + i, buf);
+      tok_issue<C, false>(a, s, s.c0 + i, d);
     else
-      tok_issue<C, true>(a, s, s.c0 + i - K, buf);
+      tok_issue<C, true>(a, s, s.c0 + i - K, d);
   };
 
   f32x4 stt[kMaxStTiles];
@@ -693,6 +832,232 @@ hipError_t launch_tok(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---- single pass -----------------------------------------------------------
+// A segment of K <= kK1 chunks in one walk over its inputs.  Each step
+// stages, rotates and multiplies one chunk as the output pass does, but
+// from the segment's zero-entry state G_c (the local pass's state): its
+// outputs are complete except for the entry state's share, and the same
+// step advances G_c.  Rotated C~, the per-token scalars and the chunk's
+// rotation stay in the LDS and the partial outputs in the wave's registers
+// until the chain has given the true entry state h_in.  Since the state is
+// linear in its entry, a chunk's true state is G_c + E_c with E_0 = h_in
+// and E_{c+1} = R(Phi_c) exp(l_c) E_c, so the correction is
+//   y_t += exp(cs_t) C~_t^T E_c,
+// one 64 x 64 x 64 product per chunk: no input is read twice and no token
+// rotated twice.  A sequence's first segment (entry zero) writes y as it
+// goes and has no correction.
+template <class C>
+__device__ __forceinline__ void tok1_correct_state(f32x4 (&e)[kMaxStTiles], const float* ang,
+                                                   float d) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int nt = wave % C::NNT;
+  const float2 f = *reinterpret_cast<const float2*>(ang + nt * 8 + 2 * g);
+  const float2 q0 = make_float2(__builtin_amdgcn_cosf(f.x), __builtin_amdgcn_sinf(f.x));
+  const float2 q1 = make_float2(__builtin_amdgcn_cosf(f.y), __builtin_amdgcn_sinf(f.y));
+#pragma unroll
+  for (int m = 0; m < C::TPW; ++m) {
+    const float v0 = d * e[m][0], v1 = d * e[m][1];
+    const float v2 = d * e[m][2], v3 = d * e[m][3];
+    e[m][0] = q0.x * v0 - q0.y * v1;
+    e[m][1] = q0.y * v0 + q0.x * v1;
+    e[m][2] = q1.x * v2 - q1.y * v3;
+    e[m][3] = q1.y * v2 + q1.x * v3;
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
+                                             unsigned char* smem) {
+  constexpr int KK = C::kK1, PPG = C::PPG;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15;
+  const int BH = a.nb * a.H;
+  TCtx s;
+  s.seg = ticket / BH;
+  s.bh = ticket % BH;
+  s.b = s.bh / a.H;
+  s.h = s.bh % a.H;
+  s.c0 = s.seg * a.K;
+  s.c1 = min(a.nC, s.c0 + a.K);
+  s.rowB = (uint32_t)(a.H * C::R * C::N * 2);
+  s.rowTh = (uint32_t)(a.H * (C::N / 2) * 4);
+  s.rowDt = (uint32_t)(a.H * 4);
+  s.rowX = (uint32_t)(a.H * C::R * C::P * 2);
+  s.Ah = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.A[s.h])));
+  const bool has_lam = a.lam != nullptr;
+  // the sequence's first segment starts from zero: its outputs are final
+  const bool direct = s.seg == 0 && !a.cont;
+  int* s_misc = reinterpret_cast<int*>(smem + C::o1Misc);
+  float2* s_srot = reinterpret_cast<float2*>(smem + C::o1Srot);
+  const int K = s.c1 - s.c0;  // 1 .. KK
+  // this wave's output unit: query block qb, p-tiles p_lo .. p_lo + PPG - 1
+  const int qb = wave / C::NPG, p_lo = (wave % C::NPG) * PPG;
+  const uint32_t qrow = (uint32_t)(qb * 16 + li);
+  const int tq = qb * 16 + li;
+
+  // (the offsets are made opaque so that per-lane addresses are formed in
+  // each step rather than kept live across the loop)
+  auto ring = [&](int i) { return smem + pf::opaque_u((uint32_t)(i % 3) * C::k1Ring); };
+  auto dbl = [&](int i) {
+    return smem + pf::opaque_u(C::o1Dbl + (uint32_t)(i & 1) * C::k1Dbl);
+  };
+  auto per = [&](int i) { return smem + pf::opaque_u(C::o1Per + (uint32_t)i * C::k1Per); };
+  auto issue = [&](int i) {
+    if (i >= K) return;
+    unsigned char* r = ring(i);
+    const TDst d = {r + C::o1B, per(i) + C::o1C, r + C::o1X, r + C::o1Th, r + C::o1Raw};
+    tok_issue<C, true, true>(a, s, s.c0 + i, d);
+  };
+  auto yrange = [&](int i) {
+    const int t0 = (s.c0 + i) * kL;
+    const int len = min(kL, a.T - t0);
+    const size_t hrow = ((size_t)s.b * a.T + t0) * a.H + s.h;
+    constexpr uint32_t yb = C::R * C::P * 2;
+    return make_rsrc(static_cast<unsigned char*>(a.y) + hrow * yb,
+                     (uint32_t)(len - 1) * s.rowX + yb);
+  };
+
+  f32x4 stt[kMaxStTiles];
+#pragma unroll
+  for (int q = 0; q < kMaxStTiles; ++q) stt[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // partial outputs and chunk decays of the segment's chunks, oldest first
+  // (a queue shifted each step, so every index is static)
+  f32x4 yp[KK][PPG];
+  float dec[KK];
+#pragma unroll
+  for (int c = 0; c < KK; ++c) {
+    dec[c] = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp) yp[c][pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  double sang = 0.0;  // lanes < NPW: the segment's angle of pair wave * NPW + lane
+  float seg_logdecay = 0.f;
+
+  issue(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  issue(1);
+  __syncthreads();
+
+  for (int i = 0; i < K; ++i) {
+    unsigned char* r = ring(i);
+    unsigned char* d2 = dbl(i);
+    unsigned char* pc = per(i);
+    TBuf t;
+    t.base = r;
+    t.B = tile_at(r + C::o1B, C::kRowN);
+    t.C = tile_at(pc + C::o1C, C::kRowN);
+    t.W = t.B;  // (no weighted tile in the single pass)
+    t.X = tile_at(r + C::o1X, C::kRowP);
+    t.Th = tile_at(r + C::o1Th, C::kRowTh);
+    t.G = tile_at(d2 + C::o1G, C::kRowN);
+    t.raw = reinterpret_cast<float*>(r + C::o1Raw);
+    t.sc = nullptr;
+    t.rot = nullptr;
+    t.cs = reinterpret_cast<float*>(pc + C::o1Cs);
+    t.gs = reinterpret_cast<float*>(d2 + C::o1Gs);
+    t.ang = reinterpret_cast<float*>(pc + C::o1Ang);
+    const float cse = tok_rotate<C, true, true>(t, has_lam, s.Ah, sang);
+    if (i > 0) tok_state_to_lds<C>(stt, t.G);
+    // the next chunk's loads (issued a step ago) have landed
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x4 acc[PPG];
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i > 0) tok_inter<C>(t.G, t.C, qrow, p_lo, __expf(t.cs[tq]), acc);
+    tok_intra<C, true>(t, qb, p_lo, acc);
+    if (direct) {
+      tok_unit_store<C>(yrange(i), s.rowX, qb, p_lo, acc);
+    } else {
+#pragma unroll
+      for (int c = 0; c + 1 < KK; ++c)
+#pragma unroll
+        for (int pp = 0; pp < PPG; ++pp) yp[c][pp] = yp[c + 1][pp];
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) yp[KK - 1][pp] = acc[pp];
+    }
+    const float d = __expf(cse);
+    tok_state_update<C, true>(t, d, stt);
+#pragma unroll
+    for (int c = 0; c + 1 < KK; ++c) dec[c] = dec[c + 1];
+    dec[KK - 1] = d;
+    // the ring buffer of chunk i + 2 was last read in the previous step's
+    // MFMA phase, which every wave finished before this step's barrier
+    issue(i + 2);
+    seg_logdecay += cse;
+  }
+  // chunk c's partial outputs and decay to index c
+  for (int j = K; j < KK; ++j) {
+#pragma unroll
+    for (int c = 0; c + 1 < KK; ++c) {
+      dec[c] = dec[c + 1];
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) yp[c][pp] = yp[c + 1][pp];
+    }
+  }
+
+  // ---- the chain (chain_phase): the true entry state ------------------------
+  if (lane < C::NPW) {
+    const float f = static_cast<float>(sang);
+    s_srot[wave * C::NPW + lane] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+  }
+  __syncthreads();  // s_srot; every MFMA read of the last step is done
+  const WaveRoles wr = {0, 0, 0, 0, kW};
+  f32x4 ent[kMaxStTiles];
+  pf::chain_phase<C>(a, wr, s.seg, s.bh, ticket, __expf(seg_logdecay), s_srot, s_misc, stt, ent);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (direct) return;
+
+  // ---- correction: y_t += exp(cs_t) C~_t^T E_c ------------------------------
+  // E_c as [P][N] bf16 tiles in the ring (free now: the chain's barriers
+  // follow the last step's reads)
+#pragma unroll
+  for (int c = 0; c < KK; ++c) {
+    if (c < K) {
+      tok_state_to_lds<C>(ent, tile_at(smem + (uint32_t)c * (C::P * C::kRowN), C::kRowN));
+      if (c + 1 < K)
+        tok1_correct_state<C>(ent, reinterpret_cast<const float*>(per(c) + C::o1Ang), dec[c]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < KK; ++c) {
+    if (c < K) {
+      unsigned char* pc = per(c);
+      const float* cs = reinterpret_cast<const float*>(pc + C::o1Cs);
+      tok_inter<C>(tile_at(smem + (uint32_t)c * (C::P * C::kRowN), C::kRowN),
+                   tile_at(pc + C::o1C, C::kRowN), qrow, p_lo, __expf(cs[tq]), yp[c]);
+      tok_unit_store<C>(yrange(c), s.rowX, qb, p_lo, yp[c]);
+    }
+  }
+}
+
+template <class C>
+__global__ void __launch_bounds__(kT) prefill_tok1_kernel(PrefillArgs a_in) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  PrefillArgs a = a_in;
+  a.N = C::N;
+  int* s_misc = reinterpret_cast<int*>(smem + C::o1Misc);
+  const int ticket = pf::take_ticket(a, s_misc);
+  if (ticket >= 0 && ticket < (int)gridDim.x)
+    tok1_segment<C>(a, ticket, smem);
+  else
+    pf::bad_ticket(a);
+  pf::finish_workgroup(a, s_misc);
+}
+
+template <class C>
+hipError_t launch_tok1(const PrefillArgs& a, hipStream_t stream) {
+  const hipError_t attr =
+      lds_limit(reinterpret_cast<const void*>(&prefill_tok1_kernel<C>), C::k1Total);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((prefill_tok1_kernel<C>), dim3(a.nb * a.H * a.nSeg), dim3(kT), C::k1Total,
+                     stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace pt
 }  // namespace m3
 
@@ -717,6 +1082,14 @@ hipError_t try_tok(const PrefillArgs& a, hipStream_t stream, bool* taken) {
 inline hipError_t tok_dispatch(const PrefillArgs& a, hipStream_t stream, bool* taken) {
   *taken = false;
   if (a.L != kL || a.R != 1 || a.N != 64 || a.P != 64) return hipSuccess;
+  // segments of up to kK1 chunks take the single pass, longer ones the two
+  // passes (the segment rule gives 8 chunks at the SISO bench shape)
+  using C1 = TCfg<1, 64, 64>;
+  static_assert(C1::k1Fits, "the single pass fits the LDS at N = P = 64");
+  if (a.K <= C1::kK1) {
+    *taken = true;
+    return launch_tok1<C1>(a, stream);
+  }
   return try_tok<1, 64, 64>(a, stream, taken);
 }
 

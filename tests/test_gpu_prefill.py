@@ -88,6 +88,14 @@ SMALL = [
     ("f32", 2, 200, 4, 32, 32, 1, 32),
     ("bf16", 3, 250, 4, 64, 64, 1, 64),
     ("bf16", 1, 300, 5, 128, 64, 1, 64),
+    # bfloat16, R = 1, N = P = 64, 64-token chunks: the single-pass kernel
+    # with segments of 5 chunks (the last chunk ragged), of 7, and of 4 over
+    # four groups of segments; and, past 8 chunks a segment, the two-pass
+    # token-lane kernel (32)
+    ("bf16", 4, 1263, 16, 64, 64, 1, 64),
+    ("bf16", 4, 1762, 16, 64, 64, 1, 64),
+    ("bf16", 2, 6370, 4, 64, 64, 1, 64),
+    ("bf16", 1, 8192, 64, 64, 64, 1, 64),
 ]
 
 
@@ -115,6 +123,16 @@ def test_slow_decay_exposes_inter_chunk_path(dtype):
     """A = -exp(U(-8,-5)): the state survives many chunks."""
     inp = I.prefill_inputs(1, 1000, 2, 64, 64, 2, dtype, seed=31, a_range=(-8.0, -5.0))
     check_prefill(inp, 64, label="slow-decay")
+
+
+@pytest.mark.parametrize("b,t,h", [(4, 2048, 16), (4, 1263, 16), (2, 6370, 4)])
+def test_slow_decay_single_pass_segments(b, t, h):
+    """The single-pass kernel (bfloat16, R = 1, N = P = 64, chunk 64) with
+    segments of 8, 5 and 4 chunks under slow decay, so that every segment's
+    outputs depend on its entry state, which reaches them only through the
+    correction after the chain."""
+    inp = I.prefill_inputs(b, t, h, 64, 64, 1, "bf16", seed=33 + t, a_range=(-8.0, -5.0))
+    check_prefill(inp, 64, label="slow-decay-single-pass")
 
 
 @pytest.mark.parametrize("dtype,R,chunk", [("f32", 1, 64), ("f32", 4, 32), ("bf16", 1, 64),
