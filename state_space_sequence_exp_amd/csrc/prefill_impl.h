@@ -150,6 +150,9 @@ struct Cfg {
   using M = Mfma<T_>;
   static constexpr int R = R_, P = P_;
   static constexpr int NC = N_;  // state size if fixed at compile time, else 0
+  // aggregates loaded at once in the chain's look-back (fewer with more
+  // state per wave: registers)
+  static constexpr int kAggBatch = N_ == 64 ? kBatch : (N_ != 0 ? kBatch / 2 : 1);
   static constexpr int es = (int)sizeof(T_);
   static constexpr int S = prefill_item_tokens(es, R_, N_, P_);  // tokens per rotation item
   static constexpr int KR = S * R_;                      // chunk rows per item
@@ -585,7 +588,7 @@ __device__ __forceinline__ float load_frag(const Tile& t, uint32_t row, int k0, 
 // robin; lane holds rows n = 4g..4g+3 of its 16x16 tile.
 __device__ __forceinline__ int state_tile(const WaveRoles& wr, int wave, int m, int ntiles) {
   const int i = (wave - wr.sw0) + m * wr.nsw;
-  return (wave >= wr.sw0 && i < ntiles) ? i : -1;
+  return (wave >= wr.sw0 && wave < wr.sw0 + wr.nsw && i < ntiles) ? i : -1;
 }
 
 // State tiles -> LDS copy G^T [P][N] (the B operand of the inter-chunk MFMA).
@@ -1309,7 +1312,7 @@ __device__ __forceinline__ void chain_phase(const PrefillArgs& a, const WaveRole
     } else {
       // newest first, several aggregates' loads in flight at a time (fewer
       // with more state per wave: registers)
-      constexpr int NB = C::NC == 64 ? kBatch : (C::NC != 0 ? kBatch / 2 : 1);
+      constexpr int NB = C::kAggBatch;
       for (int j0 = seg - 1; j0 >= g0; j0 -= NB) {
         Agg ag[NB];
 #pragma unroll

@@ -65,6 +65,7 @@ struct TCfg {
   using T = bf16;
   using M = Mfma<bf16>;
   static constexpr int R = R_, P = P_, N = N_, NC = N_;
+  static constexpr int kAggBatch = N_ == 64 ? pf::kBatch : pf::kBatch / 2;  // chain look-back
   static constexpr int es = 2;
   static constexpr int NPT = P_ / 16;          // p-tiles
   static constexpr int NNT = N_ / 16;          // n-tiles
@@ -846,6 +847,18 @@ hipError_t launch_tok(const PrefillArgs& a, hipStream_t stream) {
 // one 64 x 64 x 64 product per chunk: no input is read twice and no token
 // rotated twice.  A sequence's first segment (entry zero) writes y as it
 // goes and has no correction.
+// The chain's view of a configuration with fewer aggregates in flight.
+template <class C>
+struct TChain : C {
+  static constexpr int kAggBatch = 2;
+};
+
+// The single pass keeps the state in the first kNsw1 waves (4 tiles each):
+// they are the waves of query blocks 0 and 1, whose output units are the
+// shorter (one pair of key blocks against two), so the state update and its
+// LDS copy run while the other waves still multiply.
+constexpr int kNsw1 = 4;
+
 template <class C>
 __device__ __forceinline__ void tok1_correct_state(f32x4 (&e)[kMaxStTiles], const float* ang,
                                                    float d) {
@@ -856,7 +869,7 @@ __device__ __forceinline__ void tok1_correct_state(f32x4 (&e)[kMaxStTiles], cons
   const float2 q0 = make_float2(__builtin_amdgcn_cosf(f.x), __builtin_amdgcn_sinf(f.x));
   const float2 q1 = make_float2(__builtin_amdgcn_cosf(f.y), __builtin_amdgcn_sinf(f.y));
 #pragma unroll
-  for (int m = 0; m < C::TPW; ++m) {
+  for (int m = 0; m < C::NTILES / kNsw1; ++m) {
     const float v0 = d * e[m][0], v1 = d * e[m][1];
     const float v2 = d * e[m][2], v3 = d * e[m][3];
     e[m][0] = q0.x * v0 - q0.y * v1;
@@ -866,13 +879,75 @@ __device__ __forceinline__ void tok1_correct_state(f32x4 (&e)[kMaxStTiles], cons
   }
 }
 
+// This wave's state tiles (tile i = wave + kNsw1 m: n-tile i % NNT, p-tile
+// i / NNT; lane (g, c) holds rows 4g..4g+3 of column c) into the tile [P][N]
+// (bf16).
 template <class C>
-__device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
-                                             unsigned char* smem) {
-  constexpr int KK = C::kK1, PPG = C::PPG;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 15;
+__device__ __forceinline__ void tok1_state_to_lds(const f32x4 (&stt)[kMaxStTiles], const Tile& tG) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  if (wave >= kNsw1) return;
+#pragma unroll
+  for (int m = 0; m < C::NTILES / kNsw1; ++m) {
+    const int i = wave + kNsw1 * m;
+    const int nt = i % C::NNT, pt = i / C::NNT;
+    tG.ref<u32x2>((uint32_t)(pt * 16 + li), (uint32_t)((nt * 16 + 4 * g) * 2)) =
+        u32x2{pack_bf16(stt[m][0], stt[m][1]), pack_bf16(stt[m][2], stt[m][3])};
+  }
+}
+
+// Chunk state folded into the state waves' tiles: stt <- R(Phi_c)(d stt +
+// S), S = sum over tokens of w_u B~_u x_u^T, the A operand B~ with each
+// token's slot scaled by its state weight (t.gs), the rotation from the
+// chunk's angles (t.ang).
+template <class C>
+__device__ __forceinline__ void tok1_state_update(const TBuf& t, float d,
+                                                  f32x4 (&stt)[kMaxStTiles]) {
+  using M = typename C::M;
+  constexpr int TPW = C::NTILES / kNsw1;
+  static_assert(TPW <= kMaxStTiles && kNsw1 % C::NNT == 0, "state tiles of a wave share an n-tile");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  if (wave >= kNsw1) return;
+  const int nt = wave % C::NNT;
+  // the decayed state is the accumulator the chunk's products add to
+#pragma unroll
+  for (int m = 0; m < TPW; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) stt[m][j] *= d;
+#pragma unroll
+  for (int k0 = 0; k0 < C::LR; k0 += M::K) {
+    // slots 0..7 are tokens r0 .. r0 + 7
+    const uint32_t r0 = (uint32_t)(k0 + 8 * g);
+    bf16x8 fa = frag_tr(t.B, r0, r0 + 4, nt);
+    const float4 w0 = *reinterpret_cast<const float4*>(t.gs + 2 * kL + r0);
+    const float4 w1 = *reinterpret_cast<const float4*>(t.gs + 2 * kL + r0 + 4);
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fa[j] = from_f32<bf16>(to_f32(fa[j]) * wv[j]);
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const int pt = (wave + kNsw1 * m) / C::NNT;
+      stt[m] = M::mma(fa, frag_tr(t.X, r0, r0 + 4, pt), stt[m]);
+    }
+  }
+  // rows 4g .. 4g + 3 of n-tile nt: pairs 8 nt + 2g and 8 nt + 2g + 1
+  const float2 f = *reinterpret_cast<const float2*>(t.ang + nt * 8 + 2 * g);
+  const float2 q0 = make_float2(__builtin_amdgcn_cosf(f.x), __builtin_amdgcn_sinf(f.x));
+  const float2 q1 = make_float2(__builtin_amdgcn_cosf(f.y), __builtin_amdgcn_sinf(f.y));
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) {
+    const float v0 = stt[m][0], v1 = stt[m][1], v2 = stt[m][2], v3 = stt[m][3];
+    stt[m][0] = q0.x * v0 - q0.y * v1;
+    stt[m][1] = q0.y * v0 + q0.x * v1;
+    stt[m][2] = q1.x * v2 - q1.y * v3;
+    stt[m][3] = q1.y * v2 + q1.x * v3;
+  }
+}
+
+// The uniform values of the segment of a ticket.
+template <class C>
+__device__ __forceinline__ TCtx tok_ctx(const PrefillArgs& a, int ticket) {
   const int BH = a.nb * a.H;
   TCtx s;
   s.seg = ticket / BH;
@@ -885,6 +960,33 @@ __device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
   s.rowTh = (uint32_t)(a.H * (C::N / 2) * 4);
   s.rowDt = (uint32_t)(a.H * 4);
   s.rowX = (uint32_t)(a.H * C::R * C::P * 2);
+  s.Ah = 0.f;
+  return s;
+}
+
+// Staging of the single pass: chunk i of the segment into ring buffer i % 3
+// (B, x, theta, dt and lam) and C slot i.  (The offsets are made opaque so
+// that per-lane addresses are formed at each use rather than kept live
+// across the loop.)
+template <class C>
+__device__ __forceinline__ void tok1_issue(const PrefillArgs& a, const TCtx& s, int i,
+                                           unsigned char* smem) {
+  if (i >= s.c1 - s.c0) return;
+  unsigned char* r = smem + pf::opaque_u((uint32_t)(i % 3) * C::k1Ring);
+  unsigned char* pc = smem + pf::opaque_u(C::o1Per + (uint32_t)i * C::k1Per);
+  const TDst d = {r + C::o1B, pc + C::o1C, r + C::o1X, r + C::o1Th, r + C::o1Raw};
+  tok_issue<C, true, true>(a, s, s.c0 + i, d);
+}
+
+// One segment in one pass.
+template <class C>
+__device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
+                                             unsigned char* smem) {
+  constexpr int KK = C::kK1, PPG = C::PPG;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15;
+  TCtx s = tok_ctx<C>(a, ticket);
   s.Ah = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.A[s.h])));
   const bool has_lam = a.lam != nullptr;
   // the sequence's first segment starts from zero: its outputs are final
@@ -897,19 +999,12 @@ __device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
   const uint32_t qrow = (uint32_t)(qb * 16 + li);
   const int tq = qb * 16 + li;
 
-  // (the offsets are made opaque so that per-lane addresses are formed in
-  // each step rather than kept live across the loop)
   auto ring = [&](int i) { return smem + pf::opaque_u((uint32_t)(i % 3) * C::k1Ring); };
   auto dbl = [&](int i) {
     return smem + pf::opaque_u(C::o1Dbl + (uint32_t)(i & 1) * C::k1Dbl);
   };
   auto per = [&](int i) { return smem + pf::opaque_u(C::o1Per + (uint32_t)i * C::k1Per); };
-  auto issue = [&](int i) {
-    if (i >= K) return;
-    unsigned char* r = ring(i);
-    const TDst d = {r + C::o1B, per(i) + C::o1C, r + C::o1X, r + C::o1Th, r + C::o1Raw};
-    tok_issue<C, true, true>(a, s, s.c0 + i, d);
-  };
+  auto issue = [&](int i) { tok1_issue<C>(a, s, i, smem); };
   auto yrange = [&](int i) {
     const int t0 = (s.c0 + i) * kL;
     const int len = min(kL, a.T - t0);
@@ -959,7 +1054,7 @@ __device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
     t.gs = reinterpret_cast<float*>(d2 + C::o1Gs);
     t.ang = reinterpret_cast<float*>(pc + C::o1Ang);
     const float cse = tok_rotate<C, true, true>(t, has_lam, s.Ah, sang);
-    if (i > 0) tok_state_to_lds<C>(stt, t.G);
+    if (i > 0) tok1_state_to_lds<C>(stt, t.G);
     // the next chunk's loads (issued a step ago) have landed
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -979,7 +1074,7 @@ __device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
       for (int pp = 0; pp < PPG; ++pp) yp[KK - 1][pp] = acc[pp];
     }
     const float d = __expf(cse);
-    tok_state_update<C, true>(t, d, stt);
+    tok1_state_update<C>(t, d, stt);
 #pragma unroll
     for (int c = 0; c + 1 < KK; ++c) dec[c] = dec[c + 1];
     dec[KK - 1] = d;
@@ -1004,9 +1099,12 @@ __device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
     s_srot[wave * C::NPW + lane] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
   }
   __syncthreads();  // s_srot; every MFMA read of the last step is done
-  const WaveRoles wr = {0, 0, 0, 0, kW};
+  const WaveRoles wr = {0, 0, 0, 0, kNsw1};
   f32x4 ent[kMaxStTiles];
-  pf::chain_phase<C>(a, wr, s.seg, s.bh, ticket, __expf(seg_logdecay), s_srot, s_misc, stt, ent);
+  // (the state waves hold four tiles each beside the partial outputs: two
+  // aggregates in flight at a time)
+  pf::chain_phase<TChain<C>>(a, wr, s.seg, s.bh, ticket, __expf(seg_logdecay), s_srot, s_misc, stt,
+                          ent);
   __builtin_amdgcn_s_waitcnt(0);
   if (direct) return;
 
@@ -1016,8 +1114,8 @@ __device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
 #pragma unroll
   for (int c = 0; c < KK; ++c) {
     if (c < K) {
-      tok_state_to_lds<C>(ent, tile_at(smem + (uint32_t)c * (C::P * C::kRowN), C::kRowN));
-      if (c + 1 < K)
+      tok1_state_to_lds<C>(ent, tile_at(smem + (uint32_t)c * (C::P * C::kRowN), C::kRowN));
+      if (c + 1 < K && wave < kNsw1)
         tok1_correct_state<C>(ent, reinterpret_cast<const float*>(per(c) + C::o1Ang), dec[c]);
     }
   }

@@ -217,16 +217,17 @@ def test_workspace_reused_across_shapes():
     assert not ws[:4 * nw].view(torch.int32).cpu().numpy().any()
 
 
-def test_dirty_counters_reported():
+@pytest.mark.parametrize("n", [32, 64])
+def test_dirty_counters_reported(n):
     """A workspace whose class-0 ticket word is not zero on entry makes every
     workgroup of that class skip its segment and raise the error word (2);
     the counters are still returned to zero, so the next call (error word
-    cleared) is correct."""
+    cleared) is correct.  N = 64 takes the single-pass kernel."""
     import torch
     import state_space_sequence_exp_amd as m3
-    inp = I.prefill_inputs(1, 200, 2, 32, 64, 1, "bf16", seed=63)
+    inp = I.prefill_inputs(1, 200, 2, n, 64, 1, "bf16", seed=63)
     g = upload_prefill(inp)
-    need = m3.prefill_workspace_size(1, 200, 2, 64, 32, 1, 64, g["x"].dtype)
+    need = m3.prefill_workspace_size(1, 200, 2, 64, n, 1, 64, g["x"].dtype)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
     words = ws[:4 * counter_words(1, 200, 2, 64)].view(torch.int32)
     words[0] = 1 << 20                   # a ticket far past the grid
