@@ -833,6 +833,84 @@ hipError_t launch_tok(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Output unit of the single pass (rank 1, query block qb, PPG p-tiles from
+// p_lo):
+//   y_t = exp(cs_t) C~_t^T G + sum_u W[t,u] (C~_t^T B~_u) x_u^T.
+// The query fragments are read once for the inter-chunk term and every pair
+// of key blocks, and each pair requests all its LDS operands (key
+// fragments, key scalars, x fragments) before its first product: the mask's
+// exponentials are kept out of a branch by an empty asm statement, which
+// the scheduler does not move loads across.
+template <class C>
+__device__ __forceinline__ void tok1_unit(const TBuf& t, int qb, int p_lo, f32x4 (&acc)[C::PPG]) {
+  using M = typename C::M;
+  constexpr int PPG = C::PPG, NK = C::N / M::K;
+  static_assert(C::R == 1, "rank 1");
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const uint32_t qrow = (uint32_t)(qb * 16 + li);
+  const int tq = qb * 16 + li;
+  bf16x8 fq[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) fq[k] = frag_row(t.C, qrow, k * M::K);
+  const float csq = t.cs[tq];
+  {
+    f32x4 gi[PPG];
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp) gi[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp)
+        gi[pp] = M::mma(frag_row(t.G, (uint32_t)((p_lo + pp) * 16 + li), k * M::K), fq[k], gi[pp]);
+    const float eq = __expf(csq);
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[pp][j] = gi[pp][j] * eq;
+  }
+  for (int kb = 0; kb <= qb; kb += 2) {
+    bf16x8 fk[2][NK], fx[PPG];
+    float4 c4[2], ga4[2], go4[2];
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fk[i][k] = frag_row(t.B, (uint32_t)((kb + i) * 16 + li), k * M::K);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row0 = (kb + i) * 16 + 4 * g;
+      c4[i] = *reinterpret_cast<const float4*>(t.cs + row0);
+      ga4[i] = *reinterpret_cast<const float4*>(t.gs + row0);
+      go4[i] = *reinterpret_cast<const float4*>(t.gs + kL + row0);
+    }
+    // x^T with the scores' slot order: keys 16 kb + 4g .. + 3, then + 16
+    const uint32_t r0 = (uint32_t)(kb * 16 + 4 * g), r1 = r0 + 16;
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp) fx[pp] = frag_tr(t.X, r0, r1, p_lo + pp);
+    f32x4 sct[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sct[i] = M::mma(fk[i][k], fq[k], sct[i]);
+    float kcs[2][4], kga[2][4], kgom[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      kcs[i][0] = c4[i].x; kcs[i][1] = c4[i].y; kcs[i][2] = c4[i].z; kcs[i][3] = c4[i].w;
+      kga[i][0] = ga4[i].x; kga[i][1] = ga4[i].y; kga[i][2] = ga4[i].z; kga[i][3] = ga4[i].w;
+      kgom[i][0] = go4[i].x; kgom[i][1] = go4[i].y; kgom[i][2] = go4[i].z; kgom[i][3] = go4[i].w;
+    }
+    pf::mask_scores<1, 2>(sct, kcs, kga, kgom, kb, g, tq, csq);
+    bf16x8 fs;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      fs[j] = from_f32<bf16>(sct[0][j]);
+      fs[4 + j] = from_f32<bf16>(sct[1][j]);
+    }
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp) acc[pp] = M::mma(fx[pp], fs, acc[pp]);
+  }
+}
+
 // ---- single pass -----------------------------------------------------------
 // A segment of K <= kK1 chunks in one walk over its inputs.  Each step
 // stages, rotates and multiplies one chunk as the output pass does, but
@@ -1054,15 +1132,13 @@ __device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
     t.gs = reinterpret_cast<float*>(d2 + C::o1Gs);
     t.ang = reinterpret_cast<float*>(pc + C::o1Ang);
     const float cse = tok_rotate<C, true, true>(t, has_lam, s.Ah, sang);
-    if (i > 0) tok1_state_to_lds<C>(stt, t.G);
+    // (zero in the first step: one code path for every step)
+    tok1_state_to_lds<C>(stt, t.G);
     // the next chunk's loads (issued a step ago) have landed
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x4 acc[PPG];
-#pragma unroll
-    for (int pp = 0; pp < PPG; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (i > 0) tok_inter<C>(t.G, t.C, qrow, p_lo, __expf(t.cs[tq]), acc);
-    tok_intra<C, true>(t, qb, p_lo, acc);
+    tok1_unit<C>(t, qb, p_lo, acc);
     if (direct) {
       tok_unit_store<C>(yrange(i), s.rowX, qb, p_lo, acc);
     } else {
