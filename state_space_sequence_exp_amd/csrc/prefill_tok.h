@@ -842,7 +842,8 @@ hipError_t launch_tok(const PrefillArgs& a, hipStream_t stream) {
 // exponentials are kept out of a branch by an empty asm statement, which
 // the scheduler does not move loads across.
 template <class C>
-__device__ __forceinline__ void tok1_unit(const TBuf& t, int qb, int p_lo, f32x4 (&acc)[C::PPG]) {
+__device__ __forceinline__ void tok1_unit(const TBuf& t, int qb, int p_lo, int kb0,
+                                          f32x4 (&acc)[C::PPG]) {
   using M = typename C::M;
   constexpr int PPG = C::PPG, NK = C::N / M::K;
   static_assert(C::R == 1, "rank 1");
@@ -869,7 +870,7 @@ __device__ __forceinline__ void tok1_unit(const TBuf& t, int qb, int p_lo, f32x4
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[pp][j] = gi[pp][j] * eq;
   }
-  for (int kb = 0; kb <= qb; kb += 2) {
+  for (int kb = kb0; kb <= qb; kb += 2) {
     bf16x8 fk[2][NK], fx[PPG];
     float4 c4[2], ga4[2], go4[2];
 #pragma unroll
@@ -909,6 +910,72 @@ __device__ __forceinline__ void tok1_unit(const TBuf& t, int qb, int p_lo, f32x4
 #pragma unroll
     for (int pp = 0; pp < PPG; ++pp) acc[pp] = M::mma(fx[pp], fs, acc[pp]);
   }
+}
+
+// Hand-over of masked scores inside a step of the single pass.  The waves
+// of query blocks 2 and 3 have two pairs of key blocks, the others one; so
+// the waves of blocks 0 and 1 first compute the masked scores of query
+// blocks 2 and 3 against key blocks 0 and 1 (one 16 x 16 block each, in the
+// accumulator layout the product with x takes as its operand) and leave
+// them in `ex` (2 KB of LDS) with a workgroup-scope release count; the
+// others take them once the count shows all four, with an acquire load.
+// Lane (g, c) of block kb holds keys 16 kb + 4g .. + 3 of query column c.
+template <class C>
+__device__ __forceinline__ void tok1_scores_give(const TBuf& t, uint32_t* ex, int* flag) {
+  using M = typename C::M;
+  constexpr int NK = C::N / M::K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int qx = 2 + wave / 2, kb = wave % 2;
+  const int tq = qx * 16 + li;
+  bf16x8 fk[NK], fq[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    fk[k] = frag_row(t.B, (uint32_t)(kb * 16 + li), k * M::K);
+    fq[k] = frag_row(t.C, (uint32_t)tq, k * M::K);
+  }
+  const int row0 = kb * 16 + 4 * g;
+  const float4 c4 = *reinterpret_cast<const float4*>(t.cs + row0);
+  const float4 ga4 = *reinterpret_cast<const float4*>(t.gs + row0);
+  const float4 go4 = *reinterpret_cast<const float4*>(t.gs + kL + row0);
+  const float csq = t.cs[tq];
+  f32x4 sct[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int k = 0; k < NK; ++k) sct[0] = M::mma(fk[k], fq[k], sct[0]);
+  const float kcs[1][4] = {{c4.x, c4.y, c4.z, c4.w}};
+  const float kga[1][4] = {{ga4.x, ga4.y, ga4.z, ga4.w}};
+  const float kgom[1][4] = {{go4.x, go4.y, go4.z, go4.w}};
+  pf::mask_scores<1, 1>(sct, kcs, kga, kgom, kb, g, tq, csq);
+  reinterpret_cast<u32x2*>(ex)[(qx - 2) * 128 + kb * 64 + lane] =
+      u32x2{pack_bf16(sct[0][0], sct[0][1]), pack_bf16(sct[0][2], sct[0][3])};
+  // one count per wave (the release waits for all of the wave's stores)
+  if (lane == 0) __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// The other side: y += (masked scores of key blocks 0 and 1) x, for query
+// block qb (2 or 3) and this wave's p-tiles, once the count reaches
+// `target`.  The wait is bounded (the givers are waves of this workgroup
+// with no wait of their own before they give).
+template <class C>
+__device__ __forceinline__ void tok1_scores_take(const TBuf& t, const uint32_t* ex, int* flag,
+                                                 int target, int qb, int p_lo,
+                                                 f32x4 (&acc)[C::PPG]) {
+  using M = typename C::M;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  bf16x8 fx[C::PPG];
+  const uint32_t r0 = (uint32_t)(4 * g), r1 = r0 + 16;
+#pragma unroll
+  for (int pp = 0; pp < C::PPG; ++pp) fx[pp] = frag_tr(t.X, r0, r1, p_lo + pp);
+  for (int spins = 0; __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
+                          target && spins < (1 << 20);
+       ++spins)
+    __builtin_amdgcn_s_sleep(1);
+  const u32x2 v0 = reinterpret_cast<const u32x2*>(ex)[(qb - 2) * 128 + lane];
+  const u32x2 v1 = reinterpret_cast<const u32x2*>(ex)[(qb - 2) * 128 + 64 + lane];
+  const bf16x8 fs = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+#pragma unroll
+  for (int pp = 0; pp < C::PPG; ++pp) acc[pp] = M::mma(fx[pp], fs, acc[pp]);
 }
 
 // ---- single pass -----------------------------------------------------------
@@ -1108,6 +1175,7 @@ __device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
   double sang = 0.0;  // lanes < NPW: the segment's angle of pair wave * NPW + lane
   float seg_logdecay = 0.f;
 
+  if (tid == 0) s_misc[8] = 0;  // the scores hand-over count
   issue(0);
   __builtin_amdgcn_s_waitcnt(0);
   issue(1);
@@ -1138,7 +1206,19 @@ __device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x4 acc[PPG];
-    tok1_unit<C>(t, qb, p_lo, acc);
+    {
+      // the scores hand-over lives in this chunk's theta area (read only by
+      // the rotation before the barrier, reloaded two steps later)
+      uint32_t* ex = reinterpret_cast<uint32_t*>(r + C::o1Th);
+      int* flag = s_misc + 8;
+      if (wave < 4) {
+        tok1_scores_give<C>(t, ex, flag);
+        tok1_unit<C>(t, qb, p_lo, 0, acc);
+      } else {
+        tok1_unit<C>(t, qb, p_lo, 2, acc);
+        tok1_scores_take<C>(t, ex, flag, 4 * (i + 1), qb, p_lo, acc);
+      }
+    }
     if (direct) {
       tok_unit_store<C>(yrange(i), s.rowX, qb, p_lo, acc);
     } else {
