@@ -766,7 +766,7 @@ def main():
         "config": {"workload": "SISO prefill: batch 4, T=2048, 16 heads, N=64, P=64, R=1, "
                                "bf16 x/B/C, fp32 state, chunk 64",
                    "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "none"},
-        "roofline": {"kernel": "prefill_tok_kernel (token-lane fused chained prefill, one launch per m3_prefill call)",
+        "roofline": {"kernel": "prefill_tok1_kernel (single-pass token-lane fused chained prefill, one launch per m3_prefill call)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": nbytes,
