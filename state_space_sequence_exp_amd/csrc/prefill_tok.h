@@ -294,6 +294,13 @@ __device__ __forceinline__ void tok_issue(const PrefillArgs& a, const TCtx& s, i
         const u32x4v rL = rsrc_words(a.lam + hrow, scb);
         dma_lds<4>(rL, raw + C::k1Sc, u * s.rowDt);
         if (u == 0) dma_lds<4>(rL, raw + C::k1Sc + 256, 64 * s.rowDt);
+      } else {
+        // without lam the weight is 1 (the exponential-Euler rule): ones
+        // in its place, so the rotation reads lam on every path (the
+        // barrier after this step orders these stores before it)
+        float* lw = reinterpret_cast<float*>(d.raw + C::k1Sc);
+        lw[u] = 1.f;
+        if (u == 0) lw[64] = 1.f;
       }
     } else {
       dma_lds<4>(rD, raw, u * s.rowDt);
@@ -372,10 +379,20 @@ __device__ __forceinline__ float tok_rotate(const TBuf& t, bool has_lam, float A
   const uint32_t u = threadIdx.x & 63, w = threadIdx.x >> 6;
   constexpr uint32_t kLam = kSplit ? C::k1Sc / 4 : 128, kNext = kSplit ? 1 : 64;
   const float d = t.raw[u], dn = t.raw[kNext + u];
-  // without lam the weight is 1 (the exponential-Euler rule)
-  const float l = has_lam ? t.raw[kLam + u] : 1.f, ln = has_lam ? t.raw[kLam + kNext + u] : 1.f;
+  // without lam the weight is 1 (the exponential-Euler rule); the single
+  // pass stages ones then, and reads lam on every path
+  const float l = (kSplit || has_lam) ? t.raw[kLam + u] : 1.f;
+  const float ln = (kSplit || has_lam) ? t.raw[kLam + kNext + u] : 1.f;
   uint32_t th[NPW];
   ld_tile<NPW * 4>(t.Th, u, w * (NPW * 4), th);
+  // this lane's pairs of B (and C), requested with the other reads, before
+  // the scalar stores below, which the compiler would not move them across
+  uint32_t bv[R][NPW], cv[R][NPW];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    ld_tile<NPW * 4>(t.B, u * R + r, w * (NPW * 4), bv[r]);
+    if constexpr (kOut) ld_tile<NPW * 4>(t.C, u * R + r, w * (NPW * 4), cv[r]);
+  }
   // per-token scalars (exponential-trapezoidal weights; every wave has them)
   const float cs = wave_incl_scan(d * Ah);
   const float cse = wave_read_lane(cs, 63);
@@ -433,18 +450,16 @@ __device__ __forceinline__ float tok_rotate(const TBuf& t, bool has_lam, float A
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t row = u * R + r;
-    uint32_t bv[NPW], cv[NPW], bw[NPW], bt[NPW], ct[NPW];
-    ld_tile<NPW * 4>(t.B, row, w * (NPW * 4), bv);
-    if constexpr (kOut) ld_tile<NPW * 4>(t.C, row, w * (NPW * 4), cv);
+    uint32_t bw[NPW], bt[NPW], ct[NPW];
 #pragma unroll
     for (int k = 0; k < NPW; ++k) {
-      const bf16x2 bp = __builtin_bit_cast(bf16x2, bv[k]);
+      const bf16x2 bp = __builtin_bit_cast(bf16x2, bv[r][k]);
       const float rb0 = __builtin_amdgcn_fdot2_f32_bf16(bp, rcs[k], 0.f, false);
       const float rb1 = __builtin_amdgcn_fdot2_f32_bf16(bp, rncs[k], 0.f, false);
       if constexpr (!kSplit) bw[k] = pack_bf16(wgt * rb0, wgt * rb1);
       if constexpr (kOut) {
         bt[k] = pack_bf16(rb0, rb1);
-        const bf16x2 cp = __builtin_bit_cast(bf16x2, cv[k]);
+        const bf16x2 cp = __builtin_bit_cast(bf16x2, cv[r][k]);
         ct[k] = pack_bf16(__builtin_amdgcn_fdot2_f32_bf16(cp, rcs[k], 0.f, false),
                           __builtin_amdgcn_fdot2_f32_bf16(cp, rncs[k], 0.f, false));
       }
