@@ -1604,6 +1604,31 @@ __device__ __forceinline__ void finish_workgroup(const PrefillArgs& a, int* s_mi
   }
 }
 
+// finish_workgroup in two halves, so that the count's round trip can
+// overlap work that touches no counter: finish_count (thread 0 counts the
+// workgroup done; call it once the workgroup has published and read every
+// status word it touches; returns the count before it, meaningful in thread
+// 0 only) and finish_reset (the last workgroup zeroes the counters).
+__device__ __forceinline__ int finish_count(const PrefillArgs& a) {
+  int prev = 0;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    prev = atomicAdd(a.done, 1);
+  }
+  return prev;
+}
+__device__ __forceinline__ void finish_reset(const PrefillArgs& a, int prev, int* s_misc) {
+  const int tid = threadIdx.x;
+  if (tid == 0) s_misc[1] = prev == (int)gridDim.x - 1;
+  __syncthreads();
+  if (s_misc[1]) {
+    for (int i = tid; i < (int)gridDim.x; i += kT) a.status[i] = 0;
+    if (tid < a.ncls) a.ticket[kTicketStride * tid] = 0;
+    if (tid == 0) *a.done = 0;
+  }
+}
+
 template <class C>
 __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a_in) {
   extern __shared__ __align__(16) unsigned char smem[];

@@ -1138,10 +1138,12 @@ __device__ __forceinline__ void tok1_issue(const PrefillArgs& a, const TCtx& s, 
   tok_issue<C, true, true>(a, s, s.c0 + i, d);
 }
 
-// One segment in one pass.
+// One segment in one pass.  Counts the workgroup done once the chain is
+// over (pf::finish_count) and returns that count (thread 0), so that its
+// round trip overlaps the correction.
 template <class C>
-__device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
-                                             unsigned char* smem) {
+__device__ __forceinline__ int tok1_segment(const PrefillArgs& a, int ticket,
+                                            unsigned char* smem) {
   constexpr int KK = C::kK1, PPG = C::PPG;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1277,7 +1279,9 @@ __device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
   pf::chain_phase<TChain<C>>(a, wr, s.seg, s.bh, ticket, __expf(seg_logdecay), s_srot, s_misc, stt,
                           ent);
   __builtin_amdgcn_s_waitcnt(0);
-  if (direct) return;
+  // no counter is touched after the chain
+  const int done_prev = pf::finish_count(a);
+  if (direct) return done_prev;
 
   // ---- correction: y_t += exp(cs_t) C~_t^T E_c ------------------------------
   // E_c as [P][N] bf16 tiles in the ring (free now: the chain's barriers
@@ -1301,6 +1305,7 @@ __device__ __forceinline__ void tok1_segment(const PrefillArgs& a, int ticket,
       tok_unit_store<C>(yrange(c), s.rowX, qb, p_lo, yp[c]);
     }
   }
+  return done_prev;
 }
 
 template <class C>
@@ -1310,11 +1315,14 @@ __global__ void __launch_bounds__(kT) prefill_tok1_kernel(PrefillArgs a_in) {
   a.N = C::N;
   int* s_misc = reinterpret_cast<int*>(smem + C::o1Misc);
   const int ticket = pf::take_ticket(a, s_misc);
-  if (ticket >= 0 && ticket < (int)gridDim.x)
-    tok1_segment<C>(a, ticket, smem);
-  else
+  int done_prev;
+  if (ticket >= 0 && ticket < (int)gridDim.x) {
+    done_prev = tok1_segment<C>(a, ticket, smem);
+  } else {
     pf::bad_ticket(a);
-  pf::finish_workgroup(a, s_misc);
+    done_prev = pf::finish_count(a);
+  }
+  pf::finish_reset(a, done_prev, s_misc);
 }
 
 template <class C>
