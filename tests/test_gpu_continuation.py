@@ -52,6 +52,7 @@ SPLITS = [
     ("bf16", 1, 180, 2, 64, 64, 4, 64, (64, 179)),     # MIMO, a one-token last piece
     ("bf16", 1, 1000, 1, 64, 64, 1, 32, (333, 667)),   # many segments per piece
     ("bf16", 4, 1500, 16, 64, 64, 1, 64, (700,)),      # single pass, segments of 3 and 4 chunks
+    ("bf16", 4, 4096, 16, 64, 64, 1, 64, (2048,)),     # single pass, 8-chunk segments, no direct one
 ]
 
 
