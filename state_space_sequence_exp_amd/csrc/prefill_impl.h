@@ -1371,11 +1371,41 @@ __device__ __forceinline__ void chain_phase(const PrefillArgs& a, const WaveRole
   }
 }
 
+// The last workgroup to finish zeroes the chain counters, so the next call
+// on this workspace starts from zeros without a reset launch.  In two
+// halves, so that the count's round trip overlaps work that touches no
+// counter: finish_count (thread 0 counts the workgroup done; called once the
+// workgroup has published and read every status word it touches: its reads
+// returned their values, the waits used them, and its own stores are
+// complete, s_waitcnt before the count, so the count needs no fence;
+// returns the count before it, meaningful in thread 0 only) and
+// finish_reset (the zeroing follows the count's returned value, and the next
+// call sees it across the kernel boundary).
+__device__ __forceinline__ int finish_count(const PrefillArgs& a) {
+  int prev = 0;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    prev = atomicAdd(a.done, 1);
+  }
+  return prev;
+}
+__device__ __forceinline__ void finish_reset(const PrefillArgs& a, int prev, int* s_misc) {
+  const int tid = threadIdx.x;
+  if (tid == 0) s_misc[1] = prev == (int)gridDim.x - 1;
+  __syncthreads();
+  if (s_misc[1]) {
+    for (int i = tid; i < (int)gridDim.x; i += kT) a.status[i] = 0;
+    if (tid < a.ncls) a.ticket[kTicketStride * tid] = 0;
+    if (tid == 0) *a.done = 0;
+  }
+}
+
 // One workgroup's segment: local exit state, chain, outputs.  `ticket` is
 // known to lie inside the grid.
 template <class C>
-__device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const PrefillLayout& lay,
-                                                int ticket, unsigned char* smem) {
+__device__ __forceinline__ int prefill_segment(const PrefillArgs& a, const PrefillLayout& lay,
+                                               int ticket, unsigned char* smem) {
   constexpr int P = C::P;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1499,6 +1529,9 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
   // not need would otherwise leave the compiler a pending write to its
   // register, waited for inside the output pass)
   __builtin_amdgcn_s_waitcnt(0);
+  // no counter is touched after the chain: the workgroup counts itself done
+  // here, and the count's round trip overlaps the output pass
+  const int done_prev = finish_count(a);
   // the output pass's state distribution (see Cfg::kSplit3): the entry
   // state moves to its waves through LDS
   WaveRoles wr3 = wr;
@@ -1547,6 +1580,7 @@ __device__ __forceinline__ void prefill_segment(const PrefillArgs& a, const Pref
     }
     buf ^= 1;
   }
+  return done_prev;
 }
 
 // The workgroup's ticket (its segment), or -1.  Only the holder of a ticket
@@ -1582,53 +1616,6 @@ __device__ __forceinline__ void bad_ticket(const PrefillArgs& a) {
   if (threadIdx.x == 0) __hip_atomic_store(a.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The last workgroup to finish zeroes the chain counters, so the next call
-// on this workspace starts from zeros without a reset launch.  Every other
-// workgroup has published and read every status word it touches before
-// counting itself done: its reads returned their values (the waits used
-// them) and its own stores are complete (s_waitcnt before the count), so the
-// count needs no fence; the zeroing follows the count's returned value, and
-// the next call sees it across the kernel boundary.
-__device__ __forceinline__ void finish_workgroup(const PrefillArgs& a, int* s_misc) {
-  const int tid = threadIdx.x;
-  __syncthreads();
-  if (tid == 0) {
-    __builtin_amdgcn_s_waitcnt(0);
-    s_misc[1] = atomicAdd(a.done, 1) == (int)gridDim.x - 1;
-  }
-  __syncthreads();
-  if (s_misc[1]) {
-    for (int i = tid; i < (int)gridDim.x; i += kT) a.status[i] = 0;
-    if (tid < a.ncls) a.ticket[kTicketStride * tid] = 0;
-    if (tid == 0) *a.done = 0;
-  }
-}
-
-// finish_workgroup in two halves, so that the count's round trip can
-// overlap work that touches no counter: finish_count (thread 0 counts the
-// workgroup done; call it once the workgroup has published and read every
-// status word it touches; returns the count before it, meaningful in thread
-// 0 only) and finish_reset (the last workgroup zeroes the counters).
-__device__ __forceinline__ int finish_count(const PrefillArgs& a) {
-  int prev = 0;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_s_waitcnt(0);
-    prev = atomicAdd(a.done, 1);
-  }
-  return prev;
-}
-__device__ __forceinline__ void finish_reset(const PrefillArgs& a, int prev, int* s_misc) {
-  const int tid = threadIdx.x;
-  if (tid == 0) s_misc[1] = prev == (int)gridDim.x - 1;
-  __syncthreads();
-  if (s_misc[1]) {
-    for (int i = tid; i < (int)gridDim.x; i += kT) a.status[i] = 0;
-    if (tid < a.ncls) a.ticket[kTicketStride * tid] = 0;
-    if (tid == 0) *a.done = 0;
-  }
-}
-
 template <class C>
 __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a_in) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1641,11 +1628,14 @@ __global__ void __launch_bounds__(kT) prefill_kernel(PrefillArgs a_in) {
   // (the range test stays at the call: the segment code is compiled knowing
   // the ticket lies in the grid)
   const int ticket = take_ticket(a, s_misc);
-  if (ticket >= 0 && ticket < (int)gridDim.x)
-    prefill_segment<C>(a, lay, ticket, smem);
-  else
+  int done_prev;
+  if (ticket >= 0 && ticket < (int)gridDim.x) {
+    done_prev = prefill_segment<C>(a, lay, ticket, smem);
+  } else {
     bad_ticket(a);
-  finish_workgroup(a, s_misc);
+    done_prev = finish_count(a);
+  }
+  finish_reset(a, done_prev, s_misc);
 }
 
 template <class C>

@@ -728,8 +728,8 @@ __device__ __forceinline__ void tok_outputs(const PrefillArgs& a, const TCtx& s,
 }
 
 template <class C>
-__device__ __forceinline__ void tok_segment(const PrefillArgs& a, int ticket,
-                                            unsigned char* smem) {
+__device__ __forceinline__ int tok_segment(const PrefillArgs& a, int ticket,
+                                           unsigned char* smem) {
   constexpr int NB = C::NBUF;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -771,6 +771,7 @@ __device__ __forceinline__ void tok_segment(const PrefillArgs& a, int ticket,
   for (int q = 0; q < kMaxStTiles; ++q) stt[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   double sang = 0.0;  // lanes < NPW: the segment's angle of pair wave * NPW + lane
   float seg_logdecay = 0.f;
+  int done_prev = 0;
 
   // prologue: item 0 staged and published, item 1 on its way
   issue(0);
@@ -821,8 +822,12 @@ __device__ __forceinline__ void tok_segment(const PrefillArgs& a, int ticket,
       // the chain did not need leaves the compiler a pending write to its
       // register, and it would wait for all memory at the top of every step
       __builtin_amdgcn_s_waitcnt(0);
+      // no counter is touched after the chain: count the workgroup done
+      // here, so the count's round trip overlaps the output pass
+      done_prev = pf::finish_count(a);
     }
   }
+  return done_prev;
 }
 
 template <class C>
@@ -832,11 +837,14 @@ __global__ void __launch_bounds__(kT) prefill_tok_kernel(PrefillArgs a_in) {
   a.N = C::N;
   int* s_misc = reinterpret_cast<int*>(smem + C::oMisc);
   const int ticket = pf::take_ticket(a, s_misc);
-  if (ticket >= 0 && ticket < (int)gridDim.x)
-    tok_segment<C>(a, ticket, smem);
-  else
+  int done_prev;
+  if (ticket >= 0 && ticket < (int)gridDim.x) {
+    done_prev = tok_segment<C>(a, ticket, smem);
+  } else {
     pf::bad_ticket(a);
-  pf::finish_workgroup(a, s_misc);
+    done_prev = pf::finish_count(a);
+  }
+  pf::finish_reset(a, done_prev, s_misc);
 }
 
 template <class C>
