@@ -909,6 +909,21 @@ __device__ __forceinline__ void output_unit(const PrefillArgs& a, const Ctx& s, 
 
     // intra-chunk term over key blocks up to the diagonal
     for (int kb = 0; kb * 16 <= qb * 16 + 15; kb += KB) {
+      // the step's x pieces and key scalars first: the mask's empty asm
+      // statement keeps the scheduler from moving reads across it
+      bf16x4 xlo[PPG], xhi[PPG];
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int pp = 0; pp < PPG; ++pp) {
+          const uint32_t xr = (uint32_t)((p_lo + pp) * 16 + li);
+          // key rows kb*16 + 4g.. and (kb+1)*16 + 4g..
+          xlo[pp] = tX.ref2<bf16x4>(xr, 8u * g, (uint32_t)kb * 32u);
+          xhi[pp] = tX.ref2<bf16x4>(xr, 32u + 8u * g, (uint32_t)kb * 32u);
+        }
+      }
+      float kcs[KB][4], kga[KB][4], kgom[KB][4];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) key_scalars4<R>(sc, (kb + i) * 16 + 4 * g, kcs[i], kga[i], kgom[i]);
       f32x4 sct[KB];
 #pragma unroll
       for (int i = 0; i < KB; ++i) sct[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -921,9 +936,6 @@ __device__ __forceinline__ void output_unit(const PrefillArgs& a, const Ctx& s, 
           sct[i] = M::mma(fk, fq, sct[i]);  // rows = keys, cols = queries
         }
       }
-      float kcs[KB][4], kga[KB][4], kgom[KB][4];
-#pragma unroll
-      for (int i = 0; i < KB; ++i) key_scalars4<R>(sc, (kb + i) * 16 + 4 * g, kcs[i], kga[i], kgom[i]);
       mask_scores<R, KB>(sct, kcs, kga, kgom, kb, g, tq, csq);
       if constexpr (sizeof(T) == 2) {
         bf16x8 fa;
@@ -934,15 +946,11 @@ __device__ __forceinline__ void output_unit(const PrefillArgs& a, const Ctx& s, 
         }
 #pragma unroll
         for (int pp = 0; pp < PPG; ++pp) {
-          const uint32_t xr = (uint32_t)((p_lo + pp) * 16 + li);
-          // key rows kb*16 + 4g.. and (kb+1)*16 + 4g..
-          const bf16x4 lo = tX.ref2<bf16x4>(xr, 8u * g, (uint32_t)kb * 32u);
-          const bf16x4 hi = tX.ref2<bf16x4>(xr, 32u + 8u * g, (uint32_t)kb * 32u);
           bf16x8 fb;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            fb[j] = lo[j];
-            fb[4 + j] = hi[j];
+            fb[j] = xlo[pp][j];
+            fb[4 + j] = xhi[pp][j];
           }
           acc[pp] = Mfma<bf16>::mma(fa, fb, acc[pp]);
         }
