@@ -43,6 +43,16 @@
 // c + 2], so one barrier per chunk suffices, waves that finish their MFMA
 // work go on to rotate the next chunk while others still multiply, and the
 // loads have the next step to arrive.
+//
+// Two kernels share this layout.  prefill_tok_kernel walks a segment twice
+// (a local pass for its exit state, then the output pass from the true entry
+// state), like prefill_impl.h.  prefill_tok1_kernel, for segments of up to
+// eight chunks (the segment rule gives eight at the SISO bench shape), walks
+// it once: each chunk's outputs are computed from the segment's zero-entry
+// state, C~ and the scalars stay in the LDS and the partial outputs in
+// registers, and after the chain a correction adds the entry state's share
+// exp(cs_t) C~_t^T E_c (the state is linear in its entry), so no input is
+// read or rotated twice.  See tok1_segment.
 #pragma once
 
 #include "prefill_impl.h"
@@ -531,10 +541,7 @@ __device__ __forceinline__ bf16x8 frag_tr(const Tile& t, uint32_t r0, uint32_t r
 // Chunk state of this wave's tiles, S = sum over rows of Bw^T X (A from the
 // weighted B~ tile, B from the x tile, both through transpose reads), folded
 // in: stt <- R(Phi_c)(d stt + S).
-// kSplit (the single pass): the A operand is B~ with each token's slot
-// scaled by its state weight (t.gs), and the rotation comes from the
-// chunk's angles (t.ang).
-template <class C, bool kSplit = false>
+template <class C>
 __device__ __forceinline__ void tok_state_update(const TBuf& t, float d,
                                                  f32x4 (&stt)[kMaxStTiles]) {
   using M = typename C::M;
@@ -549,18 +556,7 @@ __device__ __forceinline__ void tok_state_update(const TBuf& t, float d,
 #pragma unroll
   for (int k0 = 0; k0 < C::LR; k0 += M::K) {
     const uint32_t r0 = (uint32_t)(k0 + 8 * g);
-    bf16x8 fa;
-    if constexpr (kSplit) {
-      // slots 0..7 are tokens r0 .. r0 + 7
-      fa = frag_tr(t.B, r0, r0 + 4, nt);
-      const float4 w0 = *reinterpret_cast<const float4*>(t.gs + 2 * kL + r0);
-      const float4 w1 = *reinterpret_cast<const float4*>(t.gs + 2 * kL + r0 + 4);
-      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) fa[j] = from_f32<bf16>(to_f32(fa[j]) * wv[j]);
-    } else {
-      fa = frag_tr(t.W, r0, r0 + 4, nt);
-    }
+    const bf16x8 fa = frag_tr(t.W, r0, r0 + 4, nt);
 #pragma unroll
     for (int m = 0; m < C::TPW; ++m) {
       const int pt = (wave + kW * m) / C::NNT;
@@ -568,15 +564,7 @@ __device__ __forceinline__ void tok_state_update(const TBuf& t, float d,
     }
   }
   // rows 4g .. 4g + 3 of n-tile nt: pairs 8 nt + 2g and 8 nt + 2g + 1
-  float2 q0, q1;
-  if constexpr (kSplit) {
-    const float2 f = *reinterpret_cast<const float2*>(t.ang + nt * 8 + 2 * g);
-    q0 = make_float2(__builtin_amdgcn_cosf(f.x), __builtin_amdgcn_sinf(f.x));
-    q1 = make_float2(__builtin_amdgcn_cosf(f.y), __builtin_amdgcn_sinf(f.y));
-  } else {
-    q0 = t.rot[nt * 8 + 2 * g];
-    q1 = t.rot[nt * 8 + 2 * g + 1];
-  }
+  const float2 q0 = t.rot[nt * 8 + 2 * g], q1 = t.rot[nt * 8 + 2 * g + 1];
 #pragma unroll
   for (int m = 0; m < C::TPW; ++m) {
     const float v0 = d * stt[m][0] + acc[m][0], v1 = d * stt[m][1] + acc[m][1];
@@ -621,18 +609,15 @@ __device__ __forceinline__ void tok_inter(const Tile& G, const Tile& Cq, uint32_
 // translation, section 3.1, equation 7).  The scores S^T = B~ C~^T (keys x
 // queries) are masked in registers, and their accumulator layout is the B
 // operand of the product with x^T.
-// kSplit (the single pass, R = 1): cs from t.cs, gamma and gamma + omega
-// from t.gs.
-template <class C, bool kSplit = false>
+template <class C>
 __device__ __forceinline__ void tok_intra(const TBuf& t, int qb, int p_lo, f32x4 (&acc)[C::PPG]) {
   using M = typename C::M;
   constexpr int R = C::R, N = C::N, PPG = C::PPG;
-  static_assert(!kSplit || R == 1, "the single pass is rank 1");
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, li = lane & 15;
   const uint32_t qrow = (uint32_t)(qb * 16 + li);
   const int tq = (qb * 16 + li) / R;
-  const float csq = kSplit ? t.cs[tq] : t.sc[tq];
+  const float csq = t.sc[tq];
   // over pairs of 16-row key blocks up to the diagonal
   for (int kb = 0; kb <= qb; kb += 2) {
     f32x4 sct[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -645,19 +630,8 @@ __device__ __forceinline__ void tok_intra(const TBuf& t, int qb, int p_lo, f32x4
     }
     float kcs[2][4], kga[2][4], kgom[2][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row0 = (kb + i) * 16 + 4 * g;
-      if constexpr (kSplit) {
-        const float4 c = *reinterpret_cast<const float4*>(t.cs + row0);
-        const float4 ga = *reinterpret_cast<const float4*>(t.gs + row0);
-        const float4 go = *reinterpret_cast<const float4*>(t.gs + kL + row0);
-        kcs[i][0] = c.x; kcs[i][1] = c.y; kcs[i][2] = c.z; kcs[i][3] = c.w;
-        kga[i][0] = ga.x; kga[i][1] = ga.y; kga[i][2] = ga.z; kga[i][3] = ga.w;
-        kgom[i][0] = go.x; kgom[i][1] = go.y; kgom[i][2] = go.z; kgom[i][3] = go.w;
-      } else {
-        pf::key_scalars4<R>(t.sc, row0, kcs[i], kga[i], kgom[i]);
-      }
-    }
+    for (int i = 0; i < 2; ++i)
+      pf::key_scalars4<R>(t.sc, (kb + i) * 16 + 4 * g, kcs[i], kga[i], kgom[i]);
     pf::mask_scores<R, 2>(sct, kcs, kga, kgom, kb, g, tq, csq);
     bf16x8 fs;
 #pragma unroll
