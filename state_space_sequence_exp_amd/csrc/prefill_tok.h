@@ -952,11 +952,12 @@ __device__ __forceinline__ void tok1_scores_give(const TBuf& t, uint32_t* ex, in
 // The other side: y += (masked scores of key blocks 0 and 1) x, for query
 // block qb (2 or 3) and this wave's p-tiles, once the count reaches
 // `target`.  The wait is bounded (the givers are waves of this workgroup
-// with no wait of their own before they give).
+// with no wait of their own before they give); one that ran out would set
+// error word 1, as a timed-out chain wait does.
 template <class C>
-__device__ __forceinline__ void tok1_scores_take(const TBuf& t, const uint32_t* ex, int* flag,
-                                                 int target, int qb, int p_lo,
-                                                 f32x4 (&acc)[C::PPG]) {
+__device__ __forceinline__ void tok1_scores_take(const PrefillArgs& a, const TBuf& t,
+                                                 const uint32_t* ex, int* flag, int target,
+                                                 int qb, int p_lo, f32x4 (&acc)[C::PPG]) {
   using M = typename C::M;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
@@ -964,10 +965,15 @@ __device__ __forceinline__ void tok1_scores_take(const TBuf& t, const uint32_t* 
   const uint32_t r0 = (uint32_t)(4 * g), r1 = r0 + 16;
 #pragma unroll
   for (int pp = 0; pp < C::PPG; ++pp) fx[pp] = frag_tr(t.X, r0, r1, p_lo + pp);
-  for (int spins = 0; __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
-                          target && spins < (1 << 20);
-       ++spins)
+  int spins = 0;
+  while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
     __builtin_amdgcn_s_sleep(1);
+    if (++spins > (1 << 20)) {
+      // (cannot happen while the givers run; reported as a timed-out wait)
+      __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+  }
   const u32x2 v0 = reinterpret_cast<const u32x2*>(ex)[(qb - 2) * 128 + lane];
   const u32x2 v1 = reinterpret_cast<const u32x2*>(ex)[(qb - 2) * 128 + 64 + lane];
   const bf16x8 fs = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
@@ -1215,7 +1221,7 @@ __device__ __forceinline__ int tok1_segment(const PrefillArgs& a, int ticket,
         tok1_unit<C>(t, qb, p_lo, 0, acc);
       } else {
         tok1_unit<C>(t, qb, p_lo, 2, acc);
-        tok1_scores_take<C>(t, ex, flag, 4 * (i + 1), qb, p_lo, acc);
+        tok1_scores_take<C>(a, t, ex, flag, 4 * (i + 1), qb, p_lo, acc);
       }
     }
     if (direct) {
