@@ -324,7 +324,11 @@ __host__ __device__ inline WaveRoles prefill_wave_roles(int LR, int P) {
   constexpr int kW = kPrefillThreads / 64;
   const int nqb = LR / 16, npt = P / 16;
   WaveRoles w;
-  const int cap = (nqb * 2 <= kW || (kW <= 4 && nqb <= kW)) ? 4 : 2;
+  // units of up to four p-tiles (each query block's scores computed once)
+  // where the query blocks are few, or many enough that the zigzag dealing
+  // still gives every wave two units of balanced cost; two p-tiles between
+  // (one unit of four per wave would leave the causal cost unbalanced)
+  const int cap = (nqb * 2 <= kW || (kW <= 4 && nqb <= kW) || nqb >= 2 * kW) ? 4 : 2;
   w.ppg = npt < cap ? npt : cap;
   w.npg = npt / w.ppg;
   w.nout = nqb * w.npg;
