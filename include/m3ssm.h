@@ -142,10 +142,11 @@ size_t m3_prefill_workspace_size(const m3_dims* dims, int chunk, m3_dtype dtype)
  *  1  a segment waited beyond its bounded spin (about a quarter of a second)
  *     for a predecessor.  Its entry state is then unknown: it continues from
  *     NaN, so its y, every state it hands on (hence the rest of that
- *     sequence's y) and h_final are NaN.  (The single-pass kernel of the
- *     bfloat16, R = 1, N = P = 64, chunk 64 shape also has a bounded wait
- *     between the waves of one workgroup, which sets this word if it runs
- *     out; it cannot while the workgroup runs.)
+ *     sequence's y) and h_final are NaN.  (Two shapes also have a bounded
+ *     wait between the waves of one workgroup, for scores one wave hands to
+ *     another: bfloat16, R = 1, chunk 64 with N = P = 64 (the single-pass
+ *     kernel) or with N = 128, P <= 64.  It sets this word if it runs out,
+ *     which it cannot while the workgroup runs.)
  *  2  the counters were not zero on entry, as seen by a workgroup whose
  *     ticket lies past the grid (its class's ticket word was not zero) or
  *     whose own status word was not zero.  That workgroup computes nothing;

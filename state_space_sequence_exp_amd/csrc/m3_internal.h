@@ -263,8 +263,20 @@ struct PrefillLayout {
   uint32_t off_GT;     // [P][N]    chunk entry state, transposed
   uint32_t off_hand;   // N P floats: the entry state handed between wave layouts (N = 64
                        // fixed, P <= 64, R = 1), else empty
+  uint32_t off_sx;     // kScoreXBytes: scores handed between waves in the output pass
+                       // (see prefill_score_handover), else empty
   uint32_t total;
 };
+
+// With N = 128 fixed, R = 1, P <= 64 and chunks of 64 tokens the output pass
+// has one unit per query block (all of its p-tiles), on four of the eight
+// waves.  Four of the others then compute the masked scores of the two last
+// query blocks against the first key pair, one 16 x 16 block each, and hand
+// them over through LDS: 4 blocks of 64 lanes x 4 bfloat16, then a counter.
+constexpr uint32_t kScoreXBytes = 4 * 64 * 8 + 16;
+__host__ __device__ constexpr bool prefill_score_handover(int L, int R, int N, int P, bool fixed) {
+  return fixed && N == 128 && R == 1 && L == 64 && P <= 64 && kPrefillThreads == 512;
+}
 
 // Whether the kernel instantiated with N fixed at compile time takes the
 // shape: bfloat16, N of 64 or 128 and a chunk of at most 64 tokens, whose
@@ -303,6 +315,8 @@ __host__ __device__ inline PrefillLayout prefill_layout(int L, int R, int N, int
   c.off_GT = o; o += (uint32_t)P * N * esize;
   c.off_hand = o;
   if (fixed && N == 64 && P <= 64 && R == 1) o += (uint32_t)N * P * 4;
+  c.off_sx = o;
+  if (prefill_score_handover(L, R, N, P, fixed)) o += kScoreXBytes;
   c.total = o;
   return c;
 }

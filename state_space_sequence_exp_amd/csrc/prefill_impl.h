@@ -162,6 +162,9 @@ struct Cfg {
   // pass keeps the state tiles on the other four waves only, and the state
   // update runs beside the outputs (the local pass spreads them over all)
   static constexpr bool kSplit3 = N_ == 64 && P_ <= 64 && R_ == 1 && kPrefillThreads == 512;
+  // the output pass's score hand-over may apply (prefill_score_handover
+  // decides with the chunk length)
+  static constexpr bool kHand3 = sizeof(T_) == 2 && prefill_score_handover(64, R_, N_, P_, true);
   // N fixed with N / 2 pairs dividing the wave: wave w holds token blocks
   // w * 128 / N .. (w + 1) * 128 / N - 1 of every pair, and the angle sums
   // before a block are the wave totals of the waves before it plus, with two
@@ -795,11 +798,93 @@ __device__ __forceinline__ void store_unit(const Ctx& s, const rsrc& ry, int qb,
   }
 }
 
+// The output pass's score hand-over (see prefill_score_handover): ex holds
+// the handed blocks, flag counts the givers' blocks, target is the count
+// that completes this chunk's (0: no hand-over).
+struct ScoreX {
+  uint32_t* ex;
+  int* flag;
+  int target;
+};
+
+// Giver: wave kW/2 + 2 i + k computes the masked scores of key block k (of
+// the first pair) against query block 2 + i, as bfloat16 in the lane layout
+// the taker's MFMA operand has, and counts it once its stores are done.
+template <class C>
+__device__ __forceinline__ void scores_give(const float* sc, const Tile& tC, const Tile& tB,
+                                            const ScoreX& hx) {
+  using M = typename C::M;
+  constexpr int NK = C::NC / M::K;
+  const int lane = threadIdx.x & 63, gw = (threadIdx.x >> 6) - kW / 2;
+  const int g = lane >> 4, li = lane & 15;
+  const int qx = 2 + gw / 2, kb = gw % 2;
+  const int tq = qx * 16 + li;
+  typename M::frag fk[NK], fq[NK];
+#pragma unroll
+  for (int n = 0; n < NK; ++n) {
+    fk[n] = load_frag(tB, (uint32_t)(kb * 16 + li), n * M::K, (const bf16*)nullptr);
+    fq[n] = load_frag(tC, (uint32_t)tq, n * M::K, (const bf16*)nullptr);
+  }
+  float kcs[1][4], kga[1][4], kgom[1][4];
+  key_scalars4<1>(sc, kb * 16 + 4 * g, kcs[0], kga[0], kgom[0]);
+  const float csq = sc[tq];
+  f32x4 sct[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int n = 0; n < NK; ++n) sct[0] = M::mma(fk[n], fq[n], sct[0]);  // keys x queries
+  mask_scores<1, 1>(sct, kcs, kga, kgom, kb, g, tq, csq);
+  reinterpret_cast<u32x2*>(hx.ex)[gw * 64 + lane] =
+      u32x2{pack_bf16(sct[0][0], sct[0][1]), pack_bf16(sct[0][2], sct[0][3])};
+  // one count per wave (the release orders all of the wave's stores)
+  if (lane == 0)
+    __hip_atomic_fetch_add(hx.flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Taker: the first key pair's term of query block qb (2 or 3) from the
+// handed scores.  The wait is bounded; running out (which the givers, with
+// no wait of their own, cannot cause) is reported as a timed-out wait.
+template <class C, int PPG>
+__device__ __forceinline__ void scores_take(const PrefillArgs& a, const ScoreX& hx, int qb,
+                                            int p_lo, const Tile& tX, f32x4 (&acc)[PPG]) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, li = lane & 15;
+  bf16x4 xlo[PPG], xhi[PPG];
+#pragma unroll
+  for (int pp = 0; pp < PPG; ++pp) {
+    const uint32_t xr = (uint32_t)((p_lo + pp) * 16 + li);
+    xlo[pp] = tX.ref2<bf16x4>(xr, 8u * g, 0u);
+    xhi[pp] = tX.ref2<bf16x4>(xr, 32u + 8u * g, 0u);
+  }
+  int spins = 0;
+  while (__hip_atomic_load(hx.flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < hx.target) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > (1 << 20)) {
+      __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+  }
+  const u32x2 v0 = reinterpret_cast<const u32x2*>(hx.ex)[(qb - 2) * 128 + lane];
+  const u32x2 v1 = reinterpret_cast<const u32x2*>(hx.ex)[(qb - 2) * 128 + 64 + lane];
+  const bf16x8 fa = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+#pragma unroll
+  for (int pp = 0; pp < PPG; ++pp) {
+    bf16x8 fb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      fb[j] = xlo[pp][j];
+      fb[4 + j] = xhi[pp][j];
+    }
+    acc[pp] = Mfma<bf16>::mma(fa, fb, acc[pp]);
+  }
+}
+
 // One output unit: y rows of query block qb for the PPG p-tiles from p_lo.
+// With the score hand-over query blocks 2 and 3 take their first key pair's
+// scores from the givers.
 template <class C, int PPG>
 __device__ __forceinline__ void output_unit(const PrefillArgs& a, const Ctx& s, const rsrc& ry,
                                             int qb, int p_lo, const float* sc, const Tile& tC,
-                                            const Tile& tB, const Tile& tX, const Tile& tG) {
+                                            const Tile& tB, const Tile& tX, const Tile& tG,
+                                            const ScoreX& hx) {
   using T = typename C::T;
   using M = typename C::M;
   constexpr int R = C::R;
@@ -907,8 +992,10 @@ __device__ __forceinline__ void output_unit(const PrefillArgs& a, const Ctx& s, 
       for (int pp = 0; pp < PPG; ++pp) acc[pp][j] *= scl;
     }
 
-    // intra-chunk term over key blocks up to the diagonal
-    for (int kb = 0; kb * 16 <= qb * 16 + 15; kb += KB) {
+    // intra-chunk term over key blocks up to the diagonal (from the second
+    // pair where the first one's scores are handed over)
+    const bool take = C::kHand3 && hx.target > 0 && qb >= 2;
+    for (int kb = take ? 2 : 0; kb * 16 <= qb * 16 + 15; kb += KB) {
       // the step's x pieces and key scalars first: the mask's empty asm
       // statement keeps the scheduler from moving reads across it
       bf16x4 xlo[PPG], xhi[PPG];
@@ -964,6 +1051,8 @@ __device__ __forceinline__ void output_unit(const PrefillArgs& a, const Ctx& s, 
         }
       }
     }
+    if constexpr (C::kHand3)
+      if (take) scores_take<C, PPG>(a, hx, qb, p_lo, tX, acc);
   }
   store_unit<C, PPG>(s, ry, qb, p_lo, acc);
 }
@@ -975,7 +1064,8 @@ template <class C>
 __device__ __forceinline__ void chunk_output(const PrefillArgs& a, const PrefillLayout& lay,
                                              const WaveRoles& wr, const Ctx& s,
                                              const ChunkRes& cr, const float* sc, const Tile& tC,
-                                             const Tile& tB, const Tile& tX, const Tile& tG) {
+                                             const Tile& tB, const Tile& tX, const Tile& tG,
+                                             const ScoreX& hx) {
   constexpr int NPT = C::NPT;
   constexpr int PPG_A = NPT < 4 ? NPT : 4;  // the two p-group widths in use
   constexpr int PPG_B = NPT < 2 ? NPT : 2;
@@ -984,6 +1074,13 @@ __device__ __forceinline__ void chunk_output(const PrefillArgs& a, const Prefill
   const uint32_t yb = (uint32_t)(C::R * C::P * C::es);
   const rsrc ry = make_rsrc(static_cast<unsigned char*>(a.y) + hrow * yb,
                             (uint32_t)(cr.len - 1) * s.rowX + yb);
+  if constexpr (C::kHand3) {
+    // (four units on waves 0 .. kW/2-1: the others give)
+    if (hx.target > 0 && wave >= kW / 2) {
+      scores_give<C>(sc, tC, tB, hx);
+      return;
+    }
+  }
   // wave w takes units w, 2kW-1-w, 2kW+w, ... so the causal (growing) cost
   // per query block balances when the units outnumber the waves
   for (int k = 0;; ++k) {
@@ -991,9 +1088,9 @@ __device__ __forceinline__ void chunk_output(const PrefillArgs& a, const Prefill
     if (unit >= wr.nout) break;
     const int qb = unit / wr.npg, p_lo = (unit % wr.npg) * wr.ppg;
     if (wr.ppg == PPG_A)
-      output_unit<C, PPG_A>(a, s, ry, qb, p_lo, sc, tC, tB, tX, tG);
+      output_unit<C, PPG_A>(a, s, ry, qb, p_lo, sc, tC, tB, tX, tG, hx);
     else
-      output_unit<C, PPG_B>(a, s, ry, qb, p_lo, sc, tC, tB, tX, tG);
+      output_unit<C, PPG_B>(a, s, ry, qb, p_lo, sc, tC, tB, tX, tG, hx);
   }
 }
 
@@ -1469,6 +1566,13 @@ __device__ __forceinline__ int prefill_segment(const PrefillArgs& a, const Prefi
     }
   }
   for (int i = tid; i < npair; i += kT) s_sang[i] = 0.0;
+  // the output pass's score hand-over, if it applies (its counter starts at
+  // zero; many barriers pass before the output pass)
+  ScoreX hx{reinterpret_cast<uint32_t*>(smem + lay.off_sx),
+            reinterpret_cast<int*>(smem + lay.off_sx + kScoreXBytes - 16), 0};
+  const bool hand = C::kHand3 && prefill_score_handover(a.L, C::R, a.N, P, C::NC != 0) &&
+                    prefill_wave_roles(lay.LR, P).nout == kW / 2;
+  if (hand && tid == 0) *hx.flag = 0;
 
   f32x4 stt[kMaxStTiles];
 #pragma unroll
@@ -1579,7 +1683,8 @@ __device__ __forceinline__ int prefill_segment(const PrefillArgs& a, const Prefi
     state_to_lds<C>(a, wr3, stt, t.G);
     if (more) issue_loads<C, true>(a, s, m, c + 1, stg);
     __syncthreads();
-    chunk_output<C>(a, lay, wr, s, chunk_res<C>(a, s, c), sc, t.C, t.B, t.X, t.G);
+    hx.target = hand ? 4 * (c - s.c0 + 1) : 0;
+    chunk_output<C>(a, lay, wr, s, chunk_res<C>(a, s, c), sc, t.C, t.B, t.X, t.G, hx);
     if (more) {
       state_update<C, NSW3>(a, lay, wr3, __expf(sc[4 * kLMax]), stt, t.W, t.X, smem);
       if (scal_wave)

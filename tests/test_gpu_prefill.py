@@ -88,6 +88,10 @@ SMALL = [
     ("f32", 2, 200, 4, 32, 32, 1, 32),
     ("bf16", 3, 250, 4, 64, 64, 1, 64),
     ("bf16", 1, 300, 5, 128, 64, 1, 64),
+    # N = 128, P <= 64, 64-token chunks: the output pass hands the scores of
+    # query blocks 2 and 3 against the first key pair between waves (P = 16,
+    # one p-tile a unit; a ragged last chunk of 62 tokens)
+    ("bf16", 1, 190, 1, 128, 16, 1, 64),
     # bfloat16, R = 1, N = P = 64, 64-token chunks: the single-pass kernel
     # with segments of 5 chunks (the last chunk ragged), of 7, and of 4 over
     # four groups of segments; and, past 8 chunks a segment, the two-pass
@@ -182,12 +186,14 @@ def test_full_config_whole_tensor(index):
     check_prefill(I.config_inputs(index), cfg.chunk, label="config%d" % index)
 
 
-@pytest.mark.parametrize("shape", [(2, 640, 4, 64, 64, 4), (4, 2048, 16, 64, 64, 1)],
-                         ids=["mimo", "single-pass"])
+@pytest.mark.parametrize("shape", [(2, 640, 4, 64, 64, 4), (4, 2048, 16, 64, 64, 1),
+                                   (1, 1000, 8, 128, 64, 1)],
+                         ids=["mimo", "single-pass", "n128-handover"])
 def test_repeatable_bitwise(shape):
     """Repeated calls give the same bits: the chain composes every entry in
-    one fixed order, and the single pass's hand-over of scores between waves
-    is complete before it is read."""
+    one fixed order, and the hand-overs of scores between waves (the single
+    pass's, and the N = 128 output pass's) are complete before they are
+    read."""
     inp = I.prefill_inputs(*shape, "bf16", seed=51)
     g = upload_prefill(inp)
     y1, h1 = gpu_prefill(inp, 64, g)
