@@ -1668,6 +1668,11 @@ __device__ __forceinline__ int prefill_segment(const PrefillArgs& a, const Prefi
     for (int q = 0; q < kMaxStTiles; ++q) stt[q] = ent[q];
   }
   constexpr int NSW3 = C::kSplit3 ? kW / 2 : kW;
+  // with the score hand-over the waves without an output unit request the
+  // next chunk's inputs after their scores, not before the step's second
+  // barrier: their rotation step is the longer one (they share SIMDs with
+  // the unit waves, which issue first), and the unit waves wait for it there
+  const bool late = hand && __builtin_amdgcn_readfirstlane(wave) >= kW / 2;
 
   // ---- phase 3: outputs from the true entry state -------------------------
   for (int c = s.c0; c < s.c1; ++c) {
@@ -1681,11 +1686,12 @@ __device__ __forceinline__ int prefill_segment(const PrefillArgs& a, const Prefi
     __syncthreads();
     step_rotate<C, true, false>(a, lay, s, m, c, stg, sc, t, inw, smem);
     state_to_lds<C>(a, wr3, stt, t.G);
-    if (more) issue_loads<C, true>(a, s, m, c + 1, stg);
+    if (more && !late) issue_loads<C, true>(a, s, m, c + 1, stg);
     __syncthreads();
     hx.target = hand ? 4 * (c - s.c0 + 1) : 0;
     chunk_output<C>(a, lay, wr, s, chunk_res<C>(a, s, c), sc, t.C, t.B, t.X, t.G, hx);
     if (more) {
+      if (late) issue_loads<C, true>(a, s, m, c + 1, stg);
       state_update<C, NSW3>(a, lay, wr3, __expf(sc[4 * kLMax]), stt, t.W, t.X, smem);
       if (scal_wave)
         chunk_scalars(a, (c + 1) * a.L, min(a.L, a.T - (c + 1) * a.L), s.Ah, wd, wl,
