@@ -165,6 +165,9 @@ struct Cfg {
   // the output pass's score hand-over may apply (prefill_score_handover
   // decides with the chunk length)
   static constexpr bool kHand3 = sizeof(T_) == 2 && prefill_score_handover(64, R_, N_, P_, true);
+  // sixteen query blocks a chunk (chunk R = 256, so R >= 2) may take the
+  // uneven dealing of chunk_output
+  static constexpr bool kDeal16 = R_ >= 2 && kPrefillThreads == 512;
   // N fixed with N / 2 pairs dividing the wave: wave w holds token blocks
   // w * 128 / N .. (w + 1) * 128 / N - 1 of every pair, and the angle sums
   // before a block are the wave totals of the waves before it plus, with two
@@ -1081,6 +1084,22 @@ __device__ __forceinline__ void chunk_output(const PrefillArgs& a, const Prefill
       return;
     }
   }
+  if (C::kDeal16 && wr.nout == 2 * kW && wr.npg == 1 && wr.ppg == PPG_A) {
+    // sixteen query blocks, one unit each, two a wave.  Waves w and w + 4
+    // share a SIMD, and the older one (w < 4) issues first, so an even split
+    // leaves the younger one running alone at the end; the older wave takes
+    // units of cost 13 and its partner 9 (in steps of eight MFMAs: one for
+    // the inter-chunk term, one per key pair), the larger unit first.  The
+    // younger waves also request the next chunk's inputs only after the
+    // step's second barrier (see the output pass).
+    constexpr int kDeal[8][2] = {{14, 4}, {15, 5}, {12, 6}, {13, 7},
+                                 {10, 0}, {11, 1}, {8, 2}, {9, 3}};
+    const int w = __builtin_amdgcn_readfirstlane(wave) & 7;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      output_unit<C, PPG_A>(a, s, ry, kDeal[w][k], 0, sc, tC, tB, tX, tG, hx);
+    return;
+  }
   // wave w takes units w, 2kW-1-w, 2kW+w, ... so the causal (growing) cost
   // per query block balances when the units outnumber the waves
   for (int k = 0;; ++k) {
@@ -1668,11 +1687,15 @@ __device__ __forceinline__ int prefill_segment(const PrefillArgs& a, const Prefi
     for (int q = 0; q < kMaxStTiles; ++q) stt[q] = ent[q];
   }
   constexpr int NSW3 = C::kSplit3 ? kW / 2 : kW;
-  // with the score hand-over the waves without an output unit request the
-  // next chunk's inputs after their scores, not before the step's second
-  // barrier: their rotation step is the longer one (they share SIMDs with
-  // the unit waves, which issue first), and the unit waves wait for it there
+  // Waves kW/2.. share SIMDs with the older waves 0 .. kW/2-1, which issue
+  // first, so their rotation step ends later, and the older waves would wait
+  // for their load requests at the step's second barrier.  With the score
+  // hand-over (no output unit on them) they request the next chunk's inputs
+  // after their scores; with sixteen units dealt unevenly (see chunk_output)
+  // right after the barrier, before their smaller units.
   const bool late = hand && __builtin_amdgcn_readfirstlane(wave) >= kW / 2;
+  const bool late16 = C::kDeal16 && wr.nout == 2 * kW && wr.npg == 1 &&
+                      __builtin_amdgcn_readfirstlane(wave) >= kW / 2;
 
   // ---- phase 3: outputs from the true entry state -------------------------
   for (int c = s.c0; c < s.c1; ++c) {
@@ -1686,8 +1709,9 @@ __device__ __forceinline__ int prefill_segment(const PrefillArgs& a, const Prefi
     __syncthreads();
     step_rotate<C, true, false>(a, lay, s, m, c, stg, sc, t, inw, smem);
     state_to_lds<C>(a, wr3, stt, t.G);
-    if (more && !late) issue_loads<C, true>(a, s, m, c + 1, stg);
+    if (more && !late && !late16) issue_loads<C, true>(a, s, m, c + 1, stg);
     __syncthreads();
+    if (more && late16) issue_loads<C, true>(a, s, m, c + 1, stg);
     hx.target = hand ? 4 * (c - s.c0 + 1) : 0;
     chunk_output<C>(a, lay, wr, s, chunk_res<C>(a, s, c), sc, t.C, t.B, t.X, t.G, hx);
     if (more) {

@@ -92,6 +92,11 @@ SMALL = [
     # query blocks 2 and 3 against the first key pair between waves (P = 16,
     # one p-tile a unit; a ragged last chunk of 62 tokens)
     ("bf16", 1, 190, 1, 128, 16, 1, 64),
+    # sixteen query blocks a chunk (chunk x R = 256) with P <= 64: one unit
+    # per query block, dealt unevenly between the waves that share a SIMD
+    ("f32", 1, 150, 1, 32, 32, 4, 64),
+    ("bf16", 1, 300, 2, 64, 32, 4, 64),
+    ("bf16", 1, 130, 1, 64, 16, 4, 64),
     # bfloat16, R = 1, N = P = 64, 64-token chunks: the single-pass kernel
     # with segments of 5 chunks (the last chunk ragged), of 7, and of 4 over
     # four groups of segments; and, past 8 chunks a segment, the two-pass
